@@ -1,0 +1,414 @@
+/*
+ * moe_ref.c -- plain, slow CPU oracle of the sparse MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY (see moe_ref.h).  Written for a reader to check by
+ * eye against the pages; there is no blocking, fusion or reordering beyond what
+ * the definitions below state.  fp64 throughout.  The only parallelism is an
+ * OpenMP "parallel for" over independent output rows inside one FFN, which
+ * changes no result.
+ *
+ * Citations:
+ *   [R] "MoE 路由与专家流式加载" (colibri-analysis 07), §1.1-§1.4
+ *   [Q] "colibrì 深度拆解：1300行纯C代码驱动7440亿参数大模型", §5.2
+ *   [C] "colibri 开发演进实录：从 CHANGELOG 看多引擎 MoE 推理框架的工程迭代脉络", §2.1, §2.2
+ */
+#include "moe_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define REF_EINVAL (-1)
+
+/* ------------------------------------------------------------------------- */
+/* int4 codec                                                                  */
+/* ------------------------------------------------------------------------- */
+
+/* [Q] §5.2: two signed int4 values share a byte, the first in the low nibble;
+ * each is stored as its low four two's-complement bits. */
+uint8_t moe_ref_pack_int4(int32_t lo, int32_t hi) {
+    return (uint8_t)((lo & 0x0F) | ((hi & 0x0F) << 4));
+}
+
+/* [Q] §5.2: unpack takes each nibble and sign-extends bit 3. */
+void moe_ref_unpack_int4(uint8_t b, int32_t *lo, int32_t *hi) {
+    int32_t a = b & 0x0F;
+    int32_t c = (b >> 4) & 0x0F;
+    if (a & 0x08) a -= 16;
+    if (c & 0x08) c -= 16;
+    *lo = a;
+    *hi = c;
+}
+
+/* Element k of a packed row (even k: low nibble, odd k: high nibble). */
+static int32_t ref_code(const uint8_t *row_q, int64_t k) {
+    int32_t lo, hi;
+    moe_ref_unpack_int4(row_q[k / 2], &lo, &hi);
+    return (k % 2 == 0) ? lo : hi;
+}
+
+/* Dequantised weight W[n][k] of an int4-gs64 matrix with K columns, in fp64.
+ * The product of a code in [-8,7] and an fp32 scale is exact in fp64. */
+static double ref_weight(const uint8_t *q, const float *s, int64_t K, int64_t n, int64_t k) {
+    const uint8_t *row_q = q + n * (K / 2);
+    const float *row_s = s + n * (K / 64);
+    return (double)ref_code(row_q, k) * (double)row_s[k / 64];
+}
+
+/* One scale per 64 consecutive weights along K ([C] §2.1, "int4-gs64").  The
+ * pages give no quantiser rule; the reading used here is symmetric absmax. */
+int moe_ref_quantize_gs64(const float *w, int64_t N, int64_t K, uint8_t *q, float *s) {
+    if (!w || !q || !s || N < 0 || K <= 0 || K % 64 != 0) return REF_EINVAL;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t g = 0; g < K / 64; g++) {
+            const float *wg = w + n * K + g * 64;
+            float amax = 0.0f;
+            for (int i = 0; i < 64; i++) {
+                float a = fabsf(wg[i]);
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 7.0f;
+            s[n * (K / 64) + g] = scale;
+            int32_t code[64];
+            for (int i = 0; i < 64; i++) {
+                int32_t c = 0;
+                if (scale > 0.0f) {
+                    float r = nearbyintf(wg[i] / scale); /* round half to even */
+                    if (r > 7.0f) r = 7.0f;
+                    if (r < -8.0f) r = -8.0f;
+                    c = (int32_t)r;
+                }
+                code[i] = c;
+            }
+            for (int i = 0; i < 64; i += 2)
+                q[n * (K / 2) + g * 32 + i / 2] = moe_ref_pack_int4(code[i], code[i + 1]);
+        }
+    }
+    return 0;
+}
+
+int moe_ref_dequantize_gs64(const uint8_t *q, const float *s, int64_t N, int64_t K, double *w) {
+    if (!q || !s || !w || N < 0 || K <= 0 || K % 64 != 0) return REF_EINVAL;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) w[n * K + k] = ref_weight(q, s, K, n, k);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Steps 1-2: router logits and noaux_tc selection ([R] §1.1, §1.2)            */
+/* ------------------------------------------------------------------------- */
+
+static int ref_layer_ok(const moe_ref_layer *L) {
+    if (!L) return 0;
+    if (L->hidden <= 0 || L->hidden % 64 != 0) return 0;
+    if (L->n_experts <= 0 || L->ffn <= 0 || L->ffn % 64 != 0) return 0;
+    if (L->shared_ffn < 0 || L->shared_ffn % 64 != 0) return 0;
+    if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > 64) return 0;
+    if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return 0;
+    if (!L->router_w) return 0;
+    return 1;
+}
+
+/* [R] §1.1: each position's logit for expert e is the router row dotted with x. */
+int moe_ref_logits(const moe_ref_layer *L, const float *x, int32_t T, double *logits) {
+    if (!ref_layer_ok(L) || (T > 0 && (!x || !logits)) || T < 0) return REF_EINVAL;
+    const int32_t H = L->hidden, E = L->n_experts;
+    for (int32_t t = 0; t < T; t++)
+        for (int32_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; h++)
+                acc += (double)x[(int64_t)t * H + h] * (double)L->router_w[(int64_t)e * H + h];
+            logits[(int64_t)t * E + e] = acc;
+        }
+    return 0;
+}
+
+static double ref_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* One token's selection.  [R] §1.1: sig = sigmoid(logit); the choice score adds
+ * the per-expert bias; the applied gate is the unbiased sig of the chosen expert.
+ * [R] §1.2: k rounds of argmax over choice, excluding experts already taken;
+ * optional adaptive top-p over the chosen gates sorted descending; norm_topk
+ * renormalises the kept gates to sum 1; routed_scale multiplies them. */
+static void ref_select_one(const moe_ref_layer *L, const double *logit,
+                           int32_t *ids, float *w, int32_t *keff_out) {
+    const int32_t E = L->n_experts, k = L->top_k;
+    double *sig = (double *)malloc(sizeof(double) * (size_t)E);
+    double *choice = (double *)malloc(sizeof(double) * (size_t)E);
+    char *taken = (char *)calloc((size_t)E, 1);
+    int32_t pick[64];
+    double pick_sig[64];
+
+    for (int32_t e = 0; e < E; e++) {
+        sig[e] = ref_sigmoid(logit[e]);
+        double b = L->router_bias ? (double)L->router_bias[e] : 0.0;
+        choice[e] = sig[e] + b;
+    }
+    /* Iterative argmax; a strictly greater score replaces the best so far, so
+     * equal scores go to the lowest expert id. */
+    for (int32_t j = 0; j < k; j++) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < E; e++) {
+            if (taken[e]) continue;
+            if (best < 0 || choice[e] > choice[best]) best = e;
+        }
+        taken[best] = 1;
+        pick[j] = best;
+        pick_sig[j] = sig[best];
+    }
+
+    /* Adaptive top-p: order the k chosen gates by sig descending (equal gates keep
+     * slot order), keep the shortest prefix whose running sum reaches p * total. */
+    char keep[64];
+    for (int32_t j = 0; j < k; j++) keep[j] = 1;
+    int32_t keff = k;
+    if (L->top_p > 0.0f && L->top_p < 1.0f) {
+        int32_t ord[64];
+        for (int32_t j = 0; j < k; j++) ord[j] = j;
+        for (int32_t a = 1; a < k; a++) { /* stable insertion sort, descending */
+            int32_t v = ord[a], b = a - 1;
+            while (b >= 0 && pick_sig[ord[b]] < pick_sig[v]) {
+                ord[b + 1] = ord[b];
+                b--;
+            }
+            ord[b + 1] = v;
+        }
+        double tot = 0.0;
+        for (int32_t a = 0; a < k; a++) tot += pick_sig[ord[a]];
+        double thr = (double)L->top_p * tot;
+        double cum = 0.0;
+        int32_t m = k;
+        for (int32_t a = 0; a < k; a++) {
+            cum += pick_sig[ord[a]];
+            if (cum >= thr) {
+                m = a + 1;
+                break;
+            }
+        }
+        for (int32_t j = 0; j < k; j++) keep[j] = 0;
+        for (int32_t a = 0; a < m; a++) keep[ord[a]] = 1;
+        keff = m;
+    }
+
+    /* Kept picks, compacted in selection order. */
+    int32_t kid[64];
+    double ksig[64];
+    int32_t n = 0;
+    for (int32_t j = 0; j < k; j++)
+        if (keep[j]) {
+            kid[n] = pick[j];
+            ksig[n] = pick_sig[j];
+            n++;
+        }
+    double denom = 0.0;
+    for (int32_t j = 0; j < n; j++) denom += ksig[j];
+    for (int32_t j = 0; j < k; j++) {
+        if (j < n) {
+            double g = ksig[j];
+            if (L->norm_topk) g = g / denom;
+            g = g * (double)L->routed_scale;
+            ids[j] = kid[j];
+            w[j] = (float)g;
+        } else {
+            ids[j] = -1;
+            w[j] = 0.0f;
+        }
+    }
+    *keff_out = keff;
+    free(sig);
+    free(choice);
+    free(taken);
+}
+
+int moe_ref_select(const moe_ref_layer *L, const double *logits, int32_t T,
+                   int32_t *ids, float *w, int32_t *keff) {
+    if (!ref_layer_ok(L) || T < 0) return REF_EINVAL;
+    if (T > 0 && (!logits || !ids || !w || !keff)) return REF_EINVAL;
+    for (int32_t t = 0; t < T; t++)
+        ref_select_one(L, logits + (int64_t)t * L->n_experts, ids + (int64_t)t * L->top_k,
+                       w + (int64_t)t * L->top_k, keff + t);
+    return 0;
+}
+
+int moe_ref_route(const moe_ref_layer *L, const float *x, int32_t T,
+                  int32_t *ids, float *w, int32_t *keff) {
+    if (!ref_layer_ok(L) || T < 0) return REF_EINVAL;
+    if (T == 0) return 0;
+    double *logits = (double *)malloc(sizeof(double) * (size_t)T * (size_t)L->n_experts);
+    if (!logits) return REF_EINVAL;
+    int rc = moe_ref_logits(L, x, T, logits);
+    if (rc == 0) rc = moe_ref_select(L, logits, T, ids, w, keff);
+    free(logits);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Step 3: batch union ([R] §1.3)                                             */
+/* ------------------------------------------------------------------------- */
+
+/* The experts chosen by any position of the batch, deduplicated, each listed
+ * once; the rows of an expert are the tokens routed to it, in token order. */
+int moe_ref_union(int32_t E, int32_t k, const int32_t *ids, const int32_t *keff, int32_t T,
+                  int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
+                  int32_t *pick_row) {
+    if (E <= 0 || k <= 0 || T < 0 || !n_uniq || !uniq || !off) return REF_EINVAL;
+    if (T > 0 && (!ids || !keff || !row_tok || !pick_row)) return REF_EINVAL;
+    for (int32_t t = 0; t < T; t++) {
+        if (keff[t] < 0 || keff[t] > k) return REF_EINVAL;
+        for (int32_t j = 0; j < keff[t]; j++)
+            if (ids[(int64_t)t * k + j] < 0 || ids[(int64_t)t * k + j] >= E) return REF_EINVAL;
+    }
+    /* count[e] by brute force over every kept pick */
+    int32_t nu = 0;
+    off[0] = 0;
+    for (int32_t e = 0; e < E; e++) {
+        int32_t c = 0;
+        for (int32_t t = 0; t < T; t++)
+            for (int32_t j = 0; j < keff[t]; j++)
+                if (ids[(int64_t)t * k + j] == e) c++;
+        off[e + 1] = off[e] + c;
+        if (c > 0) uniq[nu++] = e;
+    }
+    for (int32_t i = nu; i < E; i++) uniq[i] = -1;
+    *n_uniq = nu;
+    for (int64_t i = 0; i < (int64_t)T * k; i++) {
+        row_tok[i] = -1;
+        pick_row[i] = -1;
+    }
+    /* rows ordered by (expert ascending, token ascending) */
+    for (int32_t e = 0; e < E; e++) {
+        int32_t r = off[e];
+        for (int32_t t = 0; t < T; t++)
+            for (int32_t j = 0; j < keff[t]; j++)
+                if (ids[(int64_t)t * k + j] == e) {
+                    row_tok[r] = t;
+                    pick_row[(int64_t)t * k + j] = r;
+                    r++;
+                }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Step 4: expert FFN ([R] §1.3: gate, up, SiLU, down)                        */
+/* ------------------------------------------------------------------------- */
+
+int moe_ref_swiglu(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
+                   const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+                   const float *x, double *y) {
+    if (!gq || !gs || !uq || !us || !dq || !ds || !x || !y) return REF_EINVAL;
+    if (H <= 0 || F <= 0 || H % 64 != 0 || F % 64 != 0) return REF_EINVAL;
+    double *hbuf = (double *)malloc(sizeof(double) * (size_t)F);
+    if (!hbuf) return REF_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int32_t f = 0; f < F; f++) {
+        double g = 0.0, u = 0.0;
+        for (int32_t h = 0; h < H; h++) {
+            g += ref_weight(gq, gs, H, f, h) * (double)x[h];
+            u += ref_weight(uq, us, H, f, h) * (double)x[h];
+        }
+        double silu = g / (1.0 + exp(-g)); /* SiLU(g) = g * sigmoid(g) */
+        hbuf[f] = silu * u;
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t n = 0; n < H; n++) {
+        double acc = 0.0;
+        for (int32_t f = 0; f < F; f++) acc += ref_weight(dq, ds, F, n, f) * hbuf[f];
+        y[n] = acc;
+    }
+    free(hbuf);
+    return 0;
+}
+
+/* Expert e's tensors inside the stacked arrays. */
+static void ref_expert_ptrs(const moe_ref_layer *L, int32_t e, const uint8_t **gq,
+                            const float **gs, const uint8_t **uq, const float **us,
+                            const uint8_t **dq, const float **ds) {
+    const int64_t H = L->hidden, F = L->ffn;
+    *gq = L->gate_q + (int64_t)e * F * (H / 2);
+    *gs = L->gate_s + (int64_t)e * F * (H / 64);
+    *uq = L->up_q + (int64_t)e * F * (H / 2);
+    *us = L->up_s + (int64_t)e * F * (H / 64);
+    *dq = L->down_q + (int64_t)e * H * (F / 2);
+    *ds = L->down_s + (int64_t)e * H * (F / 64);
+}
+
+int moe_ref_expert_ffn(const moe_ref_layer *L, const float *x, int32_t T,
+                       const int32_t *off, const int32_t *row_tok, double *y_rows) {
+    if (!ref_layer_ok(L) || T < 0 || !off) return REF_EINVAL;
+    const int32_t H = L->hidden, E = L->n_experts;
+    for (int32_t e = 0; e < E; e++) {
+        for (int32_t r = off[e]; r < off[e + 1]; r++) {
+            const uint8_t *gq, *uq, *dq;
+            const float *gs, *us, *ds;
+            ref_expert_ptrs(L, e, &gq, &gs, &uq, &us, &dq, &ds);
+            int32_t t = row_tok[r];
+            if (t < 0 || t >= T) return REF_EINVAL;
+            int rc = moe_ref_swiglu(gq, gs, uq, us, dq, ds, H, L->ffn, x + (int64_t)t * H,
+                                    y_rows + (int64_t)r * H);
+            if (rc) return rc;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Steps 1-5: the layer ([R] §1: moe(x[S,hidden]); §1.4: shared expert added)  */
+/* ------------------------------------------------------------------------- */
+
+int moe_ref_layer_forward(const moe_ref_layer *L, const float *x, int32_t T,
+                          const int32_t *toks, int32_t n_toks, double *out) {
+    if (!ref_layer_ok(L) || T < 0 || (T > 0 && (!x || !out))) return REF_EINVAL;
+    const int32_t H = L->hidden, E = L->n_experts;
+    int32_t n_out = toks ? n_toks : T;
+    if (n_out < 0) return REF_EINVAL;
+    double *logit = (double *)malloc(sizeof(double) * (size_t)E);
+    double *y = (double *)malloc(sizeof(double) * (size_t)H);
+    int32_t ids[64];
+    float w[64];
+    int32_t keff = 0;
+    int rc = 0;
+    for (int32_t i = 0; i < n_out && rc == 0; i++) {
+        int32_t t = toks ? toks[i] : i;
+        if (t < 0 || t >= T) {
+            rc = REF_EINVAL;
+            break;
+        }
+        const float *xt = x + (int64_t)t * H;
+        double *ot = out + (int64_t)i * H;
+        rc = moe_ref_logits(L, xt, 1, logit);
+        if (rc) break;
+        ref_select_one(L, logit, ids, w, &keff);
+        for (int32_t h = 0; h < H; h++) ot[h] = 0.0;
+        /* weighted sum over the kept picks, in slot order */
+        for (int32_t j = 0; j < keff && rc == 0; j++) {
+            const uint8_t *gq, *uq, *dq;
+            const float *gs, *us, *ds;
+            ref_expert_ptrs(L, ids[j], &gq, &gs, &uq, &us, &dq, &ds);
+            rc = moe_ref_swiglu(gq, gs, uq, us, dq, ds, H, L->ffn, xt, y);
+            if (rc) break;
+            for (int32_t h = 0; h < H; h++) ot[h] += (double)w[j] * y[h];
+        }
+        /* the shared expert: every token, weight 1, not scaled */
+        if (rc == 0 && L->shared_ffn > 0) {
+            rc = moe_ref_swiglu(L->sh_gate_q, L->sh_gate_s, L->sh_up_q, L->sh_up_s,
+                                L->sh_down_q, L->sh_down_s, H, L->shared_ffn, xt, y);
+            if (rc) break;
+            for (int32_t h = 0; h < H; h++) ot[h] += y[h];
+        }
+    }
+    free(logit);
+    free(y);
+    return rc;
+}
+
+int moe_ref_rmsnorm(const float *h, int32_t T, int32_t H, double eps, float *y) {
+    if (!h || !y || T < 0 || H <= 0) return REF_EINVAL;
+    for (int32_t t = 0; t < T; t++) {
+        double ss = 0.0;
+        for (int32_t i = 0; i < H; i++) ss += (double)h[(int64_t)t * H + i] * h[(int64_t)t * H + i];
+        double r = 1.0 / sqrt(ss / H + eps);
+        for (int32_t i = 0; i < H; i++) y[(int64_t)t * H + i] = (float)((double)h[(int64_t)t * H + i] * r);
+    }
+    return 0;
+}

@@ -1,0 +1,422 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values worked
+from the pages' definitions (tests/golden), brute force on tiny inputs, closed
+forms, invariants the pages state, and special cases that reduce to a textbook
+computation.  CPU only.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle as R
+from routed_int4_expert_amd import synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# --------------------------------------------------------------------------- codec
+def test_pack_unpack_golden():
+    for lo, hi, byte in _rows("int4_pack.txt"):
+        lo, hi, byte = int(lo), int(hi), int(byte, 16)
+        assert R.pack_int4(lo, hi) == byte
+        assert R.unpack_int4(byte) == (lo, hi)
+
+
+def test_codec_exhaustive():
+    # every byte unpacks to two values in [-8, 7] and packs back to itself
+    for b in range(256):
+        lo, hi = R.unpack_int4(b)
+        assert -8 <= lo <= 7 and -8 <= hi <= 7
+        assert R.pack_int4(lo, hi) == b
+    # every value pair round-trips
+    for lo in range(-8, 8):
+        for hi in range(-8, 8):
+            assert R.unpack_int4(R.pack_int4(lo, hi)) == (lo, hi)
+
+
+def _codes(q):
+    """Codes of a packed matrix by the bit-level definition (numpy, no oracle)."""
+    lo = (q & 0x0F).astype(np.int16)
+    hi = (q >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((q.shape[0], q.shape[1] * 2), np.int16)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return out
+
+
+def test_quantizer_invariants():
+    rng = np.random.default_rng(1)
+    w = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    w[3, 64:128] = 0.0                      # an all-zero group
+    w[5, :64] = 1e-3                        # a constant group
+    q, s = R.quantize_gs64(w)
+    codes = _codes(q)
+    deq = R.dequantize_gs64(q, s)
+    # the dequantised weight is code * scale, exactly
+    np.testing.assert_array_equal(deq, codes.astype(np.float64) * np.repeat(s, 64, axis=1))
+    # every element within half a scale step
+    assert np.all(np.abs(w - deq) <= np.repeat(s, 64, axis=1) / 2 * (1 + 1e-6))
+    # the group's absmax element maps to +-7
+    g = w.reshape(40, 4, 64)
+    am = np.argmax(np.abs(g), axis=2)
+    for n in range(40):
+        for j in range(4):
+            if s[n, j] > 0:
+                assert abs(codes[n, j * 64 + am[n, j]]) == 7
+    assert s[3, 1] == 0 and np.all(codes[3, 64:128] == 0)
+    assert np.all(codes[5, :64] == 7)
+    # quantising the dequantised matrix again (same scales) gives the same codes
+    q2, s2 = R.quantize_gs64(deq.astype(np.float32))
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(s2, s)
+
+
+def test_synth_quantizer_matches_oracle():
+    rng = np.random.default_rng(2)
+    w = (rng.standard_normal((33, 512)) * 0.02).astype(np.float32)
+    q1, s1 = R.quantize_gs64(w)
+    q2, s2 = S.quantize_gs64(w)
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_offset_identity():
+    # the unsigned-nibble form: sum((u - 8) x) == sum(u x) - 8 sum(x), u = code + 8
+    # ("colibri 开发演进实录", §2.2, K1), exact on integer activations
+    rng = np.random.default_rng(3)
+    q, _ = R.quantize_gs64((rng.standard_normal((8, 128))).astype(np.float32))
+    codes = _codes(q).astype(np.int64)
+    u = ((q & 0x0F) ^ 0x8).astype(np.int64), ((q >> 4) ^ 0x8).astype(np.int64)
+    uu = np.empty_like(codes)
+    uu[:, 0::2], uu[:, 1::2] = u
+    x = rng.integers(-100, 100, size=128)
+    np.testing.assert_array_equal(codes @ x, uu @ x - 8 * x.sum())
+
+
+def test_expert_size_matches_pages():
+    for H, F, mb, eps in _rows("expert_size.txt"):
+        H, F = int(H), int(F)
+        nib = 3 * H * F // 2
+        assert round(nib / 1e6) == int(mb)
+        # the page divides 1 GB/s by its rounded 19 MB and truncates
+        assert int(1e9 / (round(nib / 1e6) * 1e6)) == int(eps)
+        sh = S.custom("x", hidden=H, ffn=F)
+        assert S.expert_bytes(sh) == nib + 3 * H * F // 64 * 4
+
+
+# --------------------------------------------------------------------------- routing
+def _layer(sh, seed=0):
+    return S.make_layer(sh, seed)
+
+
+def _sig(lg):
+    return expit(lg)
+
+
+def test_topk_bruteforce_tiny():
+    sh = S.SHAPES["tiny"]
+    d = _layer(sh)
+    L = R.Layer(d)
+    x = S.make_batch(sh, d)
+    lg = R.logits(L, x)
+    ids, w, keff = R.route(L, x)
+    choice = _sig(lg) + d["router_bias"].astype(np.float64)[None, :]
+    subsets = np.array(list(itertools.combinations(range(sh.n_experts), sh.top_k)))
+    for t in range(x.shape[0]):
+        sums = choice[t][subsets].sum(axis=1)
+        best = subsets[np.argmax(sums)]
+        assert keff[t] == sh.top_k
+        assert set(ids[t].tolist()) == set(best.tolist())
+        # selection order: descending choice
+        assert np.all(np.diff(choice[t][ids[t]]) <= 0)
+
+
+def test_logits_against_matmul():
+    sh = S.SHAPES["tiny"]
+    d = _layer(sh)
+    L = R.Layer(d)
+    x = S.make_batch(sh, d)
+    ref = x.astype(np.float64) @ d["router_w"].astype(np.float64).T
+    np.testing.assert_allclose(R.logits(L, x), ref, rtol=0, atol=1e-12)
+
+
+def test_no_bias_topk_is_logit_sort():
+    sh = S.custom("nobias", bias_kind="zero", n_experts=64, top_k=6, tokens=16)
+    d = _layer(sh)
+    L = R.Layer(d)
+    x = S.make_batch(sh, d)
+    lg = R.logits(L, x)
+    ids, _, _ = R.route(L, x)
+    ref = np.argsort(-lg, axis=1, kind="stable")[:, :6]
+    np.testing.assert_array_equal(ids, ref)
+
+
+def test_bias_steers_selection_only():
+    sh = S.custom("bias", n_experts=32, top_k=4, tokens=16, norm_topk=0, routed_scale=1.0)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    L = R.Layer(d)
+    lg = R.logits(L, x)
+    ids, w, keff = R.route(L, x)
+    # with norm off and scale 1 the applied weight is the unbiased sigmoid of the logit
+    sig = _sig(lg)
+    for t in range(16):
+        np.testing.assert_allclose(w[t], sig[t, ids[t]].astype(np.float32), rtol=2e-7, atol=0)
+    # a large bias pulls an expert into every token's set but its weight stays sigmoid(logit)
+    d2 = dict(d)
+    b = d["router_bias"].copy()
+    b[5] = 3.0
+    d2["router_bias"] = b
+    ids2, w2, _ = R.route(R.Layer(d2), x)
+    assert np.all(ids2[:, 0] == 5)
+    np.testing.assert_allclose(w2[:, 0], sig[:, 5].astype(np.float32), rtol=2e-7, atol=0)
+    assert np.all(w2 < 1.0)
+    # a constant shift of every bias changes neither ids nor weights
+    d3 = dict(d)
+    d3["router_bias"] = (d["router_bias"].astype(np.float64) + 0.25).astype(np.float32)
+    ids3, w3, _ = R.route(R.Layer(d3), x)
+    np.testing.assert_array_equal(ids3, ids)
+    np.testing.assert_array_equal(w3, w)
+
+
+def test_bias_swap_renormalises_common_experts():
+    sh = S.custom("swap", n_experts=32, top_k=4, tokens=8, norm_topk=1, routed_scale=1.0)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    lg = R.logits(R.Layer(d), x)
+    sig = _sig(lg)
+    d2 = dict(d)
+    b = d["router_bias"].copy()
+    b[7] = 5.0
+    d2["router_bias"] = b
+    ids2, w2, _ = R.route(R.Layer(d2), x)
+    for t in range(8):
+        kept = ids2[t]
+        ref = sig[t, kept] / sig[t, kept].sum()
+        np.testing.assert_allclose(w2[t], ref.astype(np.float32), rtol=3e-7, atol=0)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.5])
+def test_norm_and_scale(scale):
+    sh = S.custom("norm", n_experts=64, top_k=8, tokens=32, routed_scale=scale)
+    d = _layer(sh)
+    L = R.Layer(d)
+    x = S.make_batch(sh, d)
+    _, w, keff = R.route(L, x)
+    tot = w.astype(np.float64).sum(axis=1)
+    np.testing.assert_allclose(tot, scale, rtol=8 * 2 ** -23)
+    assert np.all(w > 0)
+
+
+@pytest.mark.parametrize("p", [0.3, 0.7, 0.95])
+def test_topp_minimal_prefix(p):
+    sh = S.custom("topp", n_experts=64, top_k=8, tokens=64, top_p=p, norm_topk=0,
+                  routed_scale=1.0, bias_amp=0.3)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    lg = R.logits(R.Layer(d), x)
+    sig = _sig(lg)
+    ids_full, _, _ = R.route(R.Layer({**d, "top_p": 0.0}), x)
+    ids, w, keff = R.route(R.Layer(d), x)
+    for t in range(64):
+        g = np.sort(sig[t, ids_full[t]])[::-1]
+        cum = np.cumsum(g)
+        m = keff[t]
+        assert 1 <= m <= 8
+        thr = p * cum[-1]
+        assert cum[m - 1] >= thr * (1 - 1e-12)
+        if m > 1:
+            assert cum[m - 2] < thr * (1 + 1e-12)
+        # survivors are the m largest gates, listed in selection order
+        kept = ids[t, :m]
+        assert set(kept.tolist()) == set(ids_full[t][np.argsort(-sig[t, ids_full[t]], kind="stable")[:m]].tolist())
+        order = [j for j in ids_full[t].tolist() if j in set(kept.tolist())]
+        assert kept.tolist() == order
+        assert np.all(ids[t, m:] == -1) and np.all(w[t, m:] == 0)
+
+
+def test_topp_limits():
+    sh = S.custom("toppl", n_experts=64, top_k=8, tokens=16)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    _, _, k1 = R.route(R.Layer({**d, "top_p": 1.0}), x)
+    assert np.all(k1 == 8)
+    _, _, k0 = R.route(R.Layer({**d, "top_p": 1e-6}), x)
+    assert np.all(k0 == 1)
+
+
+# --------------------------------------------------------------------------- union
+def _union_bruteforce(E, ids, keff):
+    T, k = ids.shape
+    pairs = sorted((int(ids[t, j]), t, j) for t in range(T) for j in range(keff[t]))
+    count = np.zeros(E, np.int64)
+    for e, _, _ in pairs:
+        count[e] += 1
+    off = np.concatenate([[0], np.cumsum(count)])
+    row_tok = np.array([t for _, t, _ in pairs], np.int32)
+    pick_row = -np.ones((T, k), np.int32)
+    for r, (_, t, j) in enumerate(pairs):
+        pick_row[t, j] = r
+    uniq = np.nonzero(count)[0]
+    return uniq, off, row_tok, pick_row
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_union_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    E, T, k = 40, 37, 6
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    keff = rng.integers(1, k + 1, size=T).astype(np.int32)
+    for t in range(T):
+        ids[t, keff[t]:] = -1
+    u = R.union(E, ids, keff)
+    uniq, off, row_tok, pick_row = _union_bruteforce(E, ids, keff)
+    assert u["n_uniq"] == len(uniq)
+    np.testing.assert_array_equal(u["uniq"][:len(uniq)], uniq)
+    assert np.all(u["uniq"][len(uniq):] == -1)
+    np.testing.assert_array_equal(u["off"], off)
+    np.testing.assert_array_equal(u["row_tok"][:off[-1]], row_tok)
+    np.testing.assert_array_equal(u["pick_row"], pick_row)
+    assert off[-1] == keff.sum()
+    rows = u["pick_row"][u["pick_row"] >= 0]
+    assert sorted(rows.tolist()) == list(range(off[-1]))
+
+
+def test_union_empty():
+    u = R.union(8, np.zeros((0, 2), np.int32), np.zeros((0,), np.int32))
+    assert u["n_uniq"] == 0 and np.all(u["off"] == 0)
+
+
+# --------------------------------------------------------------------------- FFN / layer
+def _dense_eval(d, x):
+    """Every expert on every token (numpy fp64 matmuls), mixed by a dense weight matrix."""
+    H, E, F, Fs, k = d["hidden"], d["n_experts"], d["ffn"], d["shared_ffn"], d["top_k"]
+    deq = R.dequantize_gs64
+    X = x.astype(np.float64)
+    L = R.Layer(d)
+    ids, w, keff = R.route(L, x)
+    T = x.shape[0]
+    Wmix = np.zeros((T, E))
+    for t in range(T):
+        for j in range(keff[t]):
+            Wmix[t, ids[t, j]] = w[t, j]
+    out = np.zeros((T, H))
+    for e in range(E):
+        G = X @ deq(d["gate_q"][e], d["gate_s"][e]).T
+        U = X @ deq(d["up_q"][e], d["up_s"][e]).T
+        Y = (G * expit(G) * U) @ deq(d["down_q"][e], d["down_s"][e]).T
+        out += Wmix[:, e:e + 1] * Y
+    if Fs:
+        G = X @ deq(d["sh_gate_q"], d["sh_gate_s"]).T
+        U = X @ deq(d["sh_up_q"], d["sh_up_s"]).T
+        out += (G * expit(G) * U) @ deq(d["sh_down_q"], d["sh_down_s"]).T
+    return out
+
+
+@pytest.mark.parametrize("shape", [
+    S.SHAPES["tiny"],
+    S.custom("mid", hidden=320, n_experts=24, ffn=192, shared_ffn=64, top_k=5, tokens=11,
+             top_p=0.8, routed_scale=2.5, bias_amp=0.3),
+    S.custom("noshared", hidden=128, n_experts=8, ffn=64, shared_ffn=0, top_k=2, tokens=5,
+             norm_topk=0),
+])
+def test_layer_matches_dense_evaluation(shape):
+    d = _layer(shape)
+    x = S.make_batch(shape, d)
+    got = R.layer_forward(R.Layer(d), x)
+    ref = _dense_eval(d, x)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # the sampled entry point agrees with the full one
+    sub = R.layer_forward(R.Layer(d), x, toks=[x.shape[0] - 1, 0])
+    np.testing.assert_array_equal(sub, got[[x.shape[0] - 1, 0]])
+
+
+def test_expert_ffn_rows_match_layer():
+    sh = S.custom("rows", hidden=192, n_experts=12, ffn=128, shared_ffn=0, top_k=3, tokens=9,
+                  norm_topk=0, routed_scale=1.0)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    L = R.Layer(d)
+    ids, w, keff = R.route(L, x)
+    u = R.union(sh.n_experts, ids, keff)
+    y = R.expert_ffn(L, x, u["off"], u["row_tok"])
+    out = R.layer_forward(L, x)
+    comb = np.zeros_like(out)
+    for t in range(9):
+        for j in range(keff[t]):
+            comb[t] += float(w[t, j]) * y[u["pick_row"][t, j]]
+    np.testing.assert_allclose(comb, out, rtol=1e-13, atol=1e-13)
+
+
+def test_dense_sigma_mixture_special_case():
+    # k = E, no top-p, norm off, scale 1: the layer is the sigmoid-weighted mixture of all experts
+    sh = S.custom("dense", hidden=128, n_experts=6, ffn=64, shared_ffn=0, top_k=6, tokens=4,
+                  norm_topk=0, routed_scale=1.0)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    L = R.Layer(d)
+    sig = expit(x.astype(np.float64) @ d["router_w"].astype(np.float64).T)
+    ref = np.zeros((4, 128))
+    for e in range(6):
+        y = np.stack([R.swiglu(d["gate_q"][e], d["gate_s"][e], d["up_q"][e], d["up_s"][e],
+                               d["down_q"][e], d["down_s"][e], x[t]) for t in range(4)])
+        ref += sig[:, e:e + 1].astype(np.float32).astype(np.float64) * y
+    np.testing.assert_allclose(R.layer_forward(L, x), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_single_expert_is_plain_swiglu_mlp():
+    # E = k = 1 with norm on: weight 1, so the layer is one SwiGLU MLP plus the shared one
+    sh = S.custom("one", hidden=128, n_experts=1, ffn=64, shared_ffn=64, top_k=1, tokens=3)
+    d = _layer(sh)
+    x = S.make_batch(sh, d)
+    deq = R.dequantize_gs64
+    X = x.astype(np.float64)
+
+    def mlp(gq, gs, uq, us, dq, ds):
+        G, U = X @ deq(gq, gs).T, X @ deq(uq, us).T
+        return (G / (1 + np.exp(-G)) * U) @ deq(dq, ds).T
+
+    ref = mlp(d["gate_q"][0], d["gate_s"][0], d["up_q"][0], d["up_s"][0], d["down_q"][0],
+              d["down_s"][0]) + mlp(d["sh_gate_q"], d["sh_gate_s"], d["sh_up_q"], d["sh_up_s"],
+                                    d["sh_down_q"], d["sh_down_s"])
+    np.testing.assert_allclose(R.layer_forward(R.Layer(d), x), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_zero_gate_gives_shared_only():
+    # SiLU(0) = 0: an expert whose gate weights are all zero contributes nothing
+    sh = S.custom("zg", hidden=128, n_experts=4, ffn=64, shared_ffn=64, top_k=2, tokens=3)
+    d = _layer(sh)
+    d["gate_q"] = np.zeros_like(d["gate_q"])
+    x = S.make_batch(sh, d)
+    out = R.layer_forward(R.Layer(d), x)
+    sh_only = np.stack([R.swiglu(d["sh_gate_q"], d["sh_gate_s"], d["sh_up_q"], d["sh_up_s"],
+                                 d["sh_down_q"], d["sh_down_s"], x[t]) for t in range(3)])
+    np.testing.assert_array_equal(out, sh_only)
+
+
+def test_rmsnorm_unit_rms():
+    h = S.normal_f32(0, "rms", (5, 256), std=3.0)
+    y = R.rmsnorm(h)
+    rms = np.sqrt((y.astype(np.float64) ** 2).mean(axis=1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-6)
+
+
+def test_bf16_rounding_mode():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1e-3], np.float64)
+    bits = R.to_bf16_bits(v)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    # ties to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> 1
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == np.float32(1.0 + 2 ** -6)
+    assert back[3] == -2.5
+    assert abs(back[4] - 1e-3) <= 1e-3 * 2 ** -8
