@@ -1,0 +1,169 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse MoE layer forward.
+ *
+ * The layer is the colibrì moe() forward as described in
+ *   [R] "MoE 路由与专家流式加载" (colibri-analysis 07, blog.chen3feng.top), §1.1-§1.4,
+ * with weights in the int4-gs64 container of
+ *   [Q] "colibrì 深度拆解：1300行纯C代码驱动7440亿参数大模型" (chenxutan.com), §5.2 (packing), and
+ *   [C] "colibri 开发演进实录：从 CHANGELOG 看多引擎 MoE 推理框架的工程迭代脉络", §2.1 (gs64).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or keeps a pointer past the call.  Scratch memory is
+ *   the caller's workspace `ws` of at least moe_workspace_bytes(L, T) bytes,
+ *   16-byte aligned; its contents on entry are ignored and on exit undefined.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on that stream and returns: no synchronisation, no
+ *   device-to-host copy.  Results are ready when the stream reaches them.
+ * - Every call returns MOE_OK (0) or a negative MOE_E* code.  Arguments are
+ *   validated on the host before anything is enqueued; on failure nothing is
+ *   launched and no output is touched.  T == 0 is a successful no-op.
+ * - Results are bitwise deterministic for identical inputs (no floating-point
+ *   atomics on the data path).  Calls may come from several host threads; calls
+ *   that share a workspace must be ordered by the caller (same stream).
+ * - Layouts are row-major; a weight matrix W[N][K] is used as y = W x with K
+ *   contiguous.
+ *
+ * int4-gs64 matrix W[N][K] ([Q] §5.2, [C] §2.1):
+ *   q : uint8 [N][K/2]  -- element 2j in the low nibble of byte j, 2j+1 in the high
+ *                          nibble, each a two's-complement int4 in [-8, 7];
+ *   s : fp32  [N][K/64] -- one scale per 64 consecutive elements of a row;
+ *   W[n][k] = q(n,k) * s[n][k/64].
+ * Routed expert tensors are stacked by expert id: gate/up q [E][F][H/2], s [E][F][H/64];
+ * down q [E][H][F/2], s [E][H][F/64].
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* NULL pointer, bad size or hyper-parameter */
+    MOE_EUNSUPPORTED = -2, /* shape outside the compiled limits below */
+    MOE_EWORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_bytes */
+    MOE_EALIGN = -4,       /* a pointer that must be 16-byte aligned is not */
+    MOE_EDEVICE = -5       /* no gfx950 device current, or a launch failed */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };        /* output element type of moe_layer_forward */
+
+/* Compiled limits (MOE_EUNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_TOKENS 4096
+#define MOE_MAX_DIM 16384                  /* hidden, ffn, shared_ffn */
+
+typedef struct {
+    const uint8_t *q; /* [N][K/2] */
+    const float *s;   /* [N][K/64] */
+} moe_q4;
+
+typedef struct {
+    int32_t hidden;         /* H, multiple of 64 */
+    int32_t n_experts;      /* E, 1..MOE_MAX_EXPERTS */
+    int32_t ffn;            /* F, routed expert width, multiple of 64 */
+    int32_t shared_ffn;     /* Fs, shared expert width, multiple of 64; 0 = no shared expert */
+    int32_t top_k;          /* k, 1..min(E, MOE_MAX_TOPK) */
+    float top_p;            /* adaptive top-p: 0 = off, else (0, 1]; 1 keeps all k */
+    int32_t norm_topk;      /* 1: kept gates renormalised to sum 1 before scaling */
+    float routed_scale;     /* routed_scaling_factor, finite */
+    const float *router_w;    /* [E][H] fp32 */
+    const float *router_bias; /* [E] fp32 selection bias; NULL = all zero */
+    moe_q4 gate, up, down;    /* routed experts, stacked by expert id */
+    moe_q4 sh_gate, sh_up, sh_down; /* shared expert [Fs][H] / [H][Fs]; ignored if Fs == 0 */
+} moe_layer;
+
+/* Optional routing outputs of moe_layer_forward.  Any member may be NULL. */
+typedef struct {
+    int32_t *ids;      /* [T][k] */
+    float *w;          /* [T][k] */
+    int32_t *keff;     /* [T] */
+    int32_t *n_uniq;   /* [1] */
+    int32_t *uniq;     /* [E] */
+    int32_t *off;      /* [E+1] */
+    int32_t *row_tok;  /* [T*k] */
+    int32_t *pick_row; /* [T*k] */
+} moe_route_out;
+
+/* Workspace bytes any call below needs for up to max_tokens tokens of layer L
+ * (0 for an invalid L; the calls then return MOE_EINVAL).  Pure host function. */
+size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens);
+
+/* Steps 1-2 ([R] §1.1, §1.2): router logits and noaux_tc selection.
+ *   x [T][H] fp32.  For each token: logit_e = Wr[e] . x (exact fp32 products summed
+ *   in fp64); sig_e = sigmoid(logit_e) and choice_e = sig_e + bias_e in fp64; k
+ *   rounds of argmax over choice, excluding experts already taken (equal scores
+ *   go to the lower expert id); if 0 < top_p < 1, the k gates sorted by sig
+ *   descending (equal gates keep selection order) are cut after the shortest
+ *   prefix whose sum reaches top_p * (sum of all k); the kept gates (sig, never
+ *   choice) are renormalised to sum 1 if norm_topk, then multiplied by
+ *   routed_scale, and rounded to fp32.
+ * Outputs: ids [T][k] int32, kept experts in selection order, -1 past keff;
+ *          w [T][k] fp32, 0 past keff;  keff [T] int32, number kept (1..k). */
+int moe_route(const moe_layer *L, const float *x, int32_t T, int32_t *ids, float *w,
+              int32_t *keff, void *ws, size_t ws_bytes, void *stream);
+
+/* Step 3 ([R] §1.3, batch-union): deduplicates the kept experts of the whole batch
+ * so each is read once, and builds the token permutation.
+ *   ids [T][k], keff [T] as produced by moe_route (ids outside [0, E) and slots
+ *   at or past keff are ignored).
+ * Outputs: n_uniq [1]; uniq [E] the distinct experts ascending, -1 after n_uniq;
+ *          off [E+1] exclusive prefix sum of per-expert row counts;
+ *          row_tok [T*k] token of each row, rows ordered by (expert, token)
+ *          ascending, -1 past off[E]; pick_row [T*k] row of pick (t, j), -1 if
+ *          not kept.  All exact integers. */
+int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32_t T,
+              int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
+              int32_t *pick_row, void *ws, size_t ws_bytes, void *stream);
+
+/* Step 4 ([R] §1.3, expert compute): for every row r < off[E] of the union, the
+ * SwiGLU FFN of expert e(r) on token row_tok[r]:
+ *   y_rows[r] = Wd_e (silu(Wg_e x) * (Wu_e x)),   fp32 accumulation, unweighted.
+ * Inputs n_uniq/uniq/off/row_tok as produced by moe_union (device).
+ * Output: y_rows [T*k][H] fp32; rows past off[E] are left untouched. */
+int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                   const int32_t *uniq, const int32_t *off, const int32_t *row_tok,
+                   float *y_rows, void *ws, size_t ws_bytes, void *stream);
+
+/* Steps 1-5 ([R] §1, §1.4): the whole layer,
+ *   out[t] = sum_{j < keff_t} w[t][j] * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t),
+ * the shared expert with weight 1 for every token.  out [T][H] is fp32
+ * (out_dtype MOE_F32) or bf16 round-to-nearest-even of the fp32 result
+ * (MOE_BF16).  dbg may be NULL; its non-NULL members receive the routing and
+ * union outputs described above. */
+int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out,
+                      int32_t out_dtype, const moe_route_out *dbg, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Static description of a return code. */
+const char *moe_strerror(int code);
+
+/* ---- measurement -------------------------------------------------------
+ * Kernel timing for benchmarks.  Between moe_prof_begin() and moe_prof_end(),
+ * every kernel the calls above launch is bracketed by two HIP events recorded
+ * on the call's own stream.  moe_prof_end() waits for those events, returns
+ * per-kernel totals (summed over launches, in milliseconds) and stops the
+ * timing.  Process-wide; not for concurrent use from several threads.
+ * moe_prof_end writes at most max_entries entries and the number of distinct
+ * kernels to *n_entries.  Both return MOE_OK, or MOE_EDEVICE if an event call
+ * failed, MOE_EINVAL for bad arguments. */
+typedef struct {
+    char name[32];     /* kernel family, e.g. "ffn_gateup" */
+    int32_t launches;
+    double ms;         /* summed event-to-event time */
+} moe_prof_stat;
+
+int moe_prof_begin(void);
+int moe_prof_end(moe_prof_stat *out, int32_t max_entries, int32_t *n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,236 @@
+"""Python binding of the gfx950 MoE layer library (libmoe_gfx950.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  The entry
+points mirror the C ABI in include/moe.h: ``moe_route``, ``moe_union``,
+``moe_expert_ffn``, ``moe_layer_forward``, ``moe_workspace_bytes`` and
+``moe_strerror``.  If the library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EALIGN, MOE_EDEVICE = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16 = 0, 1
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 16384
+
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
+           "moe_layer_forward", "moe_strerror", "moe_prof_begin", "moe_prof_end")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+class Q4(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+
+
+class LayerC(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("ffn", ctypes.c_int32),
+        ("shared_ffn", ctypes.c_int32), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float),
+        ("norm_topk", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+        ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("gate", Q4), ("up", Q4), ("down", Q4),
+        ("sh_gate", Q4), ("sh_up", Q4), ("sh_down", Q4),
+    ]
+
+
+class ProfStatC(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("ms", ctypes.c_double)]
+
+
+class RouteOutC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("ids", "w", "keff", "n_uniq", "uniq", "off", "row_tok", "pick_row")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER(LayerC)
+    L.moe_workspace_bytes.restype = sz
+    L.moe_workspace_bytes.argtypes = [P, i32]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route.argtypes = [P, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_union.restype = ctypes.c_int
+    L.moe_union.argtypes = [P, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn.restype = ctypes.c_int
+    L.moe_expert_ffn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_forward.restype = ctypes.c_int
+    L.moe_layer_forward.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOutC), vp, sz, vp]
+    L.moe_prof_begin.restype = ctypes.c_int
+    L.moe_prof_begin.argtypes = []
+    L.moe_prof_end.restype = ctypes.c_int
+    L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
+    L.moe_strerror.restype = ctypes.c_char_p
+    L.moe_strerror.argtypes = [ctypes.c_int]
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().moe_strerror(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != MOE_OK:
+        raise MoeError(code, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+TENSORS = ("router_w", "router_bias", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
+           "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s")
+PARAMS = ("hidden", "n_experts", "ffn", "shared_ffn", "top_k", "top_p", "norm_topk",
+          "routed_scale")
+
+
+class Layer:
+    """A layer's hyper-parameters and device tensors, plus its C description."""
+
+    def __init__(self, params: dict, tensors: dict):
+        self.params = {k: params[k] for k in PARAMS}
+        self.t = dict(tensors)
+        c = LayerC()
+        c.hidden, c.n_experts = int(params["hidden"]), int(params["n_experts"])
+        c.ffn, c.shared_ffn, c.top_k = int(params["ffn"]), int(params["shared_ffn"]), int(params["top_k"])
+        c.top_p, c.norm_topk = float(params["top_p"]), int(params["norm_topk"])
+        c.routed_scale = float(params["routed_scale"])
+        g = self.t.get
+        c.router_w = _ptr(g("router_w"))
+        c.router_bias = _ptr(g("router_bias"))
+        for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+            q, s = g(name + "_q"), g(name + "_s")
+            setattr(c, name, Q4(_ptr(q) if q is not None and q.numel() else None,
+                                _ptr(s) if s is not None and s.numel() else None))
+        self.c = c
+        self.hidden, self.n_experts, self.top_k = c.hidden, c.n_experts, c.top_k
+
+    @classmethod
+    def from_host(cls, d: dict, device="cuda"):
+        """Copies a host layer (numpy arrays, as made by the input generator) to the device."""
+        import torch
+        ts = {}
+        for k in TENSORS:
+            v = d.get(k)
+            if v is None:
+                continue
+            ts[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        return cls(d, ts)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def workspace_bytes(self, T: int) -> int:
+        n = lib().moe_workspace_bytes(self.ref(), int(T))
+        if n == 0:
+            raise MoeError(MOE_EINVAL, "moe_workspace_bytes")
+        return int(n)
+
+    def workspace(self, T: int, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes(T), dtype=torch.uint8, device=device)
+
+
+def moe_route(layer: Layer, x, ids=None, w=None, keff=None, ws=None, stream=None):
+    import torch
+    T, k = x.shape[0], layer.top_k
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    keff = torch.empty((T,), dtype=torch.int32, device=dev) if keff is None else keff
+    ws = layer.workspace(T, dev) if ws is None else ws
+    _check(lib().moe_route(layer.ref(), _ptr(x), T, _ptr(ids), _ptr(w), _ptr(keff), _ptr(ws),
+                           ws.numel(), _stream(stream)), "moe_route")
+    return ids, w, keff
+
+
+def moe_union(layer: Layer, ids, keff, ws=None, stream=None, out=None):
+    import torch
+    T, k, E = ids.shape[0], layer.top_k, layer.n_experts
+    dev = ids.device
+    if out is None:
+        out = dict(n_uniq=torch.empty((1,), dtype=torch.int32, device=dev),
+                   uniq=torch.empty((E,), dtype=torch.int32, device=dev),
+                   off=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                   row_tok=torch.empty((max(T * k, 1),), dtype=torch.int32, device=dev),
+                   pick_row=torch.empty((max(T, 1), k), dtype=torch.int32, device=dev))
+    ws = layer.workspace(T, dev) if ws is None else ws
+    _check(lib().moe_union(layer.ref(), _ptr(ids), _ptr(keff), T, _ptr(out["n_uniq"]),
+                           _ptr(out["uniq"]), _ptr(out["off"]), _ptr(out["row_tok"]),
+                           _ptr(out["pick_row"]), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_union")
+    return out
+
+
+def moe_expert_ffn(layer: Layer, x, un: dict, y_rows=None, ws=None, stream=None):
+    import torch
+    T, k, H = x.shape[0], layer.top_k, layer.hidden
+    y_rows = torch.zeros((max(T * k, 1), H), dtype=torch.float32, device=x.device) if y_rows is None else y_rows
+    ws = layer.workspace(T, x.device) if ws is None else ws
+    _check(lib().moe_expert_ffn(layer.ref(), _ptr(x), T, _ptr(un["n_uniq"]), _ptr(un["uniq"]),
+                                _ptr(un["off"]), _ptr(un["row_tok"]), _ptr(y_rows), _ptr(ws),
+                                ws.numel(), _stream(stream)), "moe_expert_ffn")
+    return y_rows
+
+
+def moe_layer_forward(layer: Layer, x, out=None, out_dtype: int = MOE_F32, dbg: dict | None = None,
+                      ws=None, stream=None):
+    """out [T][H] (fp32, or bf16 for MOE_BF16).  ``dbg`` maps moe_route_out member names to
+    device tensors that receive the routing/union outputs."""
+    import torch
+    T, H = x.shape[0], layer.hidden
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32,
+                          device=x.device)
+    ws = layer.workspace(T, x.device) if ws is None else ws
+    rc = None
+    if dbg:
+        rc = RouteOutC(**{k: (v.data_ptr() if v is not None else None) for k, v in dbg.items()})
+    _check(lib().moe_layer_forward(layer.ref(), _ptr(x), T, _ptr(out), out_dtype,
+                                   ctypes.byref(rc) if rc is not None else None, _ptr(ws),
+                                   ws.numel(), _stream(stream)), "moe_layer_forward")
+    return out
+
+
+def moe_prof_begin():
+    _check(lib().moe_prof_begin(), "moe_prof_begin")
+
+
+def moe_prof_end() -> dict:
+    """{kernel name: (launches, total ms)} since moe_prof_begin (waits for the events)."""
+    buf = (ProfStatC * 64)()
+    n = ctypes.c_int32(0)
+    _check(lib().moe_prof_end(buf, 64, ctypes.byref(n)), "moe_prof_end")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].ms)) for i in range(min(n.value, 64))}

@@ -1,0 +1,342 @@
+// moe_api.cpp -- host side of the C ABI declared in include/moe.h: argument
+// validation, the workspace plan and the launch sequence of the MoE layer
+// forward ("MoE 路由与专家流式加载" §1: route, select, union, expert FFN, shared
+// expert and combine).
+//
+// Validation is pure host code and runs before any HIP call, so every error
+// path is reachable without a device.  The calls never synchronise and never
+// copy device data to the host: the union size stays on the device and the
+// expert kernels are launched for the largest possible union, their surplus
+// workgroups returning at once.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// -------------------------------------------------------------- validation
+static int check_dims(const moe_layer *L) {
+    if (!L) return MOE_EINVAL;
+    if (L->hidden <= 0 || L->hidden % 64 || L->ffn <= 0 || L->ffn % 64) return MOE_EINVAL;
+    if (L->shared_ffn < 0 || L->shared_ffn % 64) return MOE_EINVAL;
+    if (L->n_experts <= 0 || L->top_k <= 0 || L->top_k > L->n_experts) return MOE_EINVAL;
+    if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return MOE_EINVAL;  // also rejects NaN
+    if (!isfinite(L->routed_scale)) return MOE_EINVAL;
+    if (L->n_experts > MOE_MAX_EXPERTS || L->top_k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+    if (L->hidden > MOE_MAX_DIM || L->ffn > MOE_MAX_DIM || L->shared_ffn > MOE_MAX_DIM)
+        return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+static int check_q4(const moe_q4 &m) {
+    if (!m.q || !m.s) return MOE_EINVAL;
+    if (!aligned16(m.q) || !aligned16(m.s)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+static int check_router(const moe_layer *L) {
+    if (!L->router_w) return MOE_EINVAL;
+    if (!aligned16(L->router_w)) return MOE_EALIGN;
+    if (L->router_bias && ((uintptr_t)L->router_bias & 3u)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+static int check_experts(const moe_layer *L, bool routed, bool shared) {
+    int rc;
+    if (routed) {
+        if ((rc = check_q4(L->gate)) || (rc = check_q4(L->up)) || (rc = check_q4(L->down))) return rc;
+    }
+    if (shared && L->shared_ffn > 0) {
+        if ((rc = check_q4(L->sh_gate)) || (rc = check_q4(L->sh_up)) || (rc = check_q4(L->sh_down)))
+            return rc;
+    }
+    return MOE_OK;
+}
+
+static int check_T(int32_t T) {
+    if (T < 0) return MOE_EINVAL;
+    if (T > MOE_MAX_TOKENS) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+static int check_ws(const moe_layer *L, int32_t T, const void *ws, size_t ws_bytes) {
+    const size_t need = moe_workspace_bytes(L, T);
+    if (need == 0) return MOE_EINVAL;
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    if (!aligned16(ws)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+// gfx950 check, once per device (lazy; the only HIP query before launching)
+static std::atomic<int> g_dev_ok[64];
+
+static int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return MOE_EDEVICE;
+    }
+    if (dev < 64) {
+        const int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (c != 0) return c > 0 ? MOE_OK : MOE_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    int ok = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    else (void)hipGetLastError();
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? MOE_OK : MOE_EDEVICE;
+}
+
+static int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
+
+// -------------------------------------------------------------- workspace plan
+static size_t router_part_bytes(const moe_layer &L, int T) {
+    // largest S(T') * T' over T' <= T, so the plan grows monotonically with T
+    size_t best = 0;
+    for (int t = 1; t <= T; t++) {
+        const RouterSplit rs = router_split(t, L.n_experts, L.hidden);
+        const size_t b = (size_t)rs.S * t * L.n_experts * sizeof(double);
+        if (b > best) best = b;
+    }
+    return best;
+}
+
+Plan make_plan(const moe_layer &L, int T) {
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    const size_t E = L.n_experts, k = L.top_k, H = L.hidden, F = L.ffn, Fs = L.shared_ffn;
+    const size_t Tz = T > 0 ? (size_t)T : 1;
+    p.T = T;
+    p.rs = router_split((int)Tz, L.n_experts, L.hidden);
+    p.max_units = (int)(Tz * k < E ? Tz * k : E);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    p.part = take(router_part_bytes(L, (int)Tz));
+    p.ids = take(Tz * k * 4);
+    p.w = take(Tz * k * 4);
+    p.keff = take(Tz * 4);
+    p.n_uniq = take(4);
+    p.uniq = take(E * 4);
+    p.off = take((E + 1) * 4);
+    p.row_tok = take(Tz * k * 4);
+    p.pick_row = take(Tz * k * 4);
+    p.h_routed = take(Tz * k * F * 4);
+    p.h_shared = take(Tz * Fs * 4);
+    p.y_routed = take(Tz * k * H * 4);
+    p.y_shared = take(Tz * H * 4);
+    p.total = o;
+    return p;
+}
+
+template <typename P>
+static P *at(void *ws, size_t off) {
+    return reinterpret_cast<P *>(reinterpret_cast<char *>(ws) + off);
+}
+
+// -------------------------------------------------------------- launch pieces
+static hipError_t run_route(const moe_layer &L, const Plan &p, const float *x, int T, int32_t *ids,
+                            float *w, int32_t *keff, void *ws, hipStream_t st) {
+    LogitsArgs la;
+    la.x = x;
+    la.wr = L.router_w;
+    la.part = at<double>(ws, p.part);
+    la.T = T;
+    la.E = L.n_experts;
+    la.H = L.hidden;
+    la.kslice = p.rs.kslice;
+    hipError_t e = launch_router_logits(la, p.rs.S, st);
+    if (e != hipSuccess) return e;
+    SelectArgs sa;
+    sa.part = la.part;
+    sa.bias = L.router_bias;
+    sa.ids = ids;
+    sa.w = w;
+    sa.keff = keff;
+    sa.S = p.rs.S;
+    sa.T = T;
+    sa.E = L.n_experts;
+    sa.k = L.top_k;
+    sa.top_p = L.top_p;
+    sa.routed_scale = L.routed_scale;
+    sa.norm_topk = L.norm_topk ? 1 : 0;
+    return launch_route_select(sa, st);
+}
+
+static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_t *keff, int T,
+                            int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
+                            int32_t *pick_row, hipStream_t st) {
+    UnionArgs ua;
+    ua.ids = ids;
+    ua.keff = keff;
+    ua.n_uniq = n_uniq;
+    ua.uniq = uniq;
+    ua.off = off;
+    ua.row_tok = row_tok;
+    ua.pick_row = pick_row;
+    ua.T = T;
+    ua.E = L.n_experts;
+    ua.k = L.top_k;
+    return launch_union(ua, st);
+}
+
+static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T,
+                        const int32_t *n_uniq, const int32_t *uniq, const int32_t *off,
+                        const int32_t *row_tok, float *y_routed, void *ws) {
+    FfnArgs a;
+    a.x = x;
+    a.n_uniq = n_uniq;
+    a.uniq = uniq;
+    a.off = off;
+    a.row_tok = row_tok;
+    a.gate = L.gate;
+    a.up = L.up;
+    a.down = L.down;
+    a.sh_gate = L.sh_gate;
+    a.sh_up = L.sh_up;
+    a.sh_down = L.sh_down;
+    a.h_routed = at<float>(ws, p.h_routed);
+    a.h_shared = at<float>(ws, p.h_shared);
+    a.y_routed = y_routed;
+    a.y_shared = at<float>(ws, p.y_shared);
+    a.T = T;
+    a.H = L.hidden;
+    a.F = L.ffn;
+    a.Fs = L.shared_ffn;
+    a.max_units = p.max_units;
+    a.with_routed = 1;
+    a.with_shared = L.shared_ffn > 0 ? 1 : 0;
+    return a;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_layer *L, int32_t max_tokens) {
+    if (check_dims(L) != MOE_OK || max_tokens < 0 || max_tokens > MOE_MAX_TOKENS) return 0;
+    return make_plan(*L, max_tokens).total;
+}
+
+int moe_route(const moe_layer *L, const float *x, int32_t T, int32_t *ids, float *w,
+              int32_t *keff, void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (T == 0) return MOE_OK;
+    if ((rc = check_router(L))) return rc;
+    if (!x || !ids || !w || !keff) return MOE_EINVAL;
+    if (!aligned16(x)) return MOE_EALIGN;
+    if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+    if ((rc = check_device())) return rc;
+    const Plan p = make_plan(*L, T);
+    return launched(run_route(*L, p, x, T, ids, w, keff, ws, (hipStream_t)stream));
+}
+
+int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32_t T,
+              int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok, int32_t *pick_row,
+              void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (T == 0) return MOE_OK;
+    if (!ids || !keff || !n_uniq || !uniq || !off || !row_tok || !pick_row) return MOE_EINVAL;
+    if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+    if ((rc = check_device())) return rc;
+    return launched(run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row,
+                              (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                   const int32_t *uniq, const int32_t *off, const int32_t *row_tok, float *y_rows,
+                   void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (T == 0) return MOE_OK;
+    if ((rc = check_experts(L, true, false))) return rc;
+    if (!x || !n_uniq || !uniq || !off || !row_tok || !y_rows) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(y_rows)) return MOE_EALIGN;
+    if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+    if ((rc = check_device())) return rc;
+    const Plan p = make_plan(*L, T);
+    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_rows, ws);
+    a.with_shared = 0;
+    return launched(launch_ffn_gemv(a, (hipStream_t)stream));
+}
+
+int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
+                      const moe_route_out *dbg, void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if ((rc = check_router(L)) || (rc = check_experts(L, true, true))) return rc;
+    if (!x || !out) return MOE_EINVAL;
+    if (!aligned16(x) || ((uintptr_t)out & 7u)) return MOE_EALIGN;
+    if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+    if ((rc = check_device())) return rc;
+    const Plan p = make_plan(*L, T);
+    hipStream_t st = (hipStream_t)stream;
+    moe_route_out d;
+    memset(&d, 0, sizeof(d));
+    if (dbg) d = *dbg;
+    int32_t *ids = d.ids ? d.ids : at<int32_t>(ws, p.ids);
+    float *w = d.w ? d.w : at<float>(ws, p.w);
+    int32_t *keff = d.keff ? d.keff : at<int32_t>(ws, p.keff);
+    int32_t *n_uniq = d.n_uniq ? d.n_uniq : at<int32_t>(ws, p.n_uniq);
+    int32_t *uniq = d.uniq ? d.uniq : at<int32_t>(ws, p.uniq);
+    int32_t *off = d.off ? d.off : at<int32_t>(ws, p.off);
+    int32_t *row_tok = d.row_tok ? d.row_tok : at<int32_t>(ws, p.row_tok);
+    int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
+
+    hipError_t e = run_route(*L, p, x, T, ids, w, keff, ws, st);
+    if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+    float *y_routed = at<float>(ws, p.y_routed);
+    if (e == hipSuccess) {
+        FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
+        e = launch_ffn_gemv(a, st);
+    }
+    if (e == hipSuccess) {
+        CombineArgs c;
+        c.w = w;
+        c.keff = keff;
+        c.pick_row = pick_row;
+        c.y_routed = y_routed;
+        c.y_shared = L->shared_ffn > 0 ? at<float>(ws, p.y_shared) : nullptr;
+        c.out = out;
+        c.T = T;
+        c.H = L->hidden;
+        c.k = L->top_k;
+        c.out_bf16 = out_dtype == MOE_BF16;
+        e = launch_combine(c, st);
+    }
+    return launched(e);
+}
+
+const char *moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (NULL pointer, size or hyper-parameter)";
+        case MOE_EUNSUPPORTED: return "shape outside the compiled limits";
+        case MOE_EWORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
+        case MOE_EALIGN: return "pointer not 16-byte aligned";
+        case MOE_EDEVICE: return "no gfx950 device current, or a kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// moe_internal.h -- shared declarations of the gfx950 MoE library (host + device).
+//
+// Only the library's own translation units include this file.  It holds the
+// workspace plan, the kernel argument blocks and the device helpers used by
+// more than one kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- router tiling
+// Router logits are a [T][E] x [E][H]^T product in fp64, tiled 64 tokens x 64
+// experts per workgroup with a split over H so small batches still cover the chip.
+constexpr int kRouterTile = 64;
+constexpr int kRouterKC = 32;  // H elements staged per LDS step
+
+struct RouterSplit {
+    int S;       // number of H slices
+    int kslice;  // H elements per slice (multiple of kRouterKC)
+};
+RouterSplit router_split(int T, int E, int H);
+
+// ---------------------------------------------------------------- workspace plan
+struct Plan {
+    int T;
+    RouterSplit rs;
+    int max_units;   // routed units a launch must cover: min(E, T*k)
+    size_t part;     // fp64 [S][T][E] router partial logits
+    size_t ids, w, keff;                           // routing, when the caller gives none
+    size_t n_uniq, uniq, off, row_tok, pick_row;   // union, when the caller gives none
+    size_t h_routed;  // fp32 [T*k][F]  SiLU(gate) * up per routed row
+    size_t h_shared;  // fp32 [T][Fs]
+    size_t y_routed;  // fp32 [T*k][H]  unweighted expert outputs per routed row
+    size_t y_shared;  // fp32 [T][H]
+    size_t total;
+};
+Plan make_plan(const moe_layer &L, int T);
+
+// ---------------------------------------------------------------- kernel arguments
+struct LogitsArgs {
+    const float *x;       // [T][H]
+    const float *wr;      // [E][H]
+    double *part;         // [S][T][E]
+    int T, E, H, kslice;
+};
+
+struct SelectArgs {
+    const double *part;   // [S][T][E]
+    const float *bias;    // [E] or nullptr
+    int32_t *ids;         // [T][k]
+    float *w;             // [T][k]
+    int32_t *keff;        // [T]
+    int S, T, E, k;
+    float top_p, routed_scale;
+    int norm_topk;
+};
+
+struct UnionArgs {
+    const int32_t *ids, *keff;
+    int32_t *n_uniq, *uniq, *off, *row_tok, *pick_row;
+    int T, E, k;
+};
+
+// One "unit" of expert work: a routed expert of the union (unit < max_units),
+// or the shared expert (unit == max_units, rows = all T tokens).
+struct FfnArgs {
+    const float *x;                  // [T][H] tokens
+    const int32_t *n_uniq, *uniq, *off, *row_tok;
+    moe_q4 gate, up, down;           // routed, stacked
+    moe_q4 sh_gate, sh_up, sh_down;  // shared
+    float *h_routed;                 // [rows][F]
+    float *h_shared;                 // [T][Fs]
+    float *y_routed;                 // [rows][H]
+    float *y_shared;                 // [T][H]
+    int T, H, F, Fs, max_units;
+    int with_routed, with_shared;
+};
+
+struct CombineArgs {
+    const float *w;         // [T][k]
+    const int32_t *keff;    // [T]
+    const int32_t *pick_row;// [T][k]
+    const float *y_routed;  // [rows][H]
+    const float *y_shared;  // [T][H] or nullptr
+    void *out;              // [T][H] fp32 or bf16
+    int T, H, k, out_bf16;
+};
+
+// Bracketing HIP events around one kernel launch while moe_prof_begin() is active.
+struct ProfScope {
+    ProfScope(const char *name, hipStream_t st);
+    ~ProfScope();
+    int slot;
+    hipStream_t st;
+};
+
+hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st);
+hipError_t launch_route_select(const SelectArgs &a, hipStream_t st);
+hipError_t launch_union(const UnionArgs &a, hipStream_t st);
+hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+
+}  // namespace moe

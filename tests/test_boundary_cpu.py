@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: exported symbols, workspace plan and every validation
+error code, forced from the host.  No call here reaches a kernel launch: each
+one fails validation first (the one valid call is made only when no GPU is
+present, where it must report MOE_EDEVICE)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_int4_expert_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", src, re.M))
+
+
+def test_exports_match_header():
+    names = _declared()
+    assert names == set(M.EXPORTS)
+    lib = M.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _layer(**kw):
+    c = M.LayerC()
+    c.hidden, c.n_experts, c.ffn, c.shared_ffn, c.top_k = 256, 16, 128, 128, 4
+    c.top_p, c.norm_topk, c.routed_scale = 0.0, 1, 1.0
+    fake = 0x10000
+    c.router_w = fake
+    c.router_bias = fake
+    for n in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        setattr(c, n, M.Q4(fake, fake))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def ws_bytes(c, T):
+    return M.lib().moe_workspace_bytes(ctypes.byref(c), T)
+
+
+def test_workspace_plan_monotone_and_invalid():
+    c = _layer()
+    sizes = [ws_bytes(c, T) for T in (0, 1, 2, 8, 63, 64, 65, 300, 4096)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert ws_bytes(_layer(hidden=100), 4) == 0
+    assert ws_bytes(c, -1) == 0 and ws_bytes(c, M.MOE_MAX_TOKENS + 1) == 0
+    big = _layer(hidden=6144, n_experts=256, ffn=2048, shared_ffn=2048, top_k=8)
+    # y rows + h rows dominate: T*k*(H+F)*4 bytes
+    assert ws_bytes(big, 512) >= 512 * 8 * (6144 + 2048) * 4
+
+
+def call_forward(c, T=4, x=0x20000, out=0x30000, dtype=0, ws=0x40000, wsb=None):
+    if wsb is None:
+        wsb = ws_bytes(c, max(T, 0)) if ws_bytes(c, max(T, 0)) else 1 << 30
+    return M.lib().moe_layer_forward(ctypes.byref(c), x, T, out, dtype, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=0), M.MOE_EINVAL),
+    (dict(hidden=100), M.MOE_EINVAL),
+    (dict(ffn=96), M.MOE_EINVAL),
+    (dict(shared_ffn=32), M.MOE_EINVAL),
+    (dict(top_k=0), M.MOE_EINVAL),
+    (dict(top_k=17, n_experts=32), M.MOE_EUNSUPPORTED),
+    (dict(top_k=20), M.MOE_EINVAL),             # k > E
+    (dict(n_experts=300, top_k=4), M.MOE_EUNSUPPORTED),
+    (dict(top_p=1.5), M.MOE_EINVAL),
+    (dict(top_p=float("nan")), M.MOE_EINVAL),
+    (dict(routed_scale=float("inf")), M.MOE_EINVAL),
+    (dict(hidden=32768), M.MOE_EUNSUPPORTED),
+    (dict(router_w=None), M.MOE_EINVAL),
+    (dict(router_w=0x10004), M.MOE_EALIGN),
+    (dict(gate=M.Q4(None, 0x10000)), M.MOE_EINVAL),
+    (dict(down=M.Q4(0x10008, 0x10000)), M.MOE_EALIGN),
+    (dict(sh_up=M.Q4(0x10000, None)), M.MOE_EINVAL),
+])
+def test_forward_validation_codes(kw, code):
+    assert call_forward(_layer(**kw)) == code
+
+
+def test_shared_tensors_ignored_without_shared_expert():
+    c = _layer(shared_ffn=0, sh_gate=M.Q4(None, None), sh_up=M.Q4(None, None),
+               sh_down=M.Q4(None, None))
+    assert call_forward(c, x=None) == M.MOE_EINVAL  # fails on x, not on the shared tensors
+
+
+def test_forward_argument_codes():
+    c = _layer()
+    assert M.lib().moe_layer_forward(None, 0x20000, 4, 0x30000, 0, None, 0x40000, 1 << 30, None) == M.MOE_EINVAL
+    assert call_forward(c, T=-1) == M.MOE_EINVAL
+    assert call_forward(c, T=M.MOE_MAX_TOKENS + 1) == M.MOE_EUNSUPPORTED
+    assert call_forward(c, dtype=7) == M.MOE_EINVAL
+    assert call_forward(c, x=None) == M.MOE_EINVAL
+    assert call_forward(c, out=None) == M.MOE_EINVAL
+    assert call_forward(c, x=0x20004) == M.MOE_EALIGN
+    assert call_forward(c, ws=None) == M.MOE_EWORKSPACE
+    assert call_forward(c, wsb=ws_bytes(c, 4) - 1) == M.MOE_EWORKSPACE
+    assert call_forward(c, ws=0x40008) == M.MOE_EALIGN
+    # T == 0 succeeds without touching anything, even with NULL buffers
+    assert call_forward(c, T=0, x=None, out=None, ws=None, wsb=0) == M.MOE_OK
+
+
+def test_other_entry_points_validate():
+    c = _layer()
+    L = M.lib()
+    r = ctypes.byref(c)
+    wsb = ws_bytes(c, 4)
+    assert L.moe_route(r, None, 4, 1 << 16, 1 << 16, 1 << 16, 1 << 18, wsb, None) == M.MOE_EINVAL
+    assert L.moe_route(r, 0x20004, 4, 1 << 16, 1 << 16, 1 << 16, 1 << 18, wsb, None) == M.MOE_EALIGN
+    assert L.moe_route(r, 0x20000, 4, 1 << 16, 1 << 16, 1 << 16, 1 << 18, 16, None) == M.MOE_EWORKSPACE
+    assert L.moe_union(r, None, 1, 4, 1, 1, 1, 1, 1, 1 << 18, wsb, None) == M.MOE_EINVAL
+    assert L.moe_union(r, 1, 1, -3, 1, 1, 1, 1, 1, 1 << 18, wsb, None) == M.MOE_EINVAL
+    assert L.moe_expert_ffn(r, 0x20000, 4, 1, 1, 1, 1, None, 1 << 18, wsb, None) == M.MOE_EINVAL
+    assert L.moe_expert_ffn(r, 0x20000, 4, 1, 1, 1, 1, 0x30004, 1 << 18, wsb, None) == M.MOE_EALIGN
+    assert L.moe_route(r, None, 0, None, None, None, None, 0, None) == M.MOE_OK
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = M.strerror(code)
+        assert isinstance(s, str) and s and s != "unknown error code"
+    assert M.strerror(99) == "unknown error code"
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    assert call_forward(_layer()) == M.MOE_EDEVICE

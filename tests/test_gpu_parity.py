@@ -1,0 +1,239 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Integers (expert ids, keff, union, permutation) must match exactly; routing
+weights within 1e-6 relative; layer outputs within rel-L2 <= 1e-3 and
+max-abs <= 2e-3 * max(1, rms(ref)) of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as R
+import routed_int4_expert_amd as M
+from routed_int4_expert_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def assert_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / (nrm if nrm > 0 else 1.0)
+    mx = float(np.abs(got - ref).max()) if got.size else 0.0
+    bound = 2e-3 * max(1.0, float(np.sqrt((ref ** 2).mean())) if ref.size else 1.0)
+    assert rel <= 1e-3 and mx <= bound, f"{what}: rel-L2 {rel:.3e}, max-abs {mx:.3e} (bound {bound:.3e})"
+    return rel, mx
+
+
+def check_routing(d, layer, x, xd, sh):
+    ids, w, keff = M.moe_route(layer, xd)
+    torch.cuda.synchronize()
+    rids, rw, rkeff = R.route(R.Layer(d), x)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rids, err_msg="ids")
+    np.testing.assert_array_equal(keff.cpu().numpy(), rkeff, err_msg="keff")
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0, err_msg="w")
+    return ids, w, keff, rids, rw, rkeff
+
+
+def check_union(layer, ids, keff, rids, rkeff, E, k):
+    un = M.moe_union(layer, ids, keff)
+    torch.cuda.synchronize()
+    ru = R.union(E, rids, rkeff)
+    T = ids.shape[0]
+    assert int(un["n_uniq"].item()) == ru["n_uniq"]
+    np.testing.assert_array_equal(un["uniq"].cpu().numpy(), ru["uniq"])
+    np.testing.assert_array_equal(un["off"].cpu().numpy(), ru["off"])
+    np.testing.assert_array_equal(un["row_tok"].cpu().numpy()[:T * k], ru["row_tok"])
+    np.testing.assert_array_equal(un["pick_row"].cpu().numpy().reshape(T, k), ru["pick_row"])
+    return un, ru
+
+
+SMALL = [
+    S.SHAPES["tiny"],
+    S.custom("ragged", hidden=320, n_experts=24, ffn=192, shared_ffn=64, top_k=5, tokens=11,
+             top_p=0.8, routed_scale=2.5, bias_amp=0.3),
+    S.custom("noshared", hidden=128, n_experts=8, ffn=64, shared_ffn=0, top_k=2, tokens=5,
+             norm_topk=0),
+    S.custom("manytok", hidden=128, n_experts=40, ffn=64, shared_ffn=128, top_k=6, tokens=300,
+             bias_amp=0.2),
+    S.custom("maxk", hidden=64, n_experts=256, ffn=64, shared_ffn=64, top_k=16, tokens=70,
+             top_p=0.5, router_std=0.125, bias_amp=0.05),
+    S.custom("onetok", hidden=512, n_experts=32, ffn=256, shared_ffn=256, top_k=4, tokens=1,
+             routed_scale=2.5),
+    S.custom("twotok", hidden=2048, n_experts=64, ffn=512, shared_ffn=512, top_k=8, tokens=2,
+             router_std=1 / 45.25),
+]
+
+
+@pytest.mark.parametrize("sh", SMALL, ids=[s.name for s in SMALL])
+def test_small_shapes_full_parity(sh):
+    say(f"shape {sh.name}: H={sh.hidden} E={sh.n_experts} F={sh.ffn} Fs={sh.shared_ffn} "
+        f"k={sh.top_k} T={sh.tokens} top_p={sh.top_p}")
+    d = S.make_layer(sh, seed=0)
+    x = S.make_batch(sh, d, seed=0)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    # expert rows (unweighted), against the oracle's per-row FFN
+    rows = int(ru["off"][-1])
+    y = M.moe_expert_ffn(layer, xd, un)
+    torch.cuda.synchronize()
+    ry = R.expert_ffn(R.Layer(d), x, ru["off"], ru["row_tok"])
+    assert_close(y.cpu().numpy()[:rows], ry, f"{sh.name} expert rows")
+    # whole layer, fp32 and bf16
+    ref = R.layer_forward(R.Layer(d), x)
+    out = M.moe_layer_forward(layer, xd)
+    out_bf = M.moe_layer_forward(layer, xd, out_dtype=M.MOE_BF16)
+    torch.cuda.synchronize()
+    rel, mx = assert_close(out.cpu().numpy(), ref, f"{sh.name} layer")
+    say(f"shape {sh.name}: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    got_bf = out_bf.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.int32)
+    want_bf = R.to_bf16_bits(out.cpu().numpy().astype(np.float64)).astype(np.int32)
+    # bf16 output is exactly the RNE of the fp32 output of the same launch sequence
+    np.testing.assert_array_equal(got_bf, want_bf)
+
+
+def test_zero_tokens_is_noop():
+    sh = S.SHAPES["tiny"]
+    d = S.make_layer(sh)
+    layer = M.Layer.from_host(d, DEV)
+    x = torch.empty((0, sh.hidden), dtype=torch.float32, device=DEV)
+    out = torch.full((1, sh.hidden), 7.0, device=DEV)
+    ws = layer.workspace(1)
+    assert M.lib().moe_layer_forward(layer.ref(), M._ptr(x), 0, M._ptr(out), 0, None, M._ptr(ws),
+                                     ws.numel(), None) == M.MOE_OK
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_deterministic_bitwise():
+    sh = SMALL[1]
+    d = S.make_layer(sh)
+    x = S.make_batch(sh, d)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    a = M.moe_layer_forward(layer, xd).cpu().numpy()
+    b = M.moe_layer_forward(layer, xd).cpu().numpy()
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_zero_gate_expert_rows_are_exactly_zero():
+    # SiLU(0) = 0: experts whose gate codes are all zero give exactly zero rows
+    sh = S.custom("zerogate", hidden=256, n_experts=16, ffn=128, shared_ffn=128, top_k=4, tokens=8)
+    d = S.make_layer(sh)
+    d["gate_q"] = d["gate_q"].copy()
+    d["gate_q"][::2] = 0
+    x = S.make_batch(sh, d)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, _, keff = M.moe_route(layer, xd)
+    un = M.moe_union(layer, ids, keff)
+    y = M.moe_expert_ffn(layer, xd, un).cpu().numpy()
+    off = un["off"].cpu().numpy()
+    for e in range(0, 16, 2):
+        assert np.all(y[off[e]:off[e + 1]] == 0.0)
+
+
+def test_fail_injection_changes_only_routed_tokens():
+    # a flipped code in one union expert must change exactly the tokens routed to it
+    sh = S.SHAPES["tiny"]
+    d = S.make_layer(sh)
+    x = S.make_batch(sh, d)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, _, keff = M.moe_route(layer, xd)
+    base = M.moe_layer_forward(layer, xd).cpu().numpy()
+    ids_h = ids.cpu().numpy()
+    e = int(ids_h[0, 0])
+    layer.t["down_q"][e, 5, 3] ^= 0x77   # row 5 of expert e's down projection
+    hit = M.moe_layer_forward(layer, xd).cpu().numpy()
+    routed = np.array([e in ids_h[t, :keff[t].item()] for t in range(sh.tokens)])
+    changed = np.any(hit != base, axis=1)
+    np.testing.assert_array_equal(changed, routed)
+    assert np.all(hit[:, :5] == base[:, :5]) and np.all(hit[:, 6:] == base[:, 6:])
+
+
+# ------------------------------------------------------------------ full-size workloads
+@pytest.fixture(scope="module")
+def glm_bank():
+    say("generating the GLM-shaped expert bank (257 experts x 21.2 MB)")
+    bank = S.Bank(S.SHAPES["glm_decode"], seed=0)
+    return bank
+
+
+@pytest.mark.timeout(300)
+def test_small_decode_workload_full():
+    sh = S.SHAPES["small_decode"]
+    say(f"small-expert decode layer: H={sh.hidden} E={sh.n_experts} F={sh.ffn} T={sh.tokens}")
+    d = S.make_layer(sh, seed=0)
+    x = S.make_batch(sh, d, seed=0)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    say(f"small-expert decode: union {ru['n_uniq']} experts, {ru['off'][-1]} rows")
+    out = M.moe_layer_forward(layer, xd)
+    torch.cuda.synchronize()
+    ref = R.layer_forward(R.Layer(d), x)
+    rel, mx = assert_close(out.cpu().numpy(), ref, "small_decode layer")
+    say(f"small-expert decode: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_glm_decode_workload(glm_bank):
+    sh = S.SHAPES["glm_decode"]
+    d = S.make_layer(sh, seed=0, bank=glm_bank)
+    layer = M.Layer.from_host(d, DEV)
+    Lr = R.Layer(d)
+    for pool in range(3):
+        x = S.make_batch(sh, d, seed=0, pool=pool)
+        say(f"GLM decode token pool {pool}")
+        xd = torch.from_numpy(x).to(DEV)
+        ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+        check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+        out = M.moe_layer_forward(layer, xd)
+        out_bf = M.moe_layer_forward(layer, xd, out_dtype=M.MOE_BF16)
+        torch.cuda.synchronize()
+        ref = R.layer_forward(Lr, x)
+        rel, mx = assert_close(out.cpu().numpy(), ref, "glm decode layer")
+        # bf16 mode: exactly the RNE of the fp32 result, hence within half a bf16 ulp
+        # (at most 2^-8 relative) plus the fp32 path's own error of the oracle
+        got_bits = out_bf.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got_bits, R.to_bf16_bits(out.cpu().numpy().astype(np.float64)))
+        got_bf = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rms = np.sqrt((ref ** 2).mean())
+        assert np.all(np.abs(got_bf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms), "bf16 output"
+        say(f"GLM decode pool {pool}: ids {ids.cpu().numpy().tolist()} rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_glm_prefill_workload(glm_bank):
+    sh = S.SHAPES["glm_prefill"]
+    d = S.make_layer(sh, seed=0, bank=glm_bank)
+    x = S.make_batch(sh, d, seed=0)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    say("GLM prefill 512 tokens: routing")
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    counts = np.diff(ru["off"])
+    say(f"GLM prefill: union {ru['n_uniq']} experts, rows max {counts.max()} median "
+        f"{int(np.median(counts[counts > 0]))}")
+    assert 150 <= ru["n_uniq"] <= 256
+    out = M.moe_layer_forward(layer, xd)
+    torch.cuda.synchronize()
+    hot = int(np.argmax(counts))
+    tok_hot = int(ru["row_tok"][ru["off"][hot]])
+    toks = sorted({0, 1, 255, 511, tok_hot})
+    say(f"GLM prefill: oracle on sampled tokens {toks}")
+    ref = R.layer_forward(R.Layer(d), x, toks=toks)
+    rel, mx = assert_close(out.cpu().numpy()[toks], ref, "glm prefill sampled tokens")
+    say(f"GLM prefill sampled: rel-L2 {rel:.2e} max-abs {mx:.2e}")
