@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="resident layer copies cycled per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy a BYTES-long device buffer 3 times (calibrates the HBM "
+                         "byte counters against a transfer of known size) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer forward "
@@ -99,6 +102,16 @@ def main():
     import torch
     import routed_int4_expert_amd as M
     from routed_int4_expert_amd import synth as S
+
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read_per_copy": n * 4, "copies": 3}), flush=True)
+        return
 
     dev = "cuda:0"
     torch.cuda.set_device(0)

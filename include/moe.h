@@ -142,6 +142,16 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out,
                       int32_t out_dtype, const moe_route_out *dbg, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* Glue between stacked MoE layers -- not a step of the layer itself.  For each of
+ * the T rows of H fp32 values: h_out = h + delta (delta NULL: h_out = h), then
+ * x_out = h_out / sqrt(mean(h_out^2) + eps) (RMSNorm with unit gain), fp32 with
+ * a fixed summation order.  h_out may alias h; x_out must not alias h or delta.
+ * Same conventions as above (device pointers, 16-byte aligned, enqueue only,
+ * validation before launch, T == 0 a no-op); H a positive multiple of 64 up to
+ * MOE_MAX_DIM, eps finite and >= 0. */
+int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t H, float eps,
+                         float *h_out, float *x_out, void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

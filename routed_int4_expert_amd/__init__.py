@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 16384
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
-           "moe_layer_forward", "moe_strerror", "moe_prof_begin", "moe_prof_end")
+           "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
+           "moe_prof_end")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,8 @@ def lib():
     L.moe_expert_ffn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward.restype = ctypes.c_int
     L.moe_layer_forward.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOutC), vp, sz, vp]
+    L.moe_residual_rmsnorm.restype = ctypes.c_int
+    L.moe_residual_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp, vp, vp]
     L.moe_prof_begin.restype = ctypes.c_int
     L.moe_prof_begin.argtypes = []
     L.moe_prof_end.restype = ctypes.c_int
@@ -222,6 +225,17 @@ def moe_layer_forward(layer: Layer, x, out=None, out_dtype: int = MOE_F32, dbg: 
                                    ctypes.byref(rc) if rc is not None else None, _ptr(ws),
                                    ws.numel(), _stream(stream)), "moe_layer_forward")
     return out
+
+
+def moe_residual_rmsnorm(h, delta=None, eps: float = 1e-6, h_out=None, x_out=None, stream=None):
+    """h_out = h + delta; x_out = RMSNorm(h_out) (unit gain).  Returns (h_out, x_out)."""
+    import torch
+    T, H = h.shape
+    h_out = torch.empty_like(h) if h_out is None else h_out
+    x_out = torch.empty_like(h) if x_out is None else x_out
+    _check(lib().moe_residual_rmsnorm(_ptr(h), _ptr(delta), T, H, eps, _ptr(h_out), _ptr(x_out),
+                                      _stream(stream)), "moe_residual_rmsnorm")
+    return h_out, x_out
 
 
 def moe_prof_begin():

@@ -10,13 +10,17 @@
 // wave's load covers LPR*16 contiguous bytes of one row.
 //
 // Codes: a byte holds elements 2j (low nibble) and 2j+1 (high nibble) as
-// two's-complement int4 ("colibrì 深度拆解" §5.2).  XOR with 0x8 turns a code q
-// into u = q + 8 in [0, 15], so a 32-element partial dot is
-//   sum(q x) = sum(u x) - 8 sum(x)
-// (the unsigned-offset identity of "colibri 开发演进实录" §2.2, K1), with u
-// converted by the byte-to-float instruction and sum(x) precomputed per 32
-// elements while staging.  The fp32 gs64 scale multiplies each 32-element
-// partial (two per 64-group), all in fp32.
+// two's-complement int4 ("colibrì 深度拆解" §5.2).  Shifting a 32-bit word of 8
+// codes right by 4s and keeping bits 0-3 and 16-19 gives the codes of elements
+// s and s+4; XOR with 0x4308 in each half turns code q into the bf16 bit pattern
+// of 136 + q (0x4300 is 128.0 and q XOR 8 = q + 8 in [0, 15] is the low mantissa),
+// so one bit operation yields a bf16 pair exactly.  Activations are staged as
+// bf16 pairs x = hi + lo (hi = bf16(x), lo = bf16(x - hi), 16 significant bits),
+// and v_dot2 accumulates (136 + q)(hi + lo) in fp32; products are exact.  Per 32
+// elements the offset is removed with the staged sum of x,
+//   sum(q x) = sum((136 + q) x) - 136 sum(x)
+// (the unsigned-offset identity of "colibri 开发演进实录" §2.2, K1), and the
+// fp32 gs64 scale multiplies each 32-element partial (two per 64-group).
 //
 // The gate/up kernel finishes with the fused SiLU(g) * u epilogue and writes
 // h [rows][F]; the down kernel writes the unweighted y [rows][H].  Each output
@@ -27,29 +31,46 @@
 
 namespace moe {
 
-// LDS row layout: 32-float chunks padded to 36 floats (the pad slot 32 holds the
-// chunk's sum), so the 16-byte reads of 8 consecutive lanes hit distinct banks.
+// LDS row layout: per 32-element chunk 36 dwords -- 32 dwords of bf16 pairs in
+// dot order ([d][s][hi,lo] for 8-element group d and pair s = elements 8d+s and
+// 8d+s+4), the chunk's sum of x at dword 32, then padding so the 16-byte reads
+// of 8 consecutive lanes hit distinct banks.
 constexpr int kChunkPitch = 36;
+constexpr uint32_t kBf16Offset = 0x43084308u;
+constexpr float kCodeOffset = 136.0f;
 
-__device__ __forceinline__ float dot32_offset(const uint4 q, const float4 *xv) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// sum over 32 codes of (136 + q_i) * x_i, x staged as 8 uint4 of bf16 pairs
+__device__ __forceinline__ float dot32_bf16(const uint4 q, const uint4 *xv) {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-    float s0 = 0.f, s1 = 0.f;
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; d++) {
-        const uint32_t u = wd[d] ^ 0x88888888u;
-        const uint32_t lo = u & 0x0F0F0F0Fu;          // elements 0,2,4,6 of this word
-        const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;   // elements 1,3,5,7
-        const float4 a = xv[2 * d], b = xv[2 * d + 1];
-        s0 = fmaf((float)(lo & 0xFFu), a.x, s0);
-        s1 = fmaf((float)(hi & 0xFFu), a.y, s1);
-        s0 = fmaf((float)((lo >> 8) & 0xFFu), a.z, s0);
-        s1 = fmaf((float)((hi >> 8) & 0xFFu), a.w, s1);
-        s0 = fmaf((float)((lo >> 16) & 0xFFu), b.x, s0);
-        s1 = fmaf((float)((hi >> 16) & 0xFFu), b.y, s1);
-        s0 = fmaf((float)(lo >> 24), b.z, s0);
-        s1 = fmaf((float)(hi >> 24), b.w, s1);
+        const uint4 x01 = xv[2 * d], x23 = xv[2 * d + 1];
+        const uint32_t p0 = (wd[d] & 0x000F000Fu) ^ kBf16Offset;
+        const uint32_t p1 = ((wd[d] >> 4) & 0x000F000Fu) ^ kBf16Offset;
+        const uint32_t p2 = ((wd[d] >> 8) & 0x000F000Fu) ^ kBf16Offset;
+        const uint32_t p3 = ((wd[d] >> 12) & 0x000F000Fu) ^ kBf16Offset;
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p0), as_bf2(x01.x), a0, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p0), as_bf2(x01.y), a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p1), as_bf2(x01.z), a1, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p1), as_bf2(x01.w), a1, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p2), as_bf2(x23.x), a0, false);
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p2), as_bf2(x23.y), a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p3), as_bf2(x23.z), a1, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p3), as_bf2(x23.w), a1, false);
     }
-    return s0 + s1;
+    return a0 + a1;
 }
 
 template <int LPR>
@@ -59,19 +80,24 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Outputs per lane group per pass: enough rows in flight for ~8 loads per lane.
-template <int LPR, bool GU>
+// Outputs per lane group per pass: four weight rows per step at one token (the
+// next step's rows are loaded while the current ones are computed), fewer with
+// more tokens so the accumulators fit in registers.
+template <int LPR, int RM, bool GU>
 struct GemvShape {
     static constexpr int G = kWave / LPR;                     // lane groups per wave
-    static constexpr int NF = (LPR >= 16 ? LPR / 16 : 1) * (GU ? 1 : 2);
+    static constexpr int NFB = (LPR >= 32 ? LPR / 32 : 1) * (GU ? 1 : 2);
+    static constexpr int NF = NFB / RM > 0 ? NFB / RM : 1;    // outputs per lane group per pass
     static constexpr int NM = GU ? 2 : 1;                     // matrices per output
-    static constexpr int WF = G * NF;                         // outputs per wave
-    static constexpr int BF = 4 * WF;                         // outputs per workgroup
+    static constexpr int WF = G * NF;                         // outputs per wave per pass
+    static constexpr int BF = 4 * WF;                         // outputs per workgroup per pass
 };
 
+// a.passes: passes per workgroup, chosen on the host so the grid fits in one
+// round of resident workgroups
 template <int LPR, int RM, bool GU>
-__global__ __launch_bounds__(256) void q4_gemv_kernel(FfnArgs a) {
-    using S = GemvShape<LPR, GU>;
+__global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) {
+    using S = GemvShape<LPR, RM, GU>;
     extern __shared__ float xs[];  // [RM][C * kChunkPitch]
     const int unit = blockIdx.y;
     const int H = a.H;
@@ -124,105 +150,167 @@ __global__ __launch_bounds__(256) void q4_gemv_kernel(FfnArgs a) {
     const int K = GU ? H : Fu;      // reduction length
     const int N = GU ? Fu : H;      // outputs of this unit
     const int C = K / 32;           // 32-element chunks per row
-    const int nb0 = blockIdx.x * S::BF;
-    if (nb0 >= N) return;
+    const int nbw = blockIdx.x * S::BF * passes;  // first output of this workgroup
+    if (nbw >= N) return;
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wv = tid / kWave;
-    const int sub = lane % LPR, grp = lane / LPR;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+    const int sub = lane % LPR;
+    const int grp = LPR == kWave ? 0 : lane / LPR;  // with 64 lanes per row the row is wave-uniform
     const int rowpitch = C * kChunkPitch;
+
+    // Steps = (pass, chunk iteration), flattened so the codes and scales of the
+    // next step are in flight while the current one is computed.
+    const int nit = (C + LPR - 1) / LPR;
+    const int nsteps = passes * nit;
+    uint4 q[S::NF][S::NM], qn[S::NF][S::NM];
+    float sc[S::NF][S::NM], scn[S::NF][S::NM];
+    float acc[S::NF][S::NM][RM];
+    auto load_step = [&](int step, uint4 (&qq)[S::NF][S::NM], float (&ss)[S::NF][S::NM]) {
+        const int p = step / nit, c = sub + (step % nit) * LPR;
+        const int cc = c < C ? c : C - 1;  // lanes past the row's end re-read its last chunk
+#pragma unroll
+        for (int f = 0; f < S::NF; f++) {
+            const int n = min(nbw + p * S::BF + wv * S::WF + f * S::G + grp, N - 1);
+#pragma unroll
+            for (int m = 0; m < S::NM; m++) {
+                // row base (wave-uniform when LPR == 64) plus a 32-bit lane offset
+                const uint8_t *rq = (m == 0 ? m0.q : m1.q) + (size_t)n * (K / 2);
+                const float *rs = (m == 0 ? m0.s : m1.s) + (size_t)n * (K / 64);
+                qq[f][m] = *reinterpret_cast<const uint4 *>(rq + (uint32_t)(16 * cc));
+                ss[f][m] = rs[(uint32_t)(cc >> 1)];
+            }
+        }
+    };
+    // the first step's codes do not depend on the staged rows: issue them before staging
+    load_step(0, q, sc);
 
     for (int rc = 0; rc < nrows; rc += RM) {
         const int R = min(RM, nrows - rc);
         __syncthreads();  // previous rows fully consumed
-        // stage R input rows (fp32) into the padded LDS layout
-        for (int i = tid; i < R * (K / 4); i += blockDim.x) {
-            const int r = i / (K / 4), c4 = i % (K / 4);
+        // stage R input rows as bf16 hi/lo pairs in dot order: one thread per 8 elements
+        uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
+        for (int i = tid; i < R * (K / 8); i += blockDim.x) {
+            const int r = i / (K / 8), g = i % (K / 8);
             const int src = rt ? rt[rc + r] : rc + r;
-            const float4 v = *reinterpret_cast<const float4 *>(xin + (size_t)src * K + 4 * c4);
-            *reinterpret_cast<float4 *>(xs + r * rowpitch + (c4 / 8) * kChunkPitch + (c4 % 8) * 4) = v;
+            const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
+            const float4 v0 = px[0], v1 = px[1];
+            const float xe[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t hb[8], lb[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                hb[e] = bf16_rne_bits(xe[e]);
+                lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
+            }
+            uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
+            w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
+            w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
+            w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
+            w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
+            uint4 *dst = reinterpret_cast<uint4 *>(xw + r * rowpitch + (g / 4) * kChunkPitch + (g % 4) * 8);
+            dst[0] = w0;
+            dst[1] = w1;
         }
         __syncthreads();
+        // per chunk: the sum of the staged values (hi + lo), fp32
         for (int i = tid; i < R * C; i += blockDim.x) {
             const int r = i / C, c = i % C;
-            const float *p = xs + r * rowpitch + c * kChunkPitch;
-            // even and odd elements summed in the order dot32_offset accumulates them, so a
-            // group of zero codes (u = 8 everywhere) cancels to exactly 0
-            float se = 0.f, so = 0.f;
+            const uint32_t *p = xw + r * rowpitch + c * kChunkPitch;
+            float sacc = 0.f;
 #pragma unroll
-            for (int q = 0; q < 32; q += 2) {
-                se += p[q];
-                so += p[q + 1];
+            for (int j = 0; j < 32; j++) {
+                const uint32_t v = p[j];
+                sacc += bf16_to_f32(v & 0xFFFFu) + bf16_to_f32(v >> 16);
             }
-            xs[r * rowpitch + c * kChunkPitch + 32] = se + so;
+            xs[r * rowpitch + c * kChunkPitch + 32] = sacc;
         }
         __syncthreads();
 
-        float acc[S::NF][S::NM][RM];
+        if (rc > 0) load_step(0, q, sc);  // rows beyond the first RM restart the weight stream
+        // one step: prefetch the next step's rows into (qn, scn), compute with (qc, scc)
+        auto do_step = [&](int step, uint4 (&qc)[S::NF][S::NM], float (&scc)[S::NF][S::NM],
+                           uint4 (&qnx)[S::NF][S::NM], float (&scnx)[S::NF][S::NM]) {
+            const int p = step / nit, it = step % nit;
+            const int nb0 = nbw + p * S::BF;
+            // unconditional, so the wait before the compute below only covers this step's
+            // loads (the last step re-fetches itself, which the cache serves)
+            load_step(step + 1 < nsteps ? step + 1 : step, qnx, scnx);
+            if (it == 0) {
 #pragma unroll
-        for (int f = 0; f < S::NF; f++)
+                for (int f = 0; f < S::NF; f++)
 #pragma unroll
-            for (int m = 0; m < S::NM; m++)
+                    for (int m = 0; m < S::NM; m++)
 #pragma unroll
-                for (int r = 0; r < RM; r++) acc[f][m][r] = 0.f;
-
-        int nidx[S::NF];
-#pragma unroll
-        for (int f = 0; f < S::NF; f++) nidx[f] = nb0 + wv * S::WF + f * S::G + grp;
-
-        for (int c = sub; c < C; c += LPR) {
-            uint4 q[S::NF][S::NM];
-            float sc[S::NF][S::NM];
-#pragma unroll
-            for (int f = 0; f < S::NF; f++) {
-                const int n = min(nidx[f], N - 1);  // rows past N compute garbage, never stored
-#pragma unroll
-                for (int m = 0; m < S::NM; m++) {
-                    const moe_q4 &mm = m == 0 ? m0 : m1;
-                    q[f][m] = *reinterpret_cast<const uint4 *>(mm.q + (size_t)n * (K / 2) + 16 * c);
-                    sc[f][m] = mm.s[(size_t)n * (K / 64) + (c >> 1)];
-                }
+                        for (int r = 0; r < RM; r++) acc[f][m][r] = 0.f;
             }
-#pragma unroll
-            for (int r = 0; r < RM; r++) {
-                if (r < R) {
-                    const float *p = xs + r * rowpitch + c * kChunkPitch;
-                    float4 xv[8];
-#pragma unroll
-                    for (int v = 0; v < 8; v++) xv[v] = *reinterpret_cast<const float4 *>(p + 4 * v);
-                    const float sx8 = 8.0f * p[32];
-#pragma unroll
-                    for (int f = 0; f < S::NF; f++)
-#pragma unroll
-                        for (int m = 0; m < S::NM; m++)
-                            acc[f][m][r] = fmaf(sc[f][m], dot32_offset(q[f][m], xv) - sx8, acc[f][m][r]);
-                }
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < S::NF; f++)
-#pragma unroll
-            for (int m = 0; m < S::NM; m++)
-#pragma unroll
-                for (int r = 0; r < RM; r++) acc[f][m][r] = group_sum<LPR>(acc[f][m][r]);
-
-        if (sub == 0) {
-#pragma unroll
-            for (int f = 0; f < S::NF; f++) {
-                const int n = nidx[f];
-                if (n >= N) continue;
+            const int c = sub + it * LPR;
+            if (c < C) {
 #pragma unroll
                 for (int r = 0; r < RM; r++) {
-                    if (r >= R) continue;
-                    float v;
-                    if (GU) {
-                        const float g = acc[f][0][r], u = acc[f][S::NM - 1][r];
-                        v = g / (1.0f + expf(-g)) * u;
-                    } else {
-                        v = acc[f][0][r];
+                    if (r < R) {
+                        const float *px = xs + r * rowpitch + c * kChunkPitch;
+                        uint4 xv[8];
+#pragma unroll
+                        for (int v = 0; v < 8; v++) xv[v] = *reinterpret_cast<const uint4 *>(px + 4 * v);
+                        const float sxo = kCodeOffset * px[32];
+#pragma unroll
+                        for (int f = 0; f < S::NF; f++)
+#pragma unroll
+                            for (int m = 0; m < S::NM; m++) {
+                                acc[f][m][r] = fmaf(scc[f][m], dot32_bf16(qc[f][m], xv) - sxo, acc[f][m][r]);
+                                // one row at a time: keeps the bf16 pair temporaries of a single row live
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
                     }
-                    out[(out_row0 + rc + r) * (size_t)N + n] = v;
+                    __builtin_amdgcn_sched_barrier(0);  // one token's activations live at a time
                 }
+            }
+            if (it == nit - 1) {
+#pragma unroll
+                for (int f = 0; f < S::NF; f++)
+#pragma unroll
+                    for (int m = 0; m < S::NM; m++)
+#pragma unroll
+                        for (int r = 0; r < RM; r++) acc[f][m][r] = group_sum<LPR>(acc[f][m][r]);
+                if (sub == 0) {
+#pragma unroll
+                    for (int f = 0; f < S::NF; f++) {
+                        const int n = nb0 + wv * S::WF + f * S::G + grp;
+                        if (n >= N) continue;
+#pragma unroll
+                        for (int r = 0; r < RM; r++) {
+                            if (r >= R) continue;
+                            float v;
+                            if (GU) {
+                                const float g = acc[f][0][r], u = acc[f][S::NM - 1][r];
+                                v = g / (1.0f + expf(-g)) * u;
+                            } else {
+                                v = acc[f][0][r];
+                            }
+                            out[(out_row0 + rc + r) * (size_t)N + n] = v;
+                        }
+                    }
+                }
+            }
+        };
+        if (RM == 1) {
+            // ping-pong between the two register buffers, two steps per iteration
+            for (int step = 0; step < nsteps; step += 2) {
+                do_step(step, q, sc, qn, scn);
+                if (step + 1 < nsteps) do_step(step + 1, qn, scn, q, sc);
+            }
+        } else {
+            // more tokens per row: more arithmetic per byte; one body keeps registers in check
+            for (int step = 0; step < nsteps; step++) {
+                do_step(step, q, sc, qn, scn);
+#pragma unroll
+                for (int f = 0; f < S::NF; f++)
+#pragma unroll
+                    for (int m = 0; m < S::NM; m++) {
+                        q[f][m] = qn[f][m];
+                        sc[f][m] = scn[f][m];
+                    }
             }
         }
     }
@@ -242,9 +330,23 @@ static int rows_per_pass(int T, int K) {
     return rm;
 }
 
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+        (void)hipGetLastError();
+    }
+    return cus;
+}
+
 template <int LPR, int RM, bool GU>
 static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
-    using S = GemvShape<LPR, GU>;
+    using S = GemvShape<LPR, RM, GU>;
     const size_t lds = (size_t)RM * (K / 32) * kChunkPitch * sizeof(float);
     if (lds > 64 * 1024) {
         // raise the dynamic-LDS cap for this kernel; the launch itself reports a real failure
@@ -252,9 +354,17 @@ static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         (void)hipGetLastError();
     }
-    dim3 grid((N + S::BF - 1) / S::BF, a.max_units + 1);
+    // resident workgroups per CU (4 waves each): registers allow 4, LDS may allow fewer
+    int per_cu = 4;
+    while (per_cu > 1 && (size_t)per_cu * lds > 160 * 1024) per_cu--;
+    const long cap = (long)device_cus() * per_cu;
+    const int units = a.max_units + 1;
+    const int blocks1 = (N + S::BF - 1) / S::BF;  // workgroups per unit at one pass each
+    int passes = 1;
+    while ((long)((blocks1 + passes - 1) / passes) * units > cap && passes < blocks1) passes++;
+    dim3 grid((blocks1 + passes - 1) / passes, units);
     ProfScope prof(GU ? "ffn_gateup" : "ffn_down", st);
-    q4_gemv_kernel<LPR, RM, GU><<<grid, 256, lds, st>>>(a);
+    q4_gemv_kernel<LPR, RM, GU><<<grid, 256, lds, st>>>(a, passes);
     return hipGetLastError();
 }
 

@@ -139,6 +139,14 @@ Plan make_plan(const moe_layer &L, int T) {
     p.h_shared = take(Tz * Fs * 4);
     p.y_routed = take(Tz * k * H * 4);
     p.y_shared = take(Tz * H * 4);
+    if (Tz > (size_t)kGemvMaxTokens) {
+        p.x_frag = take(Tz * H * 4);
+        p.x_sx = take(Tz * (H / 64) * 4);
+        p.hr_frag = take(Tz * k * F * 4);
+        p.hr_sx = take(Tz * k * (F / 64) * 4);
+        p.hs_frag = take(Tz * Fs * 4);
+        p.hs_sx = take(Tz * (Fs / 64) * 4);
+    }
     p.total = o;
     return p;
 }
@@ -149,20 +157,10 @@ static P *at(void *ws, size_t off) {
 }
 
 // -------------------------------------------------------------- launch pieces
-static hipError_t run_route(const moe_layer &L, const Plan &p, const float *x, int T, int32_t *ids,
-                            float *w, int32_t *keff, void *ws, hipStream_t st) {
-    LogitsArgs la;
-    la.x = x;
-    la.wr = L.router_w;
-    la.part = at<double>(ws, p.part);
-    la.T = T;
-    la.E = L.n_experts;
-    la.H = L.hidden;
-    la.kslice = p.rs.kslice;
-    hipError_t e = launch_router_logits(la, p.rs.S, st);
-    if (e != hipSuccess) return e;
+static SelectArgs select_args(const moe_layer &L, const Plan &p, int T, int32_t *ids, float *w,
+                              int32_t *keff, void *ws) {
     SelectArgs sa;
-    sa.part = la.part;
+    sa.part = at<double>(ws, p.part);
     sa.bias = L.router_bias;
     sa.ids = ids;
     sa.w = w;
@@ -174,12 +172,12 @@ static hipError_t run_route(const moe_layer &L, const Plan &p, const float *x, i
     sa.top_p = L.top_p;
     sa.routed_scale = L.routed_scale;
     sa.norm_topk = L.norm_topk ? 1 : 0;
-    return launch_route_select(sa, st);
+    return sa;
 }
 
-static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_t *keff, int T,
+static UnionArgs union_args(const moe_layer &L, const int32_t *ids, const int32_t *keff, int T,
                             int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
-                            int32_t *pick_row, hipStream_t st) {
+                            int32_t *pick_row) {
     UnionArgs ua;
     ua.ids = ids;
     ua.keff = keff;
@@ -191,7 +189,73 @@ static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_
     ua.T = T;
     ua.E = L.n_experts;
     ua.k = L.top_k;
-    return launch_union(ua, st);
+    return ua;
+}
+
+static hipError_t run_logits(const moe_layer &L, const Plan &p, const float *x, int T, void *ws,
+                             hipStream_t st) {
+    LogitsArgs la;
+    la.x = x;
+    la.wr = L.router_w;
+    la.part = at<double>(ws, p.part);
+    la.T = T;
+    la.E = L.n_experts;
+    la.H = L.hidden;
+    la.kslice = p.rs.kslice;
+    return launch_router_logits(la, p.rs.S, st);
+}
+
+static hipError_t run_route(const moe_layer &L, const Plan &p, const float *x, int T, int32_t *ids,
+                            float *w, int32_t *keff, void *ws, hipStream_t st) {
+    hipError_t e = run_logits(L, p, x, T, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_route_select(select_args(L, p, T, ids, w, keff, ws), st);
+}
+
+static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_t *keff, int T,
+                            int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
+                            int32_t *pick_row, hipStream_t st) {
+    return launch_union(union_args(L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
+}
+
+static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int k, void *ws) {
+    MfmaArgs m;
+    m.x = f.x;
+    m.x_frag = at<uint8_t>(ws, p.x_frag);
+    m.x_sx = at<float>(ws, p.x_sx);
+    m.n_uniq = f.n_uniq;
+    m.uniq = f.uniq;
+    m.off = f.off;
+    m.row_tok = f.row_tok;
+    m.gate = f.gate;
+    m.up = f.up;
+    m.down = f.down;
+    m.sh_gate = f.sh_gate;
+    m.sh_up = f.sh_up;
+    m.sh_down = f.sh_down;
+    m.h_routed = f.h_routed;
+    m.h_shared = f.h_shared;
+    m.hr_frag = at<uint8_t>(ws, p.hr_frag);
+    m.hs_frag = at<uint8_t>(ws, p.hs_frag);
+    m.hr_sx = at<float>(ws, p.hr_sx);
+    m.hs_sx = at<float>(ws, p.hs_sx);
+    m.y_routed = f.y_routed;
+    m.y_shared = f.y_shared;
+    m.T = f.T;
+    m.H = f.H;
+    m.F = f.F;
+    m.Fs = f.Fs;
+    m.max_units = f.max_units;
+    m.max_rows = f.T * k;
+    m.with_routed = f.with_routed;
+    m.with_shared = f.with_shared;
+    return m;
+}
+
+// grouped GEMVs for a handful of tokens, the matrix-core grouped GEMM above that
+static hipError_t run_ffn(const FfnArgs &f, const Plan &p, int k, void *ws, hipStream_t st) {
+    if (f.T <= kGemvMaxTokens) return launch_ffn_gemv(f, st);
+    return launch_ffn_mfma(mfma_args(f, p, k, ws), st);
 }
 
 static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T,
@@ -275,7 +339,7 @@ int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t 
     const Plan p = make_plan(*L, T);
     FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_rows, ws);
     a.with_shared = 0;
-    return launched(launch_ffn_gemv(a, (hipStream_t)stream));
+    return launched(run_ffn(a, p, L->top_k, ws, (hipStream_t)stream));
 }
 
 int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
@@ -303,12 +367,21 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     int32_t *row_tok = d.row_tok ? d.row_tok : at<int32_t>(ws, p.row_tok);
     int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
 
-    hipError_t e = run_route(*L, p, x, T, ids, w, keff, ws, st);
-    if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+    hipError_t e;
+    if (T <= kSelectUnionTokens) {
+        // small batch: selection and union in one workgroup
+        e = run_logits(*L, p, x, T, ws, st);
+        if (e == hipSuccess)
+            e = launch_select_union(select_args(*L, p, T, ids, w, keff, ws),
+                                    union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
+    } else {
+        e = run_route(*L, p, x, T, ids, w, keff, ws, st);
+        if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+    }
     float *y_routed = at<float>(ws, p.y_routed);
     if (e == hipSuccess) {
         FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
-        e = launch_ffn_gemv(a, st);
+        e = run_ffn(a, p, L->top_k, ws, st);
     }
     if (e == hipSuccess) {
         CombineArgs c;
@@ -325,6 +398,28 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
         e = launch_combine(c, st);
     }
     return launched(e);
+}
+
+int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t H, float eps,
+                         float *h_out, float *x_out, void *stream) {
+    if (T < 0 || H <= 0 || H % 64 || !isfinite(eps) || eps < 0.0f) return MOE_EINVAL;
+    if (H > MOE_MAX_DIM) return MOE_EUNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!h || !h_out || !x_out) return MOE_EINVAL;
+    if (x_out == h || (delta && x_out == delta)) return MOE_EINVAL;
+    if (!aligned16(h) || !aligned16(h_out) || !aligned16(x_out) || (delta && !aligned16(delta)))
+        return MOE_EALIGN;
+    int rc;
+    if ((rc = check_device())) return rc;
+    GlueArgs a;
+    a.h = h;
+    a.delta = delta;
+    a.h_out = h_out;
+    a.x_out = x_out;
+    a.T = T;
+    a.H = H;
+    a.eps = eps;
+    return launched(launch_residual_rmsnorm(a, (hipStream_t)stream));
 }
 
 const char *moe_strerror(int code) {

@@ -20,6 +20,7 @@ constexpr int kWave = 64;
 // experts per workgroup with a split over H so small batches still cover the chip.
 constexpr int kRouterTile = 64;
 constexpr int kRouterKC = 32;  // H elements staged per LDS step
+constexpr int kRouterGemvTokens = 8;  // at most this many tokens: one wave per expert instead
 
 struct RouterSplit {
     int S;       // number of H slices
@@ -39,6 +40,7 @@ struct Plan {
     size_t h_shared;  // fp32 [T][Fs]
     size_t y_routed;  // fp32 [T*k][H]  unweighted expert outputs per routed row
     size_t y_shared;  // fp32 [T][H]
+    size_t x_frag, x_sx, hr_frag, hr_sx, hs_frag, hs_sx;  // matrix-core path (T > kGemvMaxTokens)
     size_t total;
 };
 Plan make_plan(const moe_layer &L, int T);
@@ -83,6 +85,28 @@ struct FfnArgs {
     int with_routed, with_shared;
 };
 
+// The matrix-core path (more than kGemvMaxTokens tokens): FfnArgs plus the
+// activations prepared in MFMA fragment order (bf16 hi/lo, 256 bytes per row and
+// 64-group) with their per-group sums.
+constexpr int kGemvMaxTokens = 4;
+
+struct MfmaArgs {
+    const float *x;                  // [T][H]
+    uint8_t *x_frag;                 // [T][H/64][256]
+    float *x_sx;                     // [T][H/64]
+    const int32_t *n_uniq, *uniq, *off, *row_tok;
+    moe_q4 gate, up, down;
+    moe_q4 sh_gate, sh_up, sh_down;
+    float *h_routed, *h_shared;      // [rows][F], [T][Fs]
+    uint8_t *hr_frag, *hs_frag;      // h in fragment order
+    float *hr_sx, *hs_sx;
+    float *y_routed, *y_shared;      // [rows][H], [T][H]
+    int T, H, F, Fs, max_units, max_rows;
+    int with_routed, with_shared;
+};
+
+hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
+
 struct CombineArgs {
     const float *w;         // [T][k]
     const int32_t *keff;    // [T]
@@ -101,9 +125,20 @@ struct ProfScope {
     hipStream_t st;
 };
 
+struct GlueArgs {
+    const float *h, *delta;  // [T][H], delta may be null
+    float *h_out, *x_out;    // [T][H]
+    int T, H;
+    float eps;
+};
+
+hipError_t launch_residual_rmsnorm(const GlueArgs &a, hipStream_t st);
 hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st);
 hipError_t launch_route_select(const SelectArgs &a, hipStream_t st);
 hipError_t launch_union(const UnionArgs &a, hipStream_t st);
+// selection and union in one workgroup, for T <= kSelectUnionTokens
+constexpr int kSelectUnionTokens = 16;
+hipError_t launch_select_union(const SelectArgs &s, const UnionArgs &u, hipStream_t st);
 hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 

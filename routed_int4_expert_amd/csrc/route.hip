@@ -1,11 +1,14 @@
 // route.hip -- steps 1 and 2 of the MoE layer on gfx950: router logits and
 // noaux_tc sigmoid selection ("MoE 路由与专家流式加载" §1.1, §1.2).
 //
-// Logits: each workgroup owns a 64-token x 64-expert tile and one slice of H.
-// fp32 tiles of x and Wr are staged through LDS; every thread accumulates a 4x4
-// register micro-tile in fp64 (fp32 x fp32 products are exact in fp64).  The
-// per-slice partial sums go to the workspace and are added, in slice order, by
-// the selection kernel, so the result does not depend on scheduling.
+// Logits, few tokens (T <= 8): one wave per expert streams the expert's router
+// row once (lanes across H) and applies it to every token, accumulating in fp64
+// (fp32 x fp32 products are exact in fp64).
+// Logits, more tokens: each workgroup owns a 64-token x 64-expert tile and one
+// slice of H; fp32 tiles of x and Wr are staged through LDS and every thread
+// accumulates a 4x4 register micro-tile in fp64.  The per-slice partial sums go
+// to the workspace and are added, in slice order, by the selection kernel, so
+// the result does not depend on scheduling.
 //
 // Selection: one wave per token.  Each lane holds up to four experts' sigmoid
 // and biased choice score in fp64; the k picks are k wave-wide argmax
@@ -14,15 +17,21 @@
 // identically in every lane.
 #include <math.h>
 
-#include "moe_internal.h"
+#include "select_union.h"
 
 namespace moe {
 
 RouterSplit router_split(int T, int E, int H) {
+    if (T <= kRouterGemvTokens) {  // one wave per expert, whole H: no split
+        RouterSplit r;
+        r.S = 1;
+        r.kslice = H;
+        return r;
+    }
     const int tiles = ((T + kRouterTile - 1) / kRouterTile) * ((E + kRouterTile - 1) / kRouterTile);
     const int chunks = H / kRouterKC;
     int S = (256 + tiles - 1) / tiles;
-    if (S > 32) S = 32;
+    if (S > 16) S = 16;
     if (S > chunks) S = chunks;
     if (S < 1) S = 1;
     const int per = (chunks + S - 1) / S;
@@ -92,170 +101,98 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LogitsArgs a) {
     }
 }
 
+// Few tokens: one workgroup per expert; its four waves split H, every lane
+// issues all its float4 loads of the router row at once, the row is applied to
+// every token with fp64 accumulation, and the four wave sums are added in a
+// fixed order.  Complete logits, a single slice (S = 1).
+template <int TT>
+__global__ __launch_bounds__(256) void router_gemv_kernel(LogitsArgs a) {
+    __shared__ double red[4][TT];
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int n4 = a.H / 4;
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.H);
+    const float4 *x4 = reinterpret_cast<const float4 *>(a.x);
+    double acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) acc[t] = 0.0;
+#pragma unroll 8
+    for (int j = threadIdx.x; j < n4; j += 256) {
+        const float4 w = w4[j];
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+            if (t < a.T) {
+                const float4 v = x4[(size_t)t * n4 + j];
+                acc[t] = fma((double)v.x, (double)w.x, acc[t]);
+                acc[t] = fma((double)v.y, (double)w.y, acc[t]);
+                acc[t] = fma((double)v.z, (double)w.z, acc[t]);
+                acc[t] = fma((double)v.w, (double)w.w, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+#pragma unroll
+        for (int m = kWave / 2; m > 0; m >>= 1) acc[t] += shfl_xor_f64(acc[t], m);
+        if (lane == 0) red[wv][t] = acc[t];
+    }
+    __syncthreads();
+    if (threadIdx.x < TT && (int)threadIdx.x < a.T) {
+        const int t = threadIdx.x;
+        a.part[(size_t)t * a.E + e] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+    }
+}
+
 hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st) {
-    dim3 grid((a.T + kRouterTile - 1) / kRouterTile, (a.E + kRouterTile - 1) / kRouterTile, S);
     ProfScope prof("router_logits", st);
+    if (S == 1 && a.T <= kRouterGemvTokens) {
+        const int blocks = a.E;
+        if (a.T == 1) router_gemv_kernel<1><<<blocks, 256, 0, st>>>(a);
+        else if (a.T <= 2) router_gemv_kernel<2><<<blocks, 256, 0, st>>>(a);
+        else if (a.T <= 4) router_gemv_kernel<4><<<blocks, 256, 0, st>>>(a);
+        else router_gemv_kernel<kRouterGemvTokens><<<blocks, 256, 0, st>>>(a);
+        return hipGetLastError();
+    }
+    dim3 grid((a.T + kRouterTile - 1) / kRouterTile, (a.E + kRouterTile - 1) / kRouterTile, S);
     router_logits_kernel<<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ selection
-__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
-    const int lo = __shfl_xor(__double2loint(v), m, kWave);
-    const int hi = __shfl_xor(__double2hiint(v), m, kWave);
-    return __hiloint2double(hi, lo);
-}
-
-__device__ __forceinline__ double shfl_f64(double v, int src) {
-    const int lo = __shfl(__double2loint(v), src, kWave);
-    const int hi = __shfl(__double2hiint(v), src, kWave);
-    return __hiloint2double(hi, lo);
-}
-
 __global__ __launch_bounds__(256) void route_select_kernel(SelectArgs a) {
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= a.T) return;  // whole wave leaves together
-
-    constexpr int EPL = MOE_MAX_EXPERTS / kWave;  // experts per lane (4)
-    double sig[EPL], ch[EPL];
-    bool live[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-        const int e = lane + kWave * i;
-        live[i] = e < a.E;
-        sig[i] = 0.0;
-        ch[i] = -INFINITY;
-        if (live[i]) {
-            double l = 0.0;
-            for (int s = 0; s < a.S; s++) l += a.part[((size_t)s * a.T + t) * a.E + e];
-            sig[i] = 1.0 / (1.0 + exp(-l));
-            const double b = a.bias ? (double)a.bias[e] : 0.0;
-            const double c = sig[i] + b;
-            ch[i] = isnan(c) ? -INFINITY : c;
-        }
-    }
-
-    // k picks, identical in every lane after each reduction
-    int pid[MOE_MAX_TOPK];
-    double psig[MOE_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; j++) {
-        pid[j] = -1;
-        psig[j] = 0.0;
-        if (j >= a.k) continue;
-        double bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < EPL; i++) {
-            if (!live[i]) continue;
-            if (bi == 0x7fffffff || ch[i] > bv) {  // e grows with i: strict > keeps the lower id
-                bv = ch[i];
-                bi = lane + kWave * i;
-            }
-        }
-#pragma unroll
-        for (int m = kWave / 2; m > 0; m >>= 1) {
-            const double ov = shfl_xor_f64(bv, m);
-            const int oi = __shfl_xor(bi, m, kWave);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        const int owner = bi % kWave, slot = bi / kWave;
-        double mysig = 0.0;
-#pragma unroll
-        for (int i = 0; i < EPL; i++)
-            if (i == slot) mysig = sig[i];
-        psig[j] = shfl_f64(mysig, owner);
-        pid[j] = bi;
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i < EPL; i++)
-                if (i == slot) live[i] = false;
-        }
-    }
-
-    // adaptive top-p: rank of each pick by sig descending, equal sigs in slot order
-    bool keep[MOE_MAX_TOPK];
-    int keff = a.k;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; j++) keep[j] = j < a.k;
-    if (a.top_p > 0.0f && a.top_p < 1.0f) {
-        int rank[MOE_MAX_TOPK];
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_TOPK; j++) {
-            int r = 0;
-#pragma unroll
-            for (int i = 0; i < MOE_MAX_TOPK; i++)
-                if (i < a.k && j < a.k && (psig[i] > psig[j] || (psig[i] == psig[j] && i < j))) r++;
-            rank[j] = r;
-        }
-        // total and running sums in rank order
-        double tot = 0.0;
-#pragma unroll
-        for (int r = 0; r < MOE_MAX_TOPK; r++)
-#pragma unroll
-            for (int j = 0; j < MOE_MAX_TOPK; j++)
-                if (j < a.k && r < a.k && rank[j] == r) tot += psig[j];
-        const double thr = (double)a.top_p * tot;
-        double cum = 0.0;
-        int m = a.k;
-        bool done = false;
-#pragma unroll
-        for (int r = 0; r < MOE_MAX_TOPK; r++)
-#pragma unroll
-            for (int j = 0; j < MOE_MAX_TOPK; j++)
-                if (!done && j < a.k && r < a.k && rank[j] == r) {
-                    cum += psig[j];
-                    if (cum >= thr) {
-                        m = r + 1;
-                        done = true;
-                    }
-                }
-        keff = m;
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_TOPK; j++) keep[j] = j < a.k && rank[j] < m;
-    }
-
-    double denom = 0.0;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; j++)
-        if (keep[j]) denom += psig[j];
-
-    // lane j writes the output slot of pick j (kept picks compacted in slot order)
-    int pos = 0;
-    bool mine_kept = false;
-    double g = 0.0;
-    int gid = -1;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; j++) {
-        if (j == lane && keep[j]) {
-            mine_kept = true;
-            g = psig[j];
-            gid = pid[j];
-        }
-        if (j < lane && keep[j]) pos++;
-    }
-    int32_t *ids = a.ids + (size_t)t * a.k;
-    float *w = a.w + (size_t)t * a.k;
-    if (lane < a.k && mine_kept) {
-        if (a.norm_topk) g = g / denom;
-        g = g * (double)a.routed_scale;
-        ids[pos] = gid;
-        w[pos] = (float)g;
-    }
-    if (lane >= keff && lane < a.k) {
-        ids[lane] = -1;
-        w[lane] = 0.0f;
-    }
-    if (lane == 0) a.keff[t] = keff;
+    select_token(a, t, lane, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.keff + t, nullptr,
+                 nullptr);
 }
 
 hipError_t launch_route_select(const SelectArgs &a, hipStream_t st) {
     ProfScope prof("route_select", st);
     route_select_kernel<<<(a.T + 3) / 4, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+// Small batches: one workgroup selects every token (a wave each) and builds the
+// union from the picks it keeps in LDS, saving a launch and a round trip.
+__global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionArgs u) {
+    extern __shared__ uint32_t lds[];
+    int32_t *ids_l = reinterpret_cast<int32_t *>(lds);
+    int32_t *keff_l = ids_l + s.T * s.k;
+    uint32_t *scratch = reinterpret_cast<uint32_t *>(keff_l + s.T);
+    const int lane = threadIdx.x % kWave;
+    const int t = threadIdx.x / kWave;
+    if (t < s.T)
+        select_token(s, t, lane, s.ids + (size_t)t * s.k, s.w + (size_t)t * s.k, s.keff + t,
+                     ids_l + t * s.k, keff_l + t);
+    __syncthreads();
+    union_block(u, ids_l, keff_l, scratch);
+}
+
+hipError_t launch_select_union(const SelectArgs &s, const UnionArgs &u, hipStream_t st) {
+    const size_t lds = ((size_t)s.T * s.k + s.T + union_lds_words(u.E, u.T)) * sizeof(uint32_t);
+    ProfScope prof("select_union", st);
+    select_union_kernel<<<1, 1024, lds, st>>>(s, u);
     return hipGetLastError();
 }
 

@@ -122,6 +122,22 @@ def test_other_entry_points_validate():
     assert L.moe_route(r, None, 0, None, None, None, None, 0, None) == M.MOE_OK
 
 
+def test_residual_rmsnorm_validation():
+    L = M.lib()
+    f = L.moe_residual_rmsnorm
+    a, b, c, d = 0x10000, 0x20000, 0x30000, 0x40000
+    assert f(a, b, 4, 100, 1e-6, c, d, None) == M.MOE_EINVAL          # H not a multiple of 64
+    assert f(a, b, -1, 128, 1e-6, c, d, None) == M.MOE_EINVAL
+    assert f(a, b, 4, 128, -1.0, c, d, None) == M.MOE_EINVAL          # negative eps
+    assert f(a, b, 4, 128, float("nan"), c, d, None) == M.MOE_EINVAL
+    assert f(a, b, 4, 32768, 1e-6, c, d, None) == M.MOE_EUNSUPPORTED
+    assert f(None, b, 4, 128, 1e-6, c, d, None) == M.MOE_EINVAL
+    assert f(a, b, 4, 128, 1e-6, c, a, None) == M.MOE_EINVAL          # x_out aliases h
+    assert f(a, b, 4, 128, 1e-6, c, b, None) == M.MOE_EINVAL          # x_out aliases delta
+    assert f(a + 4, b, 4, 128, 1e-6, c, d, None) == M.MOE_EALIGN
+    assert f(None, None, 0, 128, 1e-6, None, None, None) == M.MOE_OK  # T == 0
+
+
 def test_strerror():
     for code in (0, -1, -2, -3, -4, -5):
         s = M.strerror(code)

@@ -126,11 +126,13 @@ def test_deterministic_bitwise():
 
 
 def test_zero_gate_expert_rows_are_exactly_zero():
-    # SiLU(0) = 0: experts whose gate codes are all zero give exactly zero rows
+    # SiLU(0) = 0: an all-zero gate matrix (as the quantiser stores it: codes 0, scales 0)
+    # gives exactly zero expert rows
     sh = S.custom("zerogate", hidden=256, n_experts=16, ffn=128, shared_ffn=128, top_k=4, tokens=8)
     d = S.make_layer(sh)
-    d["gate_q"] = d["gate_q"].copy()
+    d["gate_q"], d["gate_s"] = d["gate_q"].copy(), d["gate_s"].copy()
     d["gate_q"][::2] = 0
+    d["gate_s"][::2] = 0.0
     x = S.make_batch(sh, d)
     layer = M.Layer.from_host(d, DEV)
     xd = torch.from_numpy(x).to(DEV)
@@ -205,12 +207,11 @@ def test_glm_decode_workload(glm_bank):
         ref = R.layer_forward(Lr, x)
         rel, mx = assert_close(out.cpu().numpy(), ref, "glm decode layer")
         # bf16 mode: exactly the RNE of the fp32 result, hence within half a bf16 ulp
-        # (at most 2^-8 relative) plus the fp32 path's own error of the oracle
+        # (at most 2^-8 relative) plus the fp32 result's own largest error (mx)
         got_bits = out_bf.view(torch.int16).cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(got_bits, R.to_bf16_bits(out.cpu().numpy().astype(np.float64)))
         got_bf = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        rms = np.sqrt((ref ** 2).mean())
-        assert np.all(np.abs(got_bf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms), "bf16 output"
+        assert np.all(np.abs(got_bf - ref) <= 2.0 ** -8 * np.abs(ref) + 1.01 * mx), "bf16 output"
         say(f"GLM decode pool {pool}: ids {ids.cpu().numpy().tolist()} rel-L2 {rel:.2e} max-abs {mx:.2e}")
 
 
@@ -237,3 +238,41 @@ def test_glm_prefill_workload(glm_bank):
     ref = R.layer_forward(R.Layer(d), x, toks=toks)
     rel, mx = assert_close(out.cpu().numpy()[toks], ref, "glm prefill sampled tokens")
     say(f"GLM prefill sampled: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_glm_stack16_workload(glm_bank):
+    """16 GLM-shaped layers, 32 tokens, top-p 0.7, Zipf-skewed bias; RMSNorm + residual
+    glue between layers.  Teacher-forced per layer: the oracle takes the GPU's normalised
+    input of that layer.  Routing, keff and the union exact for all tokens; outputs of
+    sampled tokens within tolerance; the glue against the oracle's RMSNorm."""
+    sh = S.SHAPES["glm_stack16"]
+    T = sh.tokens
+    base = {k: torch.from_numpy(getattr(glm_bank, k)).to(DEV) for k in S.Bank.ROUTED + S.Bank.SHARED}
+    h = torch.from_numpy(S.tokens(sh, T, seed=0)).to(DEV)
+    out = None
+    keffs = []
+    for l in range(sh.layers):
+        say(f"stack layer {l}")
+        h, x = M.moe_residual_rmsnorm(h, out)
+        torch.cuda.synchronize()
+        h_host, x_host = h.cpu().numpy(), x.cpu().numpy()
+        np.testing.assert_allclose(x_host, R.rmsnorm(h_host), rtol=2e-6, atol=2e-6)
+        rw, rb = S.router(sh, 0, l)
+        perm = S.layer_perm(sh, 0, l)
+        ts = {k: base[k].index_select(0, torch.from_numpy(perm).to(DEV)) for k in S.Bank.ROUTED}
+        ts.update({k: base[k] for k in S.Bank.SHARED})
+        ts["router_w"], ts["router_bias"] = torch.from_numpy(rw).to(DEV), torch.from_numpy(rb).to(DEV)
+        layer = M.Layer(S.layer_params(sh), ts)
+        d = S.make_layer(sh, seed=0, layer=l, bank=glm_bank)
+        ids, w, keff, rids, rw_, rkeff = check_routing(d, layer, x_host, x, sh)
+        un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+        out = M.moe_layer_forward(layer, x)
+        torch.cuda.synchronize()
+        toks = [l % T, (7 * l + 3) % T]
+        ref = R.layer_forward(R.Layer(d), x_host, toks=toks)
+        rel, mx = assert_close(out.cpu().numpy()[toks], ref, f"stack layer {l}")
+        keffs.append(float(rkeff.mean()))
+        say(f"stack layer {l}: union {ru['n_uniq']}, mean keff {rkeff.mean():.2f}, rel-L2 {rel:.2e}")
+        del ts, layer, d
+    assert min(keffs) < sh.top_k  # top-p 0.7 actually drops picks
