@@ -110,7 +110,16 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read_per_copy": n * 4, "copies": 3}), flush=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"copy_probe_bytes_read_per_copy": n * 4, "copies": 13,
+                          "copy_ms": ms, "copy_read_plus_write_gbps": 2 * n * 4 / (ms * 1e-3) / 1e9}),
+              flush=True)
         return
 
     dev = "cuda:0"
