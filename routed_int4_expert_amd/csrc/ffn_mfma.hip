@@ -15,7 +15,9 @@
 //    at -136 * sum(x) (the unsigned-offset identity of §2.2, K1), and its result
 //    is scaled by the fp32 group scale into the fp32 running sum.
 // A workgroup owns 32 rows x 128 outputs (4 waves x 32); K is staged through
-// LDS eight groups at a time.  Outputs of a row have one owner: deterministic.
+// LDS eight groups at a time with asynchronous global-to-LDS loads, while the
+// chunk's weight codes are already in flight into registers.  Outputs of a row
+// have one owner: deterministic.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -177,15 +179,33 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
         f32x16_t acc0 = {}, acc1 = {};
         for (int g0 = 0; g0 < NG; g0 += kChunkGroups) {
             const int ng = min(kChunkGroups, NG - g0);
+            // this chunk's codes and scales first: their latency overlaps the staging below
+            uint4 cq0[kChunkGroups], cq1[kChunkGroups];
+            float cs0[kChunkGroups], cs1[kChunkGroups];
+#pragma unroll
+            for (int g = 0; g < kChunkGroups; g++) {
+                const int G = g0 + min(g, ng - 1);  // past the end: re-read the last group
+                cq0[g] = *reinterpret_cast<const uint4 *>(q0 + 32 * G);
+                cs0[g] = s0[G];
+                if (GU) {
+                    cq1[g] = *reinterpret_cast<const uint4 *>(q1 + 32 * G);
+                    cs1[g] = s1[G];
+                }
+            }
             __syncthreads();  // previous chunk consumed
-            // stage rows [rc, rc+R) x groups [g0, g0+ng) (16-byte copies) and their sums
-            const int per_row = ng * (kGroupBytes / 16);
-            for (int i = tid; i < R * per_row; i += blockDim.x) {
-                const int r = i / per_row, w = i % per_row;
+            // stage rows [rc, rc+R) x groups [g0, g0+ng) straight into LDS: a row's chunk is
+            // at most 2 KB, copied as 1-KB pieces, one asynchronous wave instruction each
+            // (lane L moves bytes 16L..16L+15); lanes past the chunk re-read its start and
+            // land in the row's unused tail
+            const int bytes = ng * kGroupBytes;
+            const int pieces = (bytes + 1023) / 1024;
+            for (int pc = wv; pc < R * pieces; pc += 256 / kWave) {
+                const int r = pc / pieces, h = pc % pieces;
                 const int src = rt ? rt[rc + r] : rc + r;
-                const uint4 v = *reinterpret_cast<const uint4 *>(
-                    afrag + ((size_t)src * NG + g0) * kGroupBytes + 16 * w);
-                *reinterpret_cast<uint4 *>(atile + r * kRowPitch + 16 * w) = v;
+                int off = h * 1024 + lane * 16;
+                if (off >= bytes) off = 0;
+                __builtin_amdgcn_global_load_lds(afrag + ((size_t)src * NG + g0) * kGroupBytes + off,
+                                                 atile + r * kRowPitch + h * 1024, 16, 0, 0);
             }
             for (int i = tid; i < kTileRows * ng; i += blockDim.x) {
                 const int r = i % kTileRows, g = i / kTileRows;
@@ -197,12 +217,9 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
                 sxt[g][r] = v;
             }
             __syncthreads();
-            for (int g = 0; g < ng; g++) {
-                const int G = g0 + g;
-                const uint4 c0 = *reinterpret_cast<const uint4 *>(q0 + 32 * G);
-                const uint4 c1 = GU ? *reinterpret_cast<const uint4 *>(q1 + 32 * G) : c0;
-                const float sc0 = s0[G];
-                const float sc1 = GU ? s1[G] : sc0;
+#pragma unroll
+            for (int g = 0; g < kChunkGroups; g++) {
+                if (g >= ng) break;
                 // group accumulators start at -136 * sum(x) of their row
                 f32x16_t ga;
 #pragma unroll
@@ -214,8 +231,8 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
                     ga[4 * q4 + 3] = -kMfmaCodeOffset * sv.w;
                 }
                 f32x16_t g0acc = ga, g1acc = ga;
-                const uint32_t w0[4] = {c0.x, c0.y, c0.z, c0.w};
-                const uint32_t w1[4] = {c1.x, c1.y, c1.z, c1.w};
+                const uint32_t w0[4] = {cq0[g].x, cq0[g].y, cq0[g].z, cq0[g].w};
+                const uint32_t w1[4] = {cq1[g].x, cq1[g].y, cq1[g].z, cq1[g].w};
                 const uint8_t *arow = atile + ln * kRowPitch + g * kGroupBytes + kg * 128;
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
@@ -232,8 +249,8 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
                 }
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
-                    acc0[v] = fmaf(sc0, g0acc[v], acc0[v]);
-                    if (GU) acc1[v] = fmaf(sc1, g1acc[v], acc1[v]);
+                    acc0[v] = fmaf(cs0[g], g0acc[v], acc0[v]);
+                    if (GU) acc1[v] = fmaf(cs1[g], g1acc[v], acc1[v]);
                 }
             }
         }

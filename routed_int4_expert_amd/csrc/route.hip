@@ -160,11 +160,13 @@ hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st) {
 
 // ------------------------------------------------------------------ selection
 __global__ __launch_bounds__(256) void route_select_kernel(SelectArgs a) {
+    __shared__ PickScratch ps[256 / kWave];
     const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int wv = threadIdx.x / kWave;
+    const int t = blockIdx.x * 4 + wv;
     if (t >= a.T) return;  // whole wave leaves together
     select_token(a, t, lane, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.keff + t, nullptr,
-                 nullptr);
+                 nullptr, &ps[wv]);
 }
 
 hipError_t launch_route_select(const SelectArgs &a, hipStream_t st) {
@@ -176,6 +178,7 @@ hipError_t launch_route_select(const SelectArgs &a, hipStream_t st) {
 // Small batches: one workgroup selects every token (a wave each) and builds the
 // union from the picks it keeps in LDS, saving a launch and a round trip.
 __global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionArgs u) {
+    __shared__ PickScratch ps[kSelectUnionTokens];
     extern __shared__ uint32_t lds[];
     int32_t *ids_l = reinterpret_cast<int32_t *>(lds);
     int32_t *keff_l = ids_l + s.T * s.k;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionA
     const int t = threadIdx.x / kWave;
     if (t < s.T)
         select_token(s, t, lane, s.ids + (size_t)t * s.k, s.w + (size_t)t * s.k, s.keff + t,
-                     ids_l + t * s.k, keff_l + t);
+                     ids_l + t * s.k, keff_l + t, &ps[t]);
     __syncthreads();
     union_block(u, ids_l, keff_l, scratch);
 }

@@ -23,24 +23,47 @@ __device__ __forceinline__ double readlane_f64(double v, int src) {
     return __hiloint2double(hi, lo);
 }
 
+// Larger double -> larger unsigned key (finite values and -inf; NaN excluded).
+__device__ __forceinline__ unsigned long long mono_key(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Per-wave LDS scratch of select_token: the k picks, compacted then ranked.
+struct PickScratch {
+    unsigned long long key[MOE_MAX_TOPK];
+    double sig[MOE_MAX_TOPK];
+    int id[MOE_MAX_TOPK];
+    int ord_id[MOE_MAX_TOPK];
+    double ord_sig[MOE_MAX_TOPK];
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // One token, one wave.  [R] §1.1: sig = sigmoid(logit) and choice = sig + bias,
-// in fp64; [R] §1.2: k rounds of argmax over choice excluding taken experts
-// (equal scores: lower id), adaptive top-p over the k gates, norm_topk, scale.
-// Lane j < k holds pick j.  Writes ids/w (this token's k slots) and *keff; when
-// ids_copy/keff_copy are given, the ids and keff are written there too.
+// in fp64; [R] §1.2: the k experts with the largest choice (the same set and order
+// as k rounds of argmax excluding taken experts, equal scores going to the lower
+// id), adaptive top-p over the k gates, norm_topk, routed scale.
+// The k-th largest choice is found exactly by a bitwise search on monotone 64-bit
+// keys (each step counts keys >= a candidate with one ballot per slot); the picks
+// are then compacted into LDS and ranked (choice descending, lower id first).
+// Lane j < k ends up holding pick j.  Writes ids/w (this token's k slots) and
+// *keff; when ids_copy/keff_copy are given, the ids and keff are written there too.
 __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
                                              float *w, int32_t *keff_out, int32_t *ids_copy,
-                                             int32_t *keff_copy) {
+                                             int32_t *keff_copy, PickScratch *ps) {
     constexpr int EPL = MOE_MAX_EXPERTS / kWave;  // experts per lane (4)
-    double sig[EPL], ch[EPL];
-    bool live[EPL];
+    double sig[EPL];
+    unsigned long long key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const int e = lane + kWave * i;
-        live[i] = e < a.E;
         sig[i] = 0.0;
-        ch[i] = -INFINITY;
-        if (live[i]) {
+        key[i] = 0ull;  // below every live key
+        if (e < a.E) {
             // slice partials added in slice order; loads issued eight at a time
             double l = 0.0;
             int s = 0;
@@ -55,47 +78,66 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
             sig[i] = 1.0 / (1.0 + exp(-l));
             const double b = a.bias ? (double)a.bias[e] : 0.0;
             const double c = sig[i] + b;
-            ch[i] = isnan(c) ? -INFINITY : c;
+            key[i] = mono_key(isnan(c) ? -INFINITY : c);
         }
     }
 
+    // thr = the k-th largest key: the largest value with at least k keys >= it
+    unsigned long long thr = 0ull;
+    for (int bit = 63; bit >= 0; bit--) {
+        const unsigned long long cand = thr | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) cnt += __popcll(__ballot(key[i] >= cand));
+        if (cnt >= a.k) thr = cand;
+    }
+    // every key above thr is picked; among keys equal to thr the lowest ids fill up to k
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int cgt = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) cgt += __popcll(__ballot(key[i] > thr));
+    const int need = a.k - cgt;
+    bool sel[EPL];
+    int eq_before = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const unsigned long long eqm = __ballot(key[i] == thr && (lane + kWave * i) < a.E);
+        const int r = eq_before + __popcll(eqm & below);
+        sel[i] = key[i] > thr || (((eqm >> lane) & 1ull) && r < need);
+        eq_before += __popcll(eqm);
+    }
+    // compact the k picks into LDS (expert order)
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const unsigned long long sm = __ballot(sel[i]);
+        if (sel[i]) {
+            const int pos = base + __popcll(sm & below);
+            ps->key[pos] = key[i];
+            ps->sig[pos] = sig[i];
+            ps->id[pos] = lane + kWave * i;
+        }
+        base += __popcll(sm);
+    }
+    wave_lds_sync();
+    // lane j < k ranks pick j: choice descending, equal choices by lower id
+    if (lane < a.k) {
+        const unsigned long long mk = ps->key[lane];
+        const int mid = ps->id[lane];
+        int rank = 0;
+        for (int i = 0; i < a.k; i++) {
+            const unsigned long long ok = ps->key[i];
+            rank += (ok > mk || (ok == mk && ps->id[i] < mid)) ? 1 : 0;
+        }
+        ps->ord_id[rank] = mid;
+        ps->ord_sig[rank] = ps->sig[lane];
+    }
+    wave_lds_sync();
     int my_id = -1;
     double my_sig = 0.0;
-    for (int j = 0; j < a.k; j++) {
-        double bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < EPL; i++) {
-            if (live[i] && (bi == 0x7fffffff || ch[i] > bv)) {  // e grows with i: strict > keeps the lower id
-                bv = ch[i];
-                bi = lane + kWave * i;
-            }
-        }
-#pragma unroll
-        for (int m = kWave / 2; m > 0; m >>= 1) {
-            const double ov = shfl_xor_f64(bv, m);
-            const int oi = __shfl_xor(bi, m, kWave);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        bi = __builtin_amdgcn_readfirstlane(bi);  // identical in every lane
-        const int owner = bi % kWave, slot = bi / kWave;
-        double s_own = sig[0];
-#pragma unroll
-        for (int i = 1; i < EPL; i++)
-            if (i == slot) s_own = sig[i];
-        const double ps = readlane_f64(s_own, owner);
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i < EPL; i++)
-                if (i == slot) live[i] = false;
-        }
-        if (lane == j) {
-            my_id = bi;
-            my_sig = ps;
-        }
+    if (lane < a.k) {
+        my_id = ps->ord_id[lane];
+        my_sig = ps->ord_sig[lane];
     }
 
     // adaptive top-p: rank of each pick by sig descending (equal sigs in slot order);
@@ -114,13 +156,13 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
             const unsigned long long m = __ballot(act && rank == r);
             tot += readlane_f64(my_sig, __ffsll((long long)m) - 1);
         }
-        const double thr = (double)a.top_p * tot;
+        const double thr_p = (double)a.top_p * tot;
         double cum = 0.0;
         int kept = a.k;
         for (int r = 0; r < a.k; r++) {
             const unsigned long long m = __ballot(act && rank == r);
             cum += readlane_f64(my_sig, __ffsll((long long)m) - 1);
-            if (cum >= thr) {
+            if (cum >= thr_p) {
                 kept = r + 1;
                 break;
             }
@@ -134,7 +176,7 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
     double denom = 0.0;
     for (int j = 0; j < a.k; j++)
         if ((km >> j) & 1ull) denom += readlane_f64(my_sig, j);
-    const int pos = __popcll(km & ((1ull << lane) - 1ull));
+    const int pos = __popcll(km & below);
     if (keep) {
         double g = my_sig;
         if (a.norm_topk) g = g / denom;
@@ -157,25 +199,28 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
 // LDS words union_block needs for E experts and T tokens.
 __host__ __device__ inline size_t union_lds_words(int E, int T) {
     const int W = (T + 31) / 32;
-    return (size_t)E * W + 2 * (size_t)E + 1;
+    const int W8 = (W + 7) / 8;
+    return (size_t)E * W + (size_t)E * W8 + 2 * (size_t)E + 1;
 }
 
 // The batch union ([R] §1.3), by a whole block: every kept (token, expert) pick
 // sets a bit in a per-expert token bitmap (LDS atomicOr: the result does not
 // depend on their order); counts are popcounts, offsets and the distinct-expert
-// list exclusive scans by one wave; each expert's rows are then emitted in token
-// order by one wave (a scan of per-word popcounts ranks every set bit), so the
-// outputs need no atomics and are deterministic.  ids/keff may live in LDS or
-// global memory.
+// list exclusive scans by one wave.  A pick's row is its expert's offset plus the
+// number of earlier tokens of that expert -- a per-8-word prefix count plus at
+// most eight popcounts -- so every pick is placed independently, without atomics,
+// and the result is deterministic.  ids/keff may live in LDS or global memory.
 __device__ __forceinline__ void union_block(const UnionArgs &a, const int32_t *ids,
                                             const int32_t *keff, uint32_t *lds) {
     const int E = a.E, T = a.T, k = a.k;
     const int W = (T + 31) / 32;
+    const int W8 = (W + 7) / 8;
     uint32_t *hit = lds;                                              // [E][W]
-    int32_t *cnt = reinterpret_cast<int32_t *>(hit + (size_t)E * W);  // [E]
+    int32_t *pre8 = reinterpret_cast<int32_t *>(hit + (size_t)E * W); // [E][W8]
+    int32_t *cnt = pre8 + (size_t)E * W8;                             // [E]
     int32_t *offs = cnt + E;                                          // [E+1]
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, wave = tid / kWave, nwaves = blockDim.x / kWave;
+    const int lane = tid % kWave, wave = tid / kWave;
 
     for (int i = tid; i < E * W; i += blockDim.x) hit[i] = 0u;
     __syncthreads();
@@ -186,9 +231,13 @@ __device__ __forceinline__ void union_block(const UnionArgs &a, const int32_t *i
         if (j < ke && e >= 0 && e < E) atomicOr(&hit[e * W + t / 32], 1u << (t % 32));
     }
     __syncthreads();
+    // per expert: running popcount, recorded every 8 words, and the total
     for (int e = tid; e < E; e += blockDim.x) {
         int c = 0;
-        for (int w = 0; w < W; w++) c += __popc(hit[e * W + w]);
+        for (int w = 0; w < W; w++) {
+            if (w % 8 == 0) pre8[e * W8 + w / 8] = c;
+            c += __popc(hit[e * W + w]);
+        }
         cnt[e] = c;
     }
     __syncthreads();
@@ -238,40 +287,23 @@ __device__ __forceinline__ void union_block(const UnionArgs &a, const int32_t *i
 
     const int rows = offs[E];
     for (int r = rows + tid; r < T * k; r += blockDim.x) a.row_tok[r] = -1;
+    // every pick: row = off[e] + (tokens before t routed to e); rows run (expert, token)
     for (int p = tid; p < T * k; p += blockDim.x) {
         const int t = p / k, j = p % k;
         const int ke = min(max(keff[t], 0), k);
         const int e = ids[p];
-        if (!(j < ke && e >= 0 && e < E)) a.pick_row[p] = -1;
-    }
-
-    // rows of each expert in token order
-    for (int e = wave; e < E; e += nwaves) {
-        if (cnt[e] == 0) continue;
-        int run = offs[e];
-        for (int w0 = 0; w0 < W; w0 += kWave) {
-            const int w = w0 + lane;
-            uint32_t bits = w < W ? hit[e * W + w] : 0u;
-            const int pc = __popc(bits);
-            int inc = pc;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const int o = __shfl_up(inc, d, kWave);
-                if (lane >= d) inc += o;
-            }
-            int r = run + inc - pc;
-            while (bits) {
-                const int b = __ffs(bits) - 1;
-                bits &= bits - 1;
-                const int t = w * 32 + b;
-                a.row_tok[r] = t;
-                const int ke = min(max(keff[t], 0), k);
-                for (int j = 0; j < ke; j++)
-                    if (ids[(size_t)t * k + j] == e) a.pick_row[(size_t)t * k + j] = r;
-                r++;
-            }
-            run += __shfl(inc, kWave - 1, kWave);
+        if (!(j < ke && e >= 0 && e < E)) {
+            a.pick_row[p] = -1;
+            continue;
         }
+        const int w = t / 32;
+        const uint32_t *he = hit + (size_t)e * W;
+        int rank = pre8[e * W8 + w / 8];
+        for (int v = (w / 8) * 8; v < w; v++) rank += __popc(he[v]);
+        rank += __popc(he[w] & ((1u << (t % 32)) - 1u));
+        const int r = offs[e] + rank;
+        a.pick_row[p] = r;
+        a.row_tok[r] = t;
     }
 }
 
