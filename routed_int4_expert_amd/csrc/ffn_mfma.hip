@@ -1,23 +1,32 @@
 // ffn_mfma.hip -- step 4 of the MoE layer on gfx950 for larger row counts: the
-// int4-gs64 SwiGLU expert FFN as an LDS-tiled grouped GEMM on the matrix cores
+// int4-gs64 SwiGLU expert FFN as a grouped GEMM on the matrix cores
 // ("MoE 路由与专家流式加载" §1.3: gate, up, SiLU, down for every union expert,
 // each expert's weights read once for all rows routed to it; §1.4: the shared
 // expert on every token).
 //
-// D[rows][outputs] = X[rows][K] * W[outputs][K]^T with v_mfma_f32_32x32x16_bf16:
-//  - B (weights): a lane's 16-byte load holds 32 consecutive codes of one
-//    output row; each 32-bit word of 8 codes becomes 4 bf16 pairs of (136 + q)
-//    by one bit operation each (0x4300 is 128.0; q XOR 8 = q + 8), so the codes
-//    enter the matrix core exactly ("colibrì 深度拆解" §5.2 packing);
-//  - A (activations): prepared once as bf16 hi + lo (16 significant bits), laid
-//    out in the same in-group element order as the codes; two MFMAs per step;
-//  - per 64-group ("colibri 开发演进实录" §2.1 gs64) the group accumulator starts
-//    at -136 * sum(x) (the unsigned-offset identity of §2.2, K1), and its result
-//    is scaled by the fp32 group scale into the fp32 running sum.
-// A workgroup owns 32 rows x 128 outputs (4 waves x 32); K is staged through
-// LDS eight groups at a time with asynchronous global-to-LDS loads, while the
-// chunk's weight codes are already in flight into registers.  Outputs of a row
-// have one owner: deterministic.
+// D[rows][outputs] = X[rows][K] * W[outputs][K]^T with v_mfma_f32_16x16x32_bf16.
+//  - B (weights): for one 64-group of one output row, lane (column j, part p)
+//    holds words 2p and 2p+1 (8 bytes, 16 codes).  Each 32-bit word of 8 codes
+//    becomes 4 bf16 pairs of (136 + q) by one bit operation per pair (0x4300 is
+//    128.0; q XOR 8 = q + 8), so the codes enter the matrix core exactly
+//    ("colibrì 深度拆解" §5.2 packing).  Word 2p+ks feeds K-step ks.
+//  - A (activations): prepared once as bf16 hi + lo (16 significant bits) in
+//    the codes' element order (per word: elements 0,4,1,5,2,6,3,7), 256 bytes
+//    per row and group; hi and lo are two MFMAs on the same B.
+//  - per 64-group ("colibri 开发演进实录" §2.1 gs64) the group accumulator
+//    starts at -136 * sum(x) (the unsigned-offset identity of §2.2, K1) and its
+//    result is scaled by the fp32 group scale into the fp32 running sum.
+//
+// Work item = up to 16 rows of one expert (one 16-row MFMA block) x a block
+// of outputs: 4 waves x 32 outputs (gate and up for the same columns) or
+// 4 waves x 64 outputs (down).  Experts with more rows, and the shared expert,
+// span several items.  K advances in chunks of 4 groups.  The weight stream is
+// kept in flight by a ring of three register slots (the chunk being computed
+// and the next two).  The activation chunk for the next step is loaded into
+// registers while the current one is computed, then written to the other of
+// two LDS buffers; the barrier between steps waits only for those LDS writes,
+// so the weight loads stay in flight across it.  Every output has one owner:
+// the result is deterministic.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -25,15 +34,15 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kPairOffset = 0x43084308u;   // bf16 pair (136 + q) from a code pair
 constexpr float kMfmaCodeOffset = 136.0f;
-constexpr int kGroupBytes = 256;                // one row's 64-element group in fragment order
-constexpr int kChunkGroups = 8;                 // groups staged per LDS step
-constexpr int kTileRows = 32;
-constexpr int kTileOut = 128;                   // outputs per workgroup (4 waves x 32)
-constexpr int kRowPitch = kChunkGroups * kGroupBytes + 16;  // LDS bytes per row (+16: bank stagger)
+constexpr int kGroupBytes = 256;                // one row's 64-group: 8 x 16 B hi, then 8 x 16 B lo
+constexpr int kCG = 4;                          // groups per K chunk
+constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 1 KB, one wave-wide LDS copy
+constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
+constexpr int kTileBytes = kMfmaItemRows * kRowPitch;
 
 __device__ __forceinline__ uint32_t bf16_rne_u(float f) {
     const uint32_t b = __float_as_uint(f);
@@ -41,17 +50,19 @@ __device__ __forceinline__ uint32_t bf16_rne_u(float f) {
 }
 
 // ------------------------------------------------------------------ prep
-// Rows of K fp32 values -> per 64-group 256 bytes: for half kg (32 elements) and
-// block j (8 elements): 8 bf16 hi then 8 bf16 lo, elements in the order
-// 0,4,1,5,2,6,3,7 of the block; and sx[row][group] = sum of (hi + lo).
-// One thread per 8-element block; the 8 blocks of a group are 8 adjacent lanes.
+// Rows of K fp32 values -> per 64-group G: 256 bytes, word w (elements
+// 64G + 8w .. +7) as 8 bf16 hi at 16w and 8 bf16 lo at 128 + 16w, elements in
+// the order 0,4,1,5,2,6,3,7; and nsx[row][G] = -136 * sum of (hi + lo) over the
+// group.  Rows are NGp groups long (whole chunks).  One thread per word; the 8
+// words of a group are 8 adjacent lanes.
 __global__ __launch_bounds__(256) void prep_frag_kernel(const float *src, int rows, int K,
-                                                       uint8_t *frag, float *sx) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // 8-element block index
-    const long nblk = (long)rows * (K / 8);
-    const bool live = i < nblk;
-    const long ii = live ? i : nblk - 1;
+                                                       uint8_t *frag, float *nsx) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // word index
+    const long nwd = (long)rows * (K / 8);
+    const bool live = i < nwd;
+    const long ii = live ? i : nwd - 1;
     const int row = (int)(ii / (K / 8)), b = (int)(ii % (K / 8));
+    const int NGp = mfma_groups_padded(K);
     const float4 *p = reinterpret_cast<const float4 *>(src + (size_t)row * K + 8 * b);
     const float4 v0 = p[0], v1 = p[1];
     const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -66,28 +77,65 @@ __global__ __launch_bounds__(256) void prep_frag_kernel(const float *src, int ro
         lb[s] = bf16_rne_u(x - hi);
         part += hi + __uint_as_float(lb[s] << 16);
     }
-    const int G = b / 8, kg = (b % 8) / 4, j = b % 4;
-    uint4 *dst = reinterpret_cast<uint4 *>(frag + (size_t)row * (K / 64) * kGroupBytes +
-                                           (size_t)G * kGroupBytes + kg * 128 + j * 32);
+    const int G = b / 8, w = b % 8;
+    uint8_t *grp = frag + ((size_t)row * NGp + G) * kGroupBytes;
     if (live) {
-        dst[0] = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                            hb[6] | (hb[7] << 16));
-        dst[1] = make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                            lb[6] | (lb[7] << 16));
+        *reinterpret_cast<uint4 *>(grp + 16 * w) =
+            make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                       hb[6] | (hb[7] << 16));
+        *reinterpret_cast<uint4 *>(grp + 128 + 16 * w) =
+            make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
+                       lb[6] | (lb[7] << 16));
     }
-    // group sum over the 8 blocks = 8 adjacent lanes (K is a multiple of 64)
+    // group sum over the 8 words = 8 adjacent lanes (K is a multiple of 64)
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) part += __shfl_xor(part, m, kWave);
-    if (live && b % 8 == 0) sx[(size_t)row * (K / 64) + G] = part;
+    if (live && w == 0) nsx[(size_t)row * NGp + G] = -kMfmaCodeOffset * part;
 }
 
-hipError_t launch_prep_frag(const float *src, int rows, int K, uint8_t *frag, float *sx,
+hipError_t launch_prep_frag(const float *src, int rows, int K, uint8_t *frag, float *nsx,
                             hipStream_t st) {
     if (rows <= 0) return hipSuccess;
-    const long nblk = (long)rows * (K / 8);
+    const long nwd = (long)rows * (K / 8);
     ProfScope prof("prep_frag", st);
-    prep_frag_kernel<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>(src, rows, K, frag, sx);
+    prep_frag_kernel<<<(unsigned)((nwd + 255) / 256), 256, 0, st>>>(src, rows, K, frag, nsx);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ work list
+// Items in union order: expert uniq[u] with c rows gets ceil(c / 16) items of
+// consecutive rows.  One workgroup of 256 threads, one thread per union slot
+// (E <= 256); an exclusive scan of the item counts places each expert's items.
+__global__ __launch_bounds__(256) void mfma_items_kernel(const int32_t *n_uniq, const int32_t *uniq,
+                                                        const int32_t *off, int E, int32_t *items,
+                                                        int32_t *n_items) {
+    __shared__ int wsum[256 / kWave];
+    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
+    const int nu = n_uniq[0];
+    int e = -1, cnt = 0;
+    if (u < nu && u < E) {
+        e = uniq[u];
+        cnt = off[e + 1] - off[e];
+    }
+    const int ni = (cnt + kMfmaItemRows - 1) / kMfmaItemRows;
+    int inc = ni;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) wsum[wv] = inc;
+    __syncthreads();
+    int base = inc - ni;
+    for (int v = 0; v < wv; v++) base += wsum[v];
+    for (int i = 0; i < ni; i++) {
+        int32_t *it = items + 4 * (base + i);
+        it[0] = e;
+        it[1] = off[e] + kMfmaItemRows * i;
+        it[2] = min(kMfmaItemRows, cnt - kMfmaItemRows * i);
+        it[3] = 0;
+    }
+    if (u == blockDim.x - 1) n_items[0] = base + ni;
 }
 
 // ------------------------------------------------------------------ grouped GEMM
@@ -101,189 +149,258 @@ __device__ __forceinline__ bf16x8_t code_pairs(uint32_t w) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// The LDS writes of this wave are done; meet the other waves.  Written out so
+// that no wait for the weight loads in flight is added.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool GU>
 __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t atile[kTileRows * kRowPitch];
-    __shared__ __attribute__((aligned(16))) float sxt[kChunkGroups][kTileRows];
-    const int unit = blockIdx.y;
-    const int H = a.H;
+    // activation chunks, double-buffered: [row][1 KB + 16] and [row][4 groups]
+    __shared__ __attribute__((aligned(16))) uint8_t at0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t at1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) float ns0[kMfmaItemRows * 4];  // -136*sum(x)
+    __shared__ __attribute__((aligned(16))) float ns1[kMfmaItemRows * 4];
 
-    int nrows, Fu;
-    const int32_t *rt;     // token of each row (GU routed), else rows are contiguous
+    // ---- the item: rows [row0, row0 + R) of a routed expert e, or of the shared expert (e < 0)
+    const int item = blockIdx.y;
+    int e, row0, R;
+    if (item < a.max_items) {
+        if (!a.with_routed || item >= a.n_items[0]) return;
+        e = a.items[4 * item];
+        row0 = a.items[4 * item + 1];
+        R = a.items[4 * item + 2];
+    } else {
+        if (!a.with_shared) return;
+        e = -1;
+        row0 = (item - a.max_items) * kMfmaItemRows;
+        R = min(kMfmaItemRows, a.T - row0);
+        if (R <= 0) return;
+    }
+    const int H = a.H;
+    const int Fu = e >= 0 ? a.F : a.Fs;
+    const int K = GU ? H : Fu;
+    const int N = GU ? Fu : H;
+    const int NG = K / 64;
+    const int NGp = mfma_groups_padded(K);
+    constexpr int kWaveOut = GU ? 32 : 64;
+    const int nb0 = blockIdx.x * (4 * kWaveOut);
+    if (nb0 >= N) return;
+
     moe_q4 m0, m1;
-    const uint8_t *afrag;  // fragment rows
-    const float *asx;
+    const int32_t *rt = nullptr;  // token of each row (routed gate/up), else rows are contiguous
+    const uint8_t *afrag;
+    const float *ansx;
     float *out;
-    size_t out_row0;
-    if (unit < a.max_units) {
-        if (!a.with_routed || unit >= a.n_uniq[0]) return;
-        const int e = a.uniq[unit];
-        const int r0 = a.off[e];
-        nrows = a.off[e + 1] - r0;
-        Fu = a.F;
+    if (e >= 0) {
         if (GU) {
             const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
             m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
             m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
-            rt = a.row_tok + r0;
+            rt = a.row_tok + row0;
             afrag = a.x_frag;
-            asx = a.x_sx;
-            out = a.h_routed;
+            ansx = a.x_nsx;
+            out = a.h_routed + (size_t)row0 * N;
         } else {
             const size_t dq = (size_t)e * H * (Fu / 2), ds = (size_t)e * H * (Fu / 64);
             m0.q = a.down.q + dq; m0.s = a.down.s + ds;
             m1 = m0;
-            rt = nullptr;
-            afrag = a.hr_frag + (size_t)r0 * (Fu / 64) * kGroupBytes;
-            asx = a.hr_sx + (size_t)r0 * (Fu / 64);
-            out = a.y_routed;
+            afrag = a.hr_frag + (size_t)row0 * NGp * kGroupBytes;
+            ansx = a.hr_nsx + (size_t)row0 * NGp;
+            out = a.y_routed + (size_t)row0 * N;
         }
-        out_row0 = (size_t)r0;
     } else {
-        if (!a.with_shared) return;
-        nrows = a.T;
-        Fu = a.Fs;
-        rt = nullptr;
         if (GU) {
             m0 = a.sh_gate; m1 = a.sh_up;
-            afrag = a.x_frag;
-            asx = a.x_sx;
-            out = a.h_shared;
+            afrag = a.x_frag + (size_t)row0 * NGp * kGroupBytes;
+            ansx = a.x_nsx + (size_t)row0 * NGp;
+            out = a.h_shared + (size_t)row0 * N;
         } else {
             m0 = a.sh_down; m1 = m0;
-            afrag = a.hs_frag;
-            asx = a.hs_sx;
-            out = a.y_shared;
+            afrag = a.hs_frag + (size_t)row0 * NGp * kGroupBytes;
+            ansx = a.hs_nsx + (size_t)row0 * NGp;
+            out = a.y_shared + (size_t)row0 * N;
         }
-        out_row0 = 0;
     }
-    const int K = GU ? H : Fu;
-    const int N = GU ? Fu : H;
-    const int NG = K / 64;
-    const int nb0 = blockIdx.x * kTileOut;
-    if (nb0 >= N) return;
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int ln = lane % 32, kg = lane / 32;
-    const int n0 = nb0 + wv * 32;
-    const int nrow = min(n0 + ln, N - 1);  // weight row of this lane (clamped: never stored)
-    const uint8_t *q0 = m0.q + (size_t)nrow * (K / 2) + 16 * kg;
-    const uint8_t *q1 = m1.q + (size_t)nrow * (K / 2) + 16 * kg;
-    const float *s0 = m0.s + (size_t)nrow * NG;
-    const float *s1 = m1.s + (size_t)nrow * NG;
+    const int j = lane % 16, p = lane / 16;
+    const int nchunks = (NG + kCG - 1) / kCG;
 
-    for (int rc = 0; rc < nrows; rc += kTileRows) {
-        const int R = min(kTileRows, nrows - rc);
-        f32x16_t acc0 = {}, acc1 = {};
-        for (int g0 = 0; g0 < NG; g0 += kChunkGroups) {
-            const int ng = min(kChunkGroups, NG - g0);
-            // this chunk's codes and scales first: their latency overlaps the staging below
-            uint4 cq0[kChunkGroups], cq1[kChunkGroups];
-            float cs0[kChunkGroups], cs1[kChunkGroups];
+    // ---- B blocks: GU -> (gate, cols 0-15), (gate, 16-31), (up, 0-15), (up, 16-31) of the
+    // wave's 32 outputs; down -> 4 x 16 of its 64 outputs.  A lane's column, clamped for
+    // loads (never stored past N).
+    int ncol[4];
+    uint32_t qoff[4], soff[4];
 #pragma unroll
-            for (int g = 0; g < kChunkGroups; g++) {
-                const int G = g0 + min(g, ng - 1);  // past the end: re-read the last group
-                cq0[g] = *reinterpret_cast<const uint4 *>(q0 + 32 * G);
-                cs0[g] = s0[G];
-                if (GU) {
-                    cq1[g] = *reinterpret_cast<const uint4 *>(q1 + 32 * G);
-                    cs1[g] = s1[G];
-                }
+    for (int b = 0; b < 4; b++) {
+        const int cb = GU ? b % 2 : b;
+        ncol[b] = nb0 + wv * kWaveOut + cb * 16 + j;
+        const int nc = min(ncol[b], N - 1);
+        qoff[b] = (uint32_t)nc * (uint32_t)(K / 2) + 8u * p;
+        soff[b] = (uint32_t)nc * (uint32_t)NG;
+    }
+    auto qbase = [&](int b) { return (GU && b >= 2) ? m1.q : m0.q; };
+    auto sbase = [&](int b) { return (GU && b >= 2) ? m1.s : m0.s; };
+
+    // ---- activation staging: wave wv moves rows wv + 4i (16 bytes per lane of each
+    // row's 1-KB chunk), lanes 0-15 the group sums of rows 0-15.  Rows past R repeat
+    // row R-1 (cached, finite; their outputs are never stored), so staging has no branches.
+    constexpr int kRowsPerWave = kMfmaItemRows / 4;
+    int srow[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; i++) {
+        const int r = min(wv + 4 * i, R - 1);
+        srow[i] = rt ? rt[r] : r;
+    }
+    const int lr = min(lane % kMfmaItemRows, R - 1);
+    const int nsrow = rt ? rt[lr] : lr;
+    struct Staged {
+        uint4 a[kRowsPerWave];
+        uint4 n;
+    };
+    // values are returned, not kept in a captured array, so they stay in registers
+    auto stage_load = [&](int c) __attribute__((always_inline)) {
+        const int g0 = c * kCG;
+        Staged v;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; i++)
+            v.a[i] = *reinterpret_cast<const uint4 *>(
+                afrag + ((size_t)srow[i] * NGp + g0) * kGroupBytes + 16 * lane);
+        v.n = *reinterpret_cast<const uint4 *>(ansx + (size_t)nsrow * NGp + g0);
+        return v;
+    };
+    auto stage_store = [&](const Staged &v, uint8_t *tile, float *nst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; i++)
+            *reinterpret_cast<uint4 *>(tile + (wv + 4 * i) * kRowPitch + 16 * lane) = v.a[i];
+        if (wv == 0 && lane < kMfmaItemRows) *reinterpret_cast<uint4 *>(nst + 4 * lane) = v.n;
+    };
+
+    uint2 cq[3][4][kCG];
+    float cs[3][4];
+    auto fetch = [&](int c, uint2 (&q)[4][kCG], float (&s)[4]) __attribute__((always_inline)) {
+        const int g0 = min(c, nchunks - 1) * kCG;  // past the end: re-fetch the last chunk
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int gi = 0; gi < kCG; gi++) {
+                const int G = min(g0 + gi, NG - 1);
+                q[b][gi] = *reinterpret_cast<const uint2 *>(qbase(b) + (qoff[b] + 32u * G));
             }
-            __syncthreads();  // previous chunk consumed
-            // stage rows [rc, rc+R) x groups [g0, g0+ng) straight into LDS: a row's chunk is
-            // at most 2 KB, copied as 1-KB pieces, one asynchronous wave instruction each
-            // (lane L moves bytes 16L..16L+15); lanes past the chunk re-read its start and
-            // land in the row's unused tail
-            const int bytes = ng * kGroupBytes;
-            const int pieces = (bytes + 1023) / 1024;
-            for (int pc = wv; pc < R * pieces; pc += 256 / kWave) {
-                const int r = pc / pieces, h = pc % pieces;
-                const int src = rt ? rt[rc + r] : rc + r;
-                int off = h * 1024 + lane * 16;
-                if (off >= bytes) off = 0;
-                __builtin_amdgcn_global_load_lds(afrag + ((size_t)src * NG + g0) * kGroupBytes + off,
-                                                 atile + r * kRowPitch + h * 1024, 16, 0, 0);
+        // lane (j, p) fetches its column's scale of group g0 + p
+#pragma unroll
+        for (int b = 0; b < 4; b++) s[b] = sbase(b)[soff[b] + (uint32_t)min(g0 + p, NG - 1)];
+    };
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c, const uint8_t *tile, const float *nst, const uint2 (&q)[4][kCG],
+                       const float (&s)[4]) __attribute__((always_inline)) {
+        const int ng = min(kCG, NG - c * kCG);
+#pragma unroll
+        for (int gi = 0; gi < kCG; gi++) {
+            if (gi >= ng) break;
+            // the column's group scale sits in lane j + 16 gi
+            float sg[4];
+#pragma unroll
+            for (int b = 0; b < 4; b++) sg[b] = __shfl(s[b], j + 16 * gi, kWave);
+            // group accumulators start at -136 * sum(x) of rows 4p .. 4p+3
+            f32x4_t ga;
+#pragma unroll
+            for (int v = 0; v < 4; v++) ga[v] = nst[(4 * p + v) * 4 + gi];
+            f32x4_t g[4];
+#pragma unroll
+            for (int b = 0; b < 4; b++) g[b] = ga;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(ar);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(ar + 128);
+                bf16x8_t bo[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? q[b][gi].y : q[b][gi].x);
+#pragma unroll
+                for (int b = 0; b < 4; b++) g[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[b], g[b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < 4; b++) g[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[b], g[b], 0, 0, 0);
             }
-            for (int i = tid; i < kTileRows * ng; i += blockDim.x) {
-                const int r = i % kTileRows, g = i / kTileRows;
-                float v = 0.f;
-                if (r < R) {
-                    const int src = rt ? rt[rc + r] : rc + r;
-                    v = asx[(size_t)src * NG + g0 + g];
-                }
-                sxt[g][r] = v;
-            }
-            __syncthreads();
 #pragma unroll
-            for (int g = 0; g < kChunkGroups; g++) {
-                if (g >= ng) break;
-                // group accumulators start at -136 * sum(x) of their row
-                f32x16_t ga;
+            for (int b = 0; b < 4; b++)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; q4++) {
-                    const float4 sv = *reinterpret_cast<const float4 *>(&sxt[g][8 * q4 + 4 * kg]);
-                    ga[4 * q4 + 0] = -kMfmaCodeOffset * sv.x;
-                    ga[4 * q4 + 1] = -kMfmaCodeOffset * sv.y;
-                    ga[4 * q4 + 2] = -kMfmaCodeOffset * sv.z;
-                    ga[4 * q4 + 3] = -kMfmaCodeOffset * sv.w;
-                }
-                f32x16_t g0acc = ga, g1acc = ga;
-                const uint32_t w0[4] = {cq0[g].x, cq0[g].y, cq0[g].z, cq0[g].w};
-                const uint32_t w1[4] = {cq1[g].x, cq1[g].y, cq1[g].z, cq1[g].w};
-                const uint8_t *arow = atile + ln * kRowPitch + g * kGroupBytes + kg * 128;
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t *>(arow + 32 * j);
-                    const bf16x8_t alo = *reinterpret_cast<const bf16x8_t *>(arow + 32 * j + 16);
-                    const bf16x8_t b0 = code_pairs(w0[j]);
-                    g0acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b0, g0acc, 0, 0, 0);
-                    g0acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b0, g0acc, 0, 0, 0);
-                    if (GU) {
-                        const bf16x8_t b1 = code_pairs(w1[j]);
-                        g1acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b1, g1acc, 0, 0, 0);
-                        g1acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b1, g1acc, 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    acc0[v] = fmaf(cs0[g], g0acc[v], acc0[v]);
-                    if (GU) acc1[v] = fmaf(cs1[g], g1acc[v], acc1[v]);
-                }
-            }
+                for (int v = 0; v < 4; v++) acc[b][v] = fmaf(sg[b], g[b][v], acc[b][v]);
         }
-        // D layout: register v of lane (ln, kg) is row 8*(v/4) + 4*kg + v%4, column ln
-        const int n = n0 + ln;
-        if (n < N) {
+    };
+
+    // one chunk: meet (every wave's LDS writes of this chunk done, the other buffer
+    // free), load the next activations into registers, fetch the codes two chunks
+    // ahead into the slot just freed, compute, write the next activations to LDS
+    auto step = [&](int c, int slot) __attribute__((always_inline)) {
+        const bool odd = c & 1;
+        lds_barrier();
+        // past the end: re-load the last chunk (not stored)
+        const Staged nx = stage_load(min(c + 1, nchunks - 1));
+        fetch(c + 2, cq[(slot + 2) % 3], cs[(slot + 2) % 3]);
+        compute(c, odd ? at1 : at0, odd ? ns1 : ns0, cq[slot], cs[slot]);
+        if (c + 1 < nchunks) stage_store(nx, odd ? at0 : at1, odd ? ns0 : ns1);
+    };
+
+    {
+        const Staged first = stage_load(0);
+        fetch(0, cq[0], cs[0]);
+        fetch(1, cq[1], cs[1]);
+        stage_store(first, at0, ns0);
+    }
+    // whole turns of the register ring without branches inside, then the rest
+    int c = 0;
+    for (; c + 3 <= nchunks; c += 3) {
+        step(c, 0);
+        step(c + 1, 1);
+        step(c + 2, 2);
+    }
+    if (c < nchunks) step(c, 0);
+    if (c + 1 < nchunks) step(c + 1, 1);
+
+    // ---- epilogue.  D layout: register v of lane (j, p) is row 4p + v, column j of the block
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int r = 8 * (v / 4) + 4 * kg + (v % 4);
-                if (r < R) {
-                    float val;
-                    if (GU) {
-                        const float gg = acc0[v], uu = acc1[v];
-                        val = gg / (1.0f + expf(-gg)) * uu;
-                    } else {
-                        val = acc0[v];
-                    }
-                    out[(out_row0 + rc + r) * (size_t)N + n] = val;
-                }
+    for (int b = 0; b < (GU ? 2 : 4); b++) {
+        const int n = ncol[b];
+        if (n >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int r = 4 * p + v;
+            if (r >= R) continue;
+            float val;
+            if (GU) {
+                const float gg = acc[b][v], uu = acc[b + 2][v];
+                val = gg / (1.0f + expf(-gg)) * uu;
+            } else {
+                val = acc[b][v];
             }
+            out[(size_t)r * N + n] = val;
         }
     }
 }
 
-// Gate/up for every unit (x prepared once), then h prepared, then down.
+// x prepared once; the work list; gate/up for every item; h prepared; down.
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     hipError_t e;
-    // activations of every token, once
-    e = launch_prep_frag(a.x, a.T, a.H, a.x_frag, a.x_sx, st);
+    e = launch_prep_frag(a.x, a.T, a.H, a.x_frag, a.x_nsx, st);
     if (e != hipSuccess) return e;
+    if (a.with_routed) {
+        ProfScope prof("mfma_items", st);
+        mfma_items_kernel<<<1, 256, 0, st>>>(a.n_uniq, a.uniq, a.off, a.E, a.items, a.n_items);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
     const int nmax = a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F;
     {
-        dim3 grid((nmax + kTileOut - 1) / kTileOut, a.max_units + 1);
+        dim3 grid((nmax + 127) / 128, a.max_items + shared_items);
         ProfScope prof("ffn_gateup_mfma", st);
         q4_mfma_kernel<true><<<grid, 256, 0, st>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -291,15 +408,15 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     // h rows in fragment order: the routed rows (as many as the largest union can
     // have) and the shared rows
     if (a.with_routed) {
-        e = launch_prep_frag(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_sx, st);
+        e = launch_prep_frag(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_nsx, st);
         if (e != hipSuccess) return e;
     }
     if (a.with_shared) {
-        e = launch_prep_frag(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_sx, st);
+        e = launch_prep_frag(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx, st);
         if (e != hipSuccess) return e;
     }
     {
-        dim3 grid((a.H + kTileOut - 1) / kTileOut, a.max_units + 1);
+        dim3 grid((a.H + 255) / 256, a.max_items + shared_items);
         ProfScope prof("ffn_down_mfma", st);
         q4_mfma_kernel<false><<<grid, 256, 0, st>>>(a);
         return hipGetLastError();

@@ -140,12 +140,18 @@ Plan make_plan(const moe_layer &L, int T) {
     p.y_routed = take(Tz * k * H * 4);
     p.y_shared = take(Tz * H * 4);
     if (Tz > (size_t)kGemvMaxTokens) {
-        p.x_frag = take(Tz * H * 4);
-        p.x_sx = take(Tz * (H / 64) * 4);
-        p.hr_frag = take(Tz * k * F * 4);
-        p.hr_sx = take(Tz * k * (F / 64) * 4);
-        p.hs_frag = take(Tz * Fs * 4);
-        p.hs_sx = take(Tz * (Fs / 64) * 4);
+        // fragment rows padded to whole 4-group chunks
+        const size_t gh = mfma_groups_padded((int)H), gf = mfma_groups_padded((int)F),
+                     gs = Fs ? mfma_groups_padded((int)Fs) : 0;
+        p.x_frag = take(Tz * gh * 256);
+        p.x_nsx = take(Tz * gh * 4);
+        p.hr_frag = take(Tz * k * gf * 256);
+        p.hr_nsx = take(Tz * k * gf * 4);
+        p.hs_frag = take(Tz * gs * 256);
+        p.hs_nsx = take(Tz * gs * 4);
+        p.max_items = mfma_max_items(p.max_units, (int)(Tz * k));
+        p.items = take((size_t)p.max_items * 16);
+        p.n_items = take(4);
     }
     p.total = o;
     return p;
@@ -218,11 +224,13 @@ static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_
     return launch_union(union_args(L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
 }
 
-static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int k, void *ws) {
+static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *ws) {
     MfmaArgs m;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
-    m.x_sx = at<float>(ws, p.x_sx);
+    m.x_nsx = at<float>(ws, p.x_nsx);
+    m.items = at<int32_t>(ws, p.items);
+    m.n_items = at<int32_t>(ws, p.n_items);
     m.n_uniq = f.n_uniq;
     m.uniq = f.uniq;
     m.off = f.off;
@@ -237,25 +245,28 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int k, void *ws) {
     m.h_shared = f.h_shared;
     m.hr_frag = at<uint8_t>(ws, p.hr_frag);
     m.hs_frag = at<uint8_t>(ws, p.hs_frag);
-    m.hr_sx = at<float>(ws, p.hr_sx);
-    m.hs_sx = at<float>(ws, p.hs_sx);
+    m.hr_nsx = at<float>(ws, p.hr_nsx);
+    m.hs_nsx = at<float>(ws, p.hs_nsx);
     m.y_routed = f.y_routed;
     m.y_shared = f.y_shared;
     m.T = f.T;
     m.H = f.H;
     m.F = f.F;
     m.Fs = f.Fs;
+    m.E = E;
     m.max_units = f.max_units;
     m.max_rows = f.T * k;
+    m.max_items = p.max_items;
     m.with_routed = f.with_routed;
     m.with_shared = f.with_shared;
     return m;
 }
 
 // grouped GEMVs for a handful of tokens, the matrix-core grouped GEMM above that
-static hipError_t run_ffn(const FfnArgs &f, const Plan &p, int k, void *ws, hipStream_t st) {
+static hipError_t run_ffn(const FfnArgs &f, const Plan &p, int E, int k, void *ws,
+                          hipStream_t st) {
     if (f.T <= kGemvMaxTokens) return launch_ffn_gemv(f, st);
-    return launch_ffn_mfma(mfma_args(f, p, k, ws), st);
+    return launch_ffn_mfma(mfma_args(f, p, E, k, ws), st);
 }
 
 static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T,
@@ -339,7 +350,7 @@ int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t 
     const Plan p = make_plan(*L, T);
     FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_rows, ws);
     a.with_shared = 0;
-    return launched(run_ffn(a, p, L->top_k, ws, (hipStream_t)stream));
+    return launched(run_ffn(a, p, L->n_experts, L->top_k, ws, (hipStream_t)stream));
 }
 
 int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
@@ -381,7 +392,7 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     float *y_routed = at<float>(ws, p.y_routed);
     if (e == hipSuccess) {
         FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
-        e = run_ffn(a, p, L->top_k, ws, st);
+        e = run_ffn(a, p, L->n_experts, L->top_k, ws, st);
     }
     if (e == hipSuccess) {
         CombineArgs c;

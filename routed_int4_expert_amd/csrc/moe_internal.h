@@ -40,7 +40,9 @@ struct Plan {
     size_t h_shared;  // fp32 [T][Fs]
     size_t y_routed;  // fp32 [T*k][H]  unweighted expert outputs per routed row
     size_t y_shared;  // fp32 [T][H]
-    size_t x_frag, x_sx, hr_frag, hr_sx, hs_frag, hs_sx;  // matrix-core path (T > kGemvMaxTokens)
+    size_t x_frag, x_nsx, hr_frag, hr_nsx, hs_frag, hs_nsx;  // matrix-core path (T > kGemvMaxTokens)
+    size_t items, n_items;  // matrix-core work list
+    int max_items;
     size_t total;
 };
 Plan make_plan(const moe_layer &L, int T);
@@ -92,18 +94,29 @@ constexpr int kGemvMaxTokens = 4;
 
 struct MfmaArgs {
     const float *x;                  // [T][H]
-    uint8_t *x_frag;                 // [T][H/64][256]
-    float *x_sx;                     // [T][H/64]
+    uint8_t *x_frag;                 // [T][NGp(H)][256]
+    float *x_nsx;                    // [T][NGp(H)]  -136 * group sum
     const int32_t *n_uniq, *uniq, *off, *row_tok;
+    int32_t *items;                  // [max_items][4]: expert, first row, rows, 0
+    int32_t *n_items;
     moe_q4 gate, up, down;
     moe_q4 sh_gate, sh_up, sh_down;
     float *h_routed, *h_shared;      // [rows][F], [T][Fs]
     uint8_t *hr_frag, *hs_frag;      // h in fragment order
-    float *hr_sx, *hs_sx;
+    float *hr_nsx, *hs_nsx;
     float *y_routed, *y_shared;      // [rows][H], [T][H]
-    int T, H, F, Fs, max_units, max_rows;
+    int T, H, F, Fs, E, max_units, max_rows, max_items;
     int with_routed, with_shared;
 };
+
+// Matrix-core work items: at most this many rows of one expert (one 16-row MFMA block).
+constexpr int kMfmaItemRows = 16;
+// Fragment rows hold a whole number of 4-group K chunks.
+__host__ __device__ inline int mfma_groups_padded(int K) { return (K / 64 + 3) / 4 * 4; }
+// Upper bound of the work items of a batch: sum over experts of ceil(rows / kMfmaItemRows).
+inline int mfma_max_items(int max_units, int max_rows) {
+    return max_units + (max_rows + kMfmaItemRows - 1) / kMfmaItemRows;
+}
 
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
 
