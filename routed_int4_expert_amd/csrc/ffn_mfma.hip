@@ -22,10 +22,11 @@
 // 4 waves x 64 outputs (down).  Experts with more rows, and the shared expert,
 // span several items.  K advances in chunks of 4 groups.  The weight stream is
 // kept in flight by a ring of three register slots (the chunk being computed
-// and the next two).  The activation chunk for the next step is loaded into
-// registers while the current one is computed, then written to the other of
-// two LDS buffers; the barrier between steps waits only for those LDS writes,
-// so the weight loads stay in flight across it.  Every output has one owner:
+// and the next two).  Activation chunks are loaded into registers two steps
+// ahead and written to the other of two LDS buffers after each compute; the
+// barrier between steps waits only for those LDS writes, and loads are issued
+// in an order where no wait for one covers data needed later (completions are
+// counted in issue order), so the weight loads stay in flight across steps.  Every output has one owner:
 // the result is deterministic.
 #include <math.h>
 
@@ -35,6 +36,7 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kPairOffset = 0x43084308u;   // bf16 pair (136 + q) from a code pair
 constexpr float kMfmaCodeOffset = 136.0f;
@@ -43,6 +45,10 @@ constexpr int kCG = 4;                          // groups per K chunk
 constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 1 KB, one wave-wide LDS copy
 constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
 constexpr int kTileBytes = kMfmaItemRows * kRowPitch;
+// a wave's weight codes of one chunk, regrouped through LDS: 4 B blocks x 16 rows x
+// 128 B, rows 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
+constexpr int kCodePitch = 144;
+constexpr int kCodeBytes = 4 * 16 * kCodePitch;
 
 __device__ __forceinline__ uint32_t bf16_rne_u(float f) {
     const uint32_t b = __float_as_uint(f);
@@ -162,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t at1[kTileBytes];
     __shared__ __attribute__((aligned(16))) float ns0[kMfmaItemRows * 4];  // -136*sum(x)
     __shared__ __attribute__((aligned(16))) float ns1[kMfmaItemRows * 4];
+    __shared__ __attribute__((aligned(16))) uint8_t cbuf[4][kCodeBytes];  // per wave
 
     // ---- the item: rows [row0, row0 + R) of a routed expert e, or of the shared expert (e < 0)
     const int item = blockIdx.y;
@@ -234,15 +241,26 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
     // wave's 32 outputs; down -> 4 x 16 of its 64 outputs.  A lane's column, clamped for
     // loads (never stored past N).
     int ncol[4];
-    uint32_t qoff[4], soff[4];
+    uint32_t soff[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         const int cb = GU ? b % 2 : b;
         ncol[b] = nb0 + wv * kWaveOut + cb * 16 + j;
-        const int nc = min(ncol[b], N - 1);
-        qoff[b] = (uint32_t)nc * (uint32_t)(K / 2) + 8u * p;
-        soff[b] = (uint32_t)nc * (uint32_t)NG;
+        soff[b] = (uint32_t)min(ncol[b], N - 1) * (uint32_t)NG;
     }
+    // code loads are coalesced: for a block of 16 rows, load i (0, 1) gives lane l row
+    // 8i + l/8 and bytes 16 (l % 8) of the row's 128-byte chunk (4 groups); rows past N
+    // re-read row N-1 (never stored)
+    constexpr int kColBlocks = GU ? 2 : 4;
+    uint32_t qrow[kColBlocks][2];
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; cb++)
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int n = min(nb0 + wv * kWaveOut + cb * 16 + 8 * i + lane / 8, N - 1);
+            qrow[cb][i] = (uint32_t)n * (uint32_t)(K / 2);
+        }
+    const uint32_t qlast = (uint32_t)(K / 2 - 16);  // last 16-byte piece of a row
     auto qbase = [&](int b) { return (GU && b >= 2) ? m1.q : m0.q; };
     auto sbase = [&](int b) { return (GU && b >= 2) ? m1.s : m0.s; };
 
@@ -280,17 +298,17 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
         if (wv == 0 && lane < kMfmaItemRows) *reinterpret_cast<uint4 *>(nst + 4 * lane) = v.n;
     };
 
-    uint2 cq[3][4][kCG];
+    u32x4_t cq[3][4][2];
     float cs[3][4];
-    auto fetch = [&](int c, uint2 (&q)[4][kCG], float (&s)[4]) __attribute__((always_inline)) {
+    auto fetch = [&](int c, u32x4_t (&q)[4][2], float (&s)[4]) __attribute__((always_inline)) {
         const int g0 = min(c, nchunks - 1) * kCG;  // past the end: re-fetch the last chunk
+        // past the row's end (a last chunk of fewer than 4 groups): re-read its last piece
+        const uint32_t off = min((uint32_t)(32 * g0 + 16 * (lane % 8)), qlast);
 #pragma unroll
         for (int b = 0; b < 4; b++)
 #pragma unroll
-            for (int gi = 0; gi < kCG; gi++) {
-                const int G = min(g0 + gi, NG - 1);
-                q[b][gi] = *reinterpret_cast<const uint2 *>(qbase(b) + (qoff[b] + 32u * G));
-            }
+            for (int i = 0; i < 2; i++)
+                q[b][i] = *reinterpret_cast<const u32x4_t *>(qbase(b) + (qrow[GU ? b % 2 : b][i] + off));
         // lane (j, p) fetches its column's scale of group g0 + p
 #pragma unroll
         for (int b = 0; b < 4; b++) s[b] = sbase(b)[soff[b] + (uint32_t)min(g0 + p, NG - 1)];
@@ -300,9 +318,17 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int c, const uint8_t *tile, const float *nst, const uint2 (&q)[4][kCG],
+    uint8_t *cw = cbuf[wv];
+    auto compute = [&](int c, const uint8_t *tile, const float *nst, const u32x4_t (&q)[4][2],
                        const float (&s)[4]) __attribute__((always_inline)) {
         const int ng = min(kCG, NG - c * kCG);
+        // regroup the chunk's codes: row-major into this wave's LDS area, then each lane
+        // reads its column's words 2p, 2p+1 of every group
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                *reinterpret_cast<u32x4_t *>(cw + (16 * b + 8 * i + lane / 8) * kCodePitch + 16 * (lane % 8)) = q[b][i];
 #pragma unroll
         for (int gi = 0; gi < kCG; gi++) {
             if (gi >= ng) break;
@@ -317,6 +343,10 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
             f32x4_t g[4];
 #pragma unroll
             for (int b = 0; b < 4; b++) g[b] = ga;
+            uint2 w[4];
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
@@ -324,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
                 const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(ar + 128);
                 bf16x8_t bo[4];
 #pragma unroll
-                for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? q[b][gi].y : q[b][gi].x);
+                for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? w[b].y : w[b].x);
 #pragma unroll
                 for (int b = 0; b < 4; b++) g[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[b], g[b], 0, 0, 0);
 #pragma unroll
@@ -337,34 +367,44 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
         }
     };
 
-    // one chunk: meet (every wave's LDS writes of this chunk done, the other buffer
-    // free), load the next activations into registers, fetch the codes two chunks
-    // ahead into the slot just freed, compute, write the next activations to LDS
-    auto step = [&](int c, int slot) __attribute__((always_inline)) {
+    // One chunk step.  Loads are issued so that no wait covers data needed later:
+    // the activations of chunk c+2 (before the codes of c+2, so writing them to LDS two
+    // steps later never waits for codes that are still ahead of use), then the codes
+    // of c+2 into the slot just freed.  The activations of c+1, loaded a step ago, go to
+    // the other LDS buffer after the compute.  Staging register sets alternate.
+    Staged stg0, stg1;
+    auto step = [&](int c, int slot, Staged &ld, const Staged &st) __attribute__((always_inline)) {
         const bool odd = c & 1;
         lds_barrier();
-        // past the end: re-load the last chunk (not stored)
-        const Staged nx = stage_load(min(c + 1, nchunks - 1));
+        ld = stage_load(min(c + 2, nchunks - 1));  // past the end: re-load the last chunk (not stored)
         fetch(c + 2, cq[(slot + 2) % 3], cs[(slot + 2) % 3]);
         compute(c, odd ? at1 : at0, odd ? ns1 : ns0, cq[slot], cs[slot]);
-        if (c + 1 < nchunks) stage_store(nx, odd ? at0 : at1, odd ? ns0 : ns1);
+        if (c + 1 < nchunks) stage_store(st, odd ? at0 : at1, odd ? ns0 : ns1);
     };
 
     {
         const Staged first = stage_load(0);
         fetch(0, cq[0], cs[0]);
+        stg1 = stage_load(min(1, nchunks - 1));
         fetch(1, cq[1], cs[1]);
         stage_store(first, at0, ns0);
     }
-    // whole turns of the register ring without branches inside, then the rest
+    // whole turns of both rings (codes: 3 slots, staging: 2 sets) without branches
+    // inside, then the rest
     int c = 0;
-    for (; c + 3 <= nchunks; c += 3) {
-        step(c, 0);
-        step(c + 1, 1);
-        step(c + 2, 2);
+    for (; c + 6 <= nchunks; c += 6) {
+        step(c, 0, stg0, stg1);
+        step(c + 1, 1, stg1, stg0);
+        step(c + 2, 2, stg0, stg1);
+        step(c + 3, 0, stg1, stg0);
+        step(c + 4, 1, stg0, stg1);
+        step(c + 5, 2, stg1, stg0);
     }
-    if (c < nchunks) step(c, 0);
-    if (c + 1 < nchunks) step(c + 1, 1);
+    if (c < nchunks) step(c, 0, stg0, stg1);
+    if (c + 1 < nchunks) step(c + 1, 1, stg1, stg0);
+    if (c + 2 < nchunks) step(c + 2, 2, stg0, stg1);
+    if (c + 3 < nchunks) step(c + 3, 0, stg1, stg0);
+    if (c + 4 < nchunks) step(c + 4, 1, stg0, stg1);
 
     // ---- epilogue.  D layout: register v of lane (j, p) is row 4p + v, column j of the block
 #pragma unroll
