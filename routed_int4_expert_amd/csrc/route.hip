@@ -195,7 +195,9 @@ __global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionA
 hipError_t launch_select_union(const SelectArgs &s, const UnionArgs &u, hipStream_t st) {
     const size_t lds = ((size_t)s.T * s.k + s.T + union_lds_words(u.E, u.T)) * sizeof(uint32_t);
     ProfScope prof("select_union", st);
-    select_union_kernel<<<1, 1024, lds, st>>>(s, u);
+    // a wave per token, at least four waves for the union
+    const int threads = max(256, kWave * s.T);
+    select_union_kernel<<<1, threads, lds, st>>>(s, u);
     return hipGetLastError();
 }
 

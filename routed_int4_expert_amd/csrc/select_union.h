@@ -29,13 +29,11 @@ __device__ __forceinline__ unsigned long long mono_key(double v) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Per-wave LDS scratch of select_token: the k picks, compacted then ranked.
+// Per-wave LDS scratch of select_token: the k picks, compacted.
 struct PickScratch {
     unsigned long long key[MOE_MAX_TOPK];
     double sig[MOE_MAX_TOPK];
     int id[MOE_MAX_TOPK];
-    int ord_id[MOE_MAX_TOPK];
-    double ord_sig[MOE_MAX_TOPK];
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -48,8 +46,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // as k rounds of argmax excluding taken experts, equal scores going to the lower
 // id), adaptive top-p over the k gates, norm_topk, routed scale.
 // The k-th largest choice is found exactly by a bitwise search on monotone 64-bit
-// keys (each step counts keys >= a candidate with one ballot per slot); the picks
-// are then compacted into LDS and ranked (choice descending, lower id first).
+// keys (each step counts keys >= a candidate with one ballot per slot, stopping
+// once exactly k keys qualify); the picks are then compacted and ranked (choice
+// descending, lower id first).
 // Lane j < k ends up holding pick j.  Writes ids/w (this token's k slots) and
 // *keff; when ids_copy/keff_copy are given, the ids and keff are written there too.
 __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
@@ -82,31 +81,43 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         }
     }
 
-    // thr = the k-th largest key: the largest value with at least k keys >= it
+    // thr = the k-th largest key: the largest value with at least k keys >= it, built
+    // bit by bit.  As soon as exactly k keys are >= a candidate, those k are the picks
+    // (no key equal to the k-th is left out), which ends the search early.
     unsigned long long thr = 0ull;
+    bool exact = false;
     for (int bit = 63; bit >= 0; bit--) {
         const unsigned long long cand = thr | (1ull << bit);
         int cnt = 0;
 #pragma unroll
         for (int i = 0; i < EPL; i++) cnt += __popcll(__ballot(key[i] >= cand));
         if (cnt >= a.k) thr = cand;
+        if (cnt == a.k) {
+            exact = true;
+            break;
+        }
     }
     // every key above thr is picked; among keys equal to thr the lowest ids fill up to k
     const unsigned long long below = (1ull << lane) - 1ull;
-    int cgt = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; i++) cgt += __popcll(__ballot(key[i] > thr));
-    const int need = a.k - cgt;
     bool sel[EPL];
-    int eq_before = 0;
+    if (exact) {
 #pragma unroll
-    for (int i = 0; i < EPL; i++) {
-        const unsigned long long eqm = __ballot(key[i] == thr && (lane + kWave * i) < a.E);
-        const int r = eq_before + __popcll(eqm & below);
-        sel[i] = key[i] > thr || (((eqm >> lane) & 1ull) && r < need);
-        eq_before += __popcll(eqm);
+        for (int i = 0; i < EPL; i++) sel[i] = key[i] >= thr;
+    } else {
+        int cgt = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) cgt += __popcll(__ballot(key[i] > thr));
+        const int need = a.k - cgt;
+        int eq_before = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const unsigned long long eqm = __ballot(key[i] == thr && (lane + kWave * i) < a.E);
+            const int r = eq_before + __popcll(eqm & below);
+            sel[i] = key[i] > thr || (((eqm >> lane) & 1ull) && r < need);
+            eq_before += __popcll(eqm);
+        }
     }
-    // compact the k picks into LDS (expert order)
+    // compact the k picks into LDS (expert order): lane j < k then holds pick j
     int base = 0;
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
@@ -120,24 +131,36 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         base += __popcll(sm);
     }
     wave_lds_sync();
-    // lane j < k ranks pick j: choice descending, equal choices by lower id
+    unsigned long long mk = 0ull;
+    int mid = 0x7fffffff;
+    double msig = 0.0;
     if (lane < a.k) {
-        const unsigned long long mk = ps->key[lane];
-        const int mid = ps->id[lane];
-        int rank = 0;
-        for (int i = 0; i < a.k; i++) {
-            const unsigned long long ok = ps->key[i];
-            rank += (ok > mk || (ok == mk && ps->id[i] < mid)) ? 1 : 0;
-        }
-        ps->ord_id[rank] = mid;
-        ps->ord_sig[rank] = ps->sig[lane];
+        mk = ps->key[lane];
+        mid = ps->id[lane];
+        msig = ps->sig[lane];
     }
-    wave_lds_sync();
+    // rank of pick j (choice descending, equal choices by lower id), the other picks
+    // read from their lanes through scalar registers
+    int rank = 0;
+    for (int i = 0; i < a.k; i++) {
+        const unsigned long long ok =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(mk >> 32), i) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mk, i);
+        const int oid = __builtin_amdgcn_readlane(mid, i);
+        rank += (ok > mk || (ok == mk && oid < mid)) ? 1 : 0;
+    }
+    // slot r takes the pick of rank r: find it with a ballot per slot
     int my_id = -1;
     double my_sig = 0.0;
-    if (lane < a.k) {
-        my_id = ps->ord_id[lane];
-        my_sig = ps->ord_sig[lane];
+    for (int r = 0; r < a.k; r++) {
+        const unsigned long long m = __ballot(lane < a.k && rank == r);
+        const int src = __ffsll((long long)m) - 1;
+        const int id_r = __builtin_amdgcn_readlane(mid, src);
+        const double sig_r = readlane_f64(msig, src);
+        if (lane == r) {
+            my_id = id_r;
+            my_sig = sig_r;
+        }
     }
 
     // adaptive top-p: rank of each pick by sig descending (equal sigs in slot order);
