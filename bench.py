@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -104,6 +105,29 @@ WORKLOADS = {
     "glm_stack16": "16 GLM-shaped layers resident (distinct HBM), 32 tokens/step, top-p 0.7, "
                    "Zipf(1.1) bias, RMSNorm + residual between layers, fp32",
 }
+
+
+def counted_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (profiles/hbm_counters.json, calibrated against a copy of known size), or None
+    when there is none for this workload or the kernel's source changed since."""
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(root, "profiles", "hbm_counters.json")) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in data.get("entries", []):
+        if e.get("workload") != workload or e.get("kernel") != kernel:
+            continue
+        try:
+            with open(os.path.join(root, e["source"]), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != e["source_sha256"]:
+                    return None
+        except OSError:
+            return None
+        return float(e["hbm_bytes_per_launch"])
+    return None
 
 
 def main():
@@ -274,7 +298,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": float(achieved / HBM_PEAK_GBPS),
-            "traffic": None,
+            "traffic": counted_traffic(wl, gu_name),
             "bytes_per_launch": float(gu_bytes),
             "avg_launch_us": float(gu_avg_ms * 1e3),
             "mfma_util_vs_bf16_dense": float(gu_flops / (gu_avg_ms * 1e-3) / BF16_PEAK_FLOPS),
