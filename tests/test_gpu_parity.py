@@ -69,6 +69,10 @@ SMALL = [
              routed_scale=2.5),
     S.custom("twotok", hidden=2048, n_experts=64, ffn=512, shared_ffn=512, top_k=8, tokens=2,
              router_std=1 / 45.25),
+    # few tokens with routed and shared FFN widths that split the down projection into two
+    # launches (the combine then runs on its own)
+    S.custom("raggedfew", hidden=320, n_experts=24, ffn=192, shared_ffn=64, top_k=5, tokens=3,
+             top_p=0.8, routed_scale=2.5, bias_amp=0.3),
 ]
 
 
