@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include "moe_internal.h"
+#include "select_union.h"
 
 namespace moe {
 
@@ -80,6 +81,50 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Selection and union for the few tokens of a decode step, by one workgroup into
+// LDS ([R] §1.1-§1.3; select_token and union_block as in the select+union kernel):
+// lds = ids[T*k] w[T*k] keff[T] n_uniq[1] uniq[E] off[E+1] row_tok[T*k] pick_row[T*k]
+// scratch.  Workgroup (0,0) also writes them to global memory for the later launches.
+// Compiled into the one-row kernels only (one token), where it adds no register spills.
+__device__ __forceinline__ void select_and_union_lds(const FfnArgs &a, int32_t *lds) {
+    __shared__ PickScratch ps_sel[kGemvMaxTokens];
+    const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
+    int32_t *ids_l = lds;
+    float *w_l = reinterpret_cast<float *>(ids_l + T * k);
+    int32_t *keff_l = reinterpret_cast<int32_t *>(w_l + T * k);
+    int32_t *nu_l = keff_l + T;
+    int32_t *uniq_l = nu_l + 1;
+    int32_t *off_l = uniq_l + E;
+    int32_t *rt_l = off_l + E + 1;
+    int32_t *pick_l = rt_l + T * k;
+    uint32_t *scr = reinterpret_cast<uint32_t *>(pick_l + T * k);
+    const int t = threadIdx.x / kWave;
+    if (t < T)
+        select_token(a.sel, t, threadIdx.x % kWave, ids_l + t * k, w_l + t * k, keff_l + t, nullptr,
+                     nullptr, &ps_sel[t]);
+    __syncthreads();
+    UnionArgs u = a.uni;
+    u.n_uniq = nu_l;
+    u.uniq = uniq_l;
+    u.off = off_l;
+    u.row_tok = rt_l;
+    u.pick_row = pick_l;
+    union_block(u, ids_l, keff_l, scr);
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+        for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+            a.sel.ids[i] = ids_l[i];
+            a.sel.w[i] = w_l[i];
+            a.uni.row_tok[i] = rt_l[i];
+            a.uni.pick_row[i] = pick_l[i];
+        }
+        for (int i = threadIdx.x; i < T; i += blockDim.x) a.sel.keff[i] = keff_l[i];
+        for (int i = threadIdx.x; i < E; i += blockDim.x) a.uni.uniq[i] = uniq_l[i];
+        for (int i = threadIdx.x; i <= E; i += blockDim.x) a.uni.off[i] = off_l[i];
+        if (threadIdx.x == 0) a.uni.n_uniq[0] = nu_l[0];
+    }
+}
+
 // Outputs per lane group per pass: four weight rows per step at one token (the
 // next step's rows are loaded while the current ones are computed), fewer with
 // more tokens so the accumulators fit in registers.
@@ -98,9 +143,21 @@ struct GemvShape {
 template <int LPR, int RM, bool GU>
 __global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) {
     using S = GemvShape<LPR, RM, GU>;
-    extern __shared__ float xs[];  // [RM][C * kChunkPitch]
+    extern __shared__ float xs[];  // [RM][C * kChunkPitch] (+ selection and union, when fused)
     const int unit = blockIdx.y;
     const int H = a.H;
+
+    // ---- the union: from global memory, or selected here ([R] §1.1-§1.3) into LDS
+    const int32_t *n_uniq_p = a.n_uniq, *uniq_p = a.uniq, *off_p = a.off, *row_tok_p = a.row_tok;
+    if constexpr (GU && RM == 1) if (a.fuse_select && unit < a.max_units && a.with_routed) {
+        int32_t *lds = reinterpret_cast<int32_t *>(xs + (size_t)RM * (H / 32) * kChunkPitch);
+        select_and_union_lds(a, lds);
+        const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
+        n_uniq_p = lds + 2 * T * k + T;
+        uniq_p = n_uniq_p + 1;
+        off_p = uniq_p + E;
+        row_tok_p = off_p + E + 1;
+    }
 
     // ---- the unit: a routed expert of the union, or the shared expert
     int nrows, Fu;
@@ -110,16 +167,16 @@ __global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) 
     float *out;         // output rows
     size_t out_row0;    // first output row index
     if (unit < a.max_units) {
-        if (!a.with_routed || unit >= a.n_uniq[0]) return;
-        const int e = a.uniq[unit];
-        const int r0 = a.off[e];
-        nrows = a.off[e + 1] - r0;
+        if (!a.with_routed || unit >= n_uniq_p[0]) return;
+        const int e = uniq_p[unit];
+        const int r0 = off_p[e];
+        nrows = off_p[e + 1] - r0;
         Fu = a.F;
         if (GU) {
             const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
             m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
             m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
-            rt = a.row_tok + r0;
+            rt = row_tok_p + r0;
             xin = a.x;
             out = a.h_routed;
         } else {
@@ -347,7 +404,8 @@ static int device_cus() {
 template <int LPR, int RM, bool GU>
 static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     using S = GemvShape<LPR, RM, GU>;
-    const size_t lds = (size_t)RM * (K / 32) * kChunkPitch * sizeof(float);
+    size_t lds = (size_t)RM * (K / 32) * kChunkPitch * sizeof(float);
+    if (GU && RM == 1 && a.fuse_select) lds += select_lds_words(a.sel.E, a.sel.T, a.sel.k) * sizeof(uint32_t);
     if (lds > 64 * 1024) {
         // raise the dynamic-LDS cap for this kernel; the launch itself reports a real failure
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_gemv_kernel<LPR, RM, GU>),
@@ -356,7 +414,7 @@ static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     }
     // resident workgroups per CU (4 waves each): registers allow 4, LDS may allow fewer
     int per_cu = 4;
-    while (per_cu > 1 && (size_t)per_cu * lds > 160 * 1024) per_cu--;
+    while (per_cu > 1 && (size_t)per_cu * (lds + 2048) > 160 * 1024) per_cu--;  // + static LDS
     const long cap = (long)device_cus() * per_cu;
     const int units = a.max_units + 1;
     const int blocks1 = (N + S::BF - 1) / S::BF;  // workgroups per unit at one pass each

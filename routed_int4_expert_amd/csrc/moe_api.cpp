@@ -295,6 +295,9 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     a.max_units = p.max_units;
     a.with_routed = 1;
     a.with_shared = L.shared_ffn > 0 ? 1 : 0;
+    a.fuse_select = 0;
+    memset(&a.sel, 0, sizeof(a.sel));
+    memset(&a.uni, 0, sizeof(a.uni));
     return a;
 }
 
@@ -379,7 +382,11 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
 
     hipError_t e;
-    if (T <= kSelectUnionTokens) {
+    // one token: selection and union run inside the gate/up launch
+    const bool sel_in_ffn = T == 1;
+    if (sel_in_ffn) {
+        e = run_logits(*L, p, x, T, ws, st);
+    } else if (T <= kSelectUnionTokens) {
         // small batch: selection and union in one workgroup
         e = run_logits(*L, p, x, T, ws, st);
         if (e == hipSuccess)
@@ -392,6 +399,11 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     float *y_routed = at<float>(ws, p.y_routed);
     if (e == hipSuccess) {
         FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
+        if (sel_in_ffn) {
+            a.fuse_select = 1;
+            a.sel = select_args(*L, p, T, ids, w, keff, ws);
+            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
+        }
         e = run_ffn(a, p, L->n_experts, L->top_k, ws, st);
     }
     if (e == hipSuccess) {

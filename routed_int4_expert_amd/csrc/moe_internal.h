@@ -85,7 +85,19 @@ struct FfnArgs {
     float *y_shared;                 // [T][H]
     int T, H, F, Fs, max_units;
     int with_routed, with_shared;
+    // Selection and union inside the gate/up launch (one token): every routed
+    // workgroup selects and builds the union in LDS from the router logits; workgroup
+    // (0,0) also writes them out through sel (ids, w, keff) and uni (union arrays).
+    int fuse_select;
+    SelectArgs sel;
+    UnionArgs uni;
 };
+
+// LDS words of the in-launch selection and union for T tokens of top-k over E experts.
+__host__ __device__ inline size_t select_lds_words(int E, int T, int k) {
+    const int W = (T + 31) / 32, W8 = (W + 7) / 8;
+    return 4 * (size_t)T * k + T + 1 + E + (E + 1) + (size_t)E * W + (size_t)E * W8 + 2 * (size_t)E + 1;
+}
 
 // The matrix-core path (more than kGemvMaxTokens tokens): FfnArgs plus the
 // activations prepared in MFMA fragment order (bf16 hi/lo, 256 bytes per row and

@@ -92,9 +92,24 @@ def test_small_shapes_full_parity(sh):
     torch.cuda.synchronize()
     ry = R.expert_ffn(R.Layer(d), x, ru["off"], ru["row_tok"])
     assert_close(y.cpu().numpy()[:rows], ry, f"{sh.name} expert rows")
-    # whole layer, fp32 and bf16
+    # whole layer, fp32 and bf16; the routing and union it reports equal the oracle's
     ref = R.layer_forward(R.Layer(d), x)
-    out = M.moe_layer_forward(layer, xd)
+    T, k, E = sh.tokens, sh.top_k, sh.n_experts
+    i32 = dict(dtype=torch.int32, device=DEV)
+    dbg = dict(ids=torch.full((T, k), -7, **i32), w=torch.full((T, k), -7.0, device=DEV),
+               keff=torch.full((T,), -7, **i32), n_uniq=torch.full((1,), -7, **i32),
+               uniq=torch.full((E,), -7, **i32), off=torch.full((E + 1,), -7, **i32),
+               row_tok=torch.full((T * k,), -7, **i32), pick_row=torch.full((T, k), -7, **i32))
+    out = M.moe_layer_forward(layer, xd, dbg=dbg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dbg["ids"].cpu().numpy(), rids, err_msg="forward ids")
+    np.testing.assert_array_equal(dbg["keff"].cpu().numpy(), rkeff, err_msg="forward keff")
+    np.testing.assert_allclose(dbg["w"].cpu().numpy(), rw, rtol=1e-6, atol=0, err_msg="forward w")
+    assert int(dbg["n_uniq"].item()) == ru["n_uniq"]
+    np.testing.assert_array_equal(dbg["uniq"].cpu().numpy(), ru["uniq"], err_msg="forward uniq")
+    np.testing.assert_array_equal(dbg["off"].cpu().numpy(), ru["off"], err_msg="forward off")
+    np.testing.assert_array_equal(dbg["row_tok"].cpu().numpy(), ru["row_tok"], err_msg="forward row_tok")
+    np.testing.assert_array_equal(dbg["pick_row"].cpu().numpy(), ru["pick_row"], err_msg="forward pick_row")
     out_bf = M.moe_layer_forward(layer, xd, out_dtype=M.MOE_BF16)
     torch.cuda.synchronize()
     rel, mx = assert_close(out.cpu().numpy(), ref, f"{sh.name} layer")
