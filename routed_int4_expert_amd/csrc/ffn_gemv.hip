@@ -86,7 +86,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // lds = ids[T*k] w[T*k] keff[T] n_uniq[1] uniq[E] off[E+1] row_tok[T*k] pick_row[T*k]
 // scratch.  Workgroup (0,0) also writes them to global memory for the later launches.
 // Compiled into the one-row kernels only (one token), where it adds no register spills.
-__device__ __forceinline__ void select_and_union_lds(const FfnArgs &a, int32_t *lds) {
+__device__ __forceinline__ void select_and_union_lds(const FfnArgs &a, int32_t *lds, bool writer) {
     __shared__ PickScratch ps_sel[kGemvMaxTokens];
     const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
     int32_t *ids_l = lds;
@@ -111,7 +111,7 @@ __device__ __forceinline__ void select_and_union_lds(const FfnArgs &a, int32_t *
     u.pick_row = pick_l;
     union_block(u, ids_l, keff_l, scr);
     __syncthreads();
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (writer) {
         for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
             a.sel.ids[i] = ids_l[i];
             a.sel.w[i] = w_l[i];
@@ -138,20 +138,18 @@ struct GemvShape {
     static constexpr int BF = 4 * WF;                         // outputs per workgroup per pass
 };
 
-// a.passes: passes per workgroup, chosen on the host so the grid fits in one
-// round of resident workgroups
+// The work of workgroup bx of one unit (the kernels below map it from blockIdx).
 template <int LPR, int RM, bool GU>
-__global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) {
+__device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit, int bx) {
     using S = GemvShape<LPR, RM, GU>;
     extern __shared__ float xs[];  // [RM][C * kChunkPitch] (+ selection and union, when fused)
-    const int unit = blockIdx.y;
     const int H = a.H;
 
     // ---- the union: from global memory, or selected here ([R] §1.1-§1.3) into LDS
     const int32_t *n_uniq_p = a.n_uniq, *uniq_p = a.uniq, *off_p = a.off, *row_tok_p = a.row_tok;
     if constexpr (GU && RM == 1) if (a.fuse_select && unit < a.max_units && a.with_routed) {
         int32_t *lds = reinterpret_cast<int32_t *>(xs + (size_t)RM * (H / 32) * kChunkPitch);
-        select_and_union_lds(a, lds);
+        select_and_union_lds(a, lds, bx == 0 && unit == 0);
         const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
         n_uniq_p = lds + 2 * T * k + T;
         uniq_p = n_uniq_p + 1;
@@ -207,7 +205,7 @@ __global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) 
     const int K = GU ? H : Fu;      // reduction length
     const int N = GU ? Fu : H;      // outputs of this unit
     const int C = K / 32;           // 32-element chunks per row
-    const int nbw = blockIdx.x * S::BF * passes;  // first output of this workgroup
+    const int nbw = bx * S::BF * passes;  // first output of this workgroup
     if (nbw >= N) return;
 
     const int tid = threadIdx.x;
@@ -371,6 +369,13 @@ __global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) 
             }
         }
     }
+}
+
+// a.passes: passes per workgroup, chosen on the host so the grid fits in one
+// round of resident workgroups
+template <int LPR, int RM, bool GU>
+__global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) {
+    gemv_body<LPR, RM, GU>(a, passes, blockIdx.y, blockIdx.x);
 }
 
 static int lanes_per_row(int K) {

@@ -384,6 +384,8 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     hipError_t e;
     // one token: selection and union run inside the gate/up launch
     const bool sel_in_ffn = T == 1;
+    float *y_routed = at<float>(ws, p.y_routed);
+    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
     if (sel_in_ffn) {
         e = run_logits(*L, p, x, T, ws, st);
     } else if (T <= kSelectUnionTokens) {
@@ -396,9 +398,7 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
         e = run_route(*L, p, x, T, ids, w, keff, ws, st);
         if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
     }
-    float *y_routed = at<float>(ws, p.y_routed);
     if (e == hipSuccess) {
-        FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
         if (sel_in_ffn) {
             a.fuse_select = 1;
             a.sel = select_args(*L, p, T, ids, w, keff, ws);

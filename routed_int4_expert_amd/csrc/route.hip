@@ -17,6 +17,7 @@
 // identically in every lane.
 #include <math.h>
 
+#include "router_gemv.h"
 #include "select_union.h"
 
 namespace moe {
@@ -101,46 +102,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LogitsArgs a) {
     }
 }
 
-// Few tokens: one workgroup per expert; its four waves split H, every lane
-// issues all its float4 loads of the router row at once, the row is applied to
-// every token with fp64 accumulation, and the four wave sums are added in a
-// fixed order.  Complete logits, a single slice (S = 1).
+// Few tokens: one workgroup per expert (router_gemv.h).
 template <int TT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(LogitsArgs a) {
-    __shared__ double red[4][TT];
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    const int n4 = a.H / 4;
-    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.H);
-    const float4 *x4 = reinterpret_cast<const float4 *>(a.x);
-    double acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; t++) acc[t] = 0.0;
-#pragma unroll 8
-    for (int j = threadIdx.x; j < n4; j += 256) {
-        const float4 w = w4[j];
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
-            if (t < a.T) {
-                const float4 v = x4[(size_t)t * n4 + j];
-                acc[t] = fma((double)v.x, (double)w.x, acc[t]);
-                acc[t] = fma((double)v.y, (double)w.y, acc[t]);
-                acc[t] = fma((double)v.z, (double)w.z, acc[t]);
-                acc[t] = fma((double)v.w, (double)w.w, acc[t]);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < TT; t++) {
-#pragma unroll
-        for (int m = kWave / 2; m > 0; m >>= 1) acc[t] += shfl_xor_f64(acc[t], m);
-        if (lane == 0) red[wv][t] = acc[t];
-    }
-    __syncthreads();
-    if (threadIdx.x < TT && (int)threadIdx.x < a.T) {
-        const int t = threadIdx.x;
-        a.part[(size_t)t * a.E + e] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
-    }
+    router_gemv_body<TT>(a, blockIdx.x);
 }
 
 hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st) {

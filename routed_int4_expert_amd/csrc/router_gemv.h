@@ -1,0 +1,56 @@
+// router_gemv.h -- step 1 of the MoE layer ("MoE 路由与专家流式加载" §1.1) for a
+// few tokens: the logits of one expert, logit[t][e] = Wr[e]·x[t], by one workgroup.
+// Its four waves split H, every lane issues all its float4 loads of the router row
+// at once, the row is applied to every token with exact fp32 products summed in
+// fp64, and the four wave sums are added in a fixed order.  Complete logits, a
+// single slice (S = 1).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ double router_shfl_xor_f64(double v, int m) {
+    const int lo = __shfl_xor(__double2loint(v), m, kWave);
+    const int hi = __shfl_xor(__double2hiint(v), m, kWave);
+    return __hiloint2double(hi, lo);
+}
+
+template <int TT>
+__device__ __forceinline__ void router_gemv_body(const LogitsArgs &a, int e) {
+    __shared__ double red[4][TT];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int n4 = a.H / 4;
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.H);
+    const float4 *x4 = reinterpret_cast<const float4 *>(a.x);
+    double acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) acc[t] = 0.0;
+#pragma unroll 8
+    for (int j = threadIdx.x; j < n4; j += 256) {
+        const float4 w = w4[j];
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+            if (t < a.T) {
+                const float4 v = x4[(size_t)t * n4 + j];
+                acc[t] = fma((double)v.x, (double)w.x, acc[t]);
+                acc[t] = fma((double)v.y, (double)w.y, acc[t]);
+                acc[t] = fma((double)v.z, (double)w.z, acc[t]);
+                acc[t] = fma((double)v.w, (double)w.w, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+#pragma unroll
+        for (int m = kWave / 2; m > 0; m >>= 1) acc[t] += router_shfl_xor_f64(acc[t], m);
+        if (lane == 0) red[wv][t] = acc[t];
+    }
+    __syncthreads();
+    if (threadIdx.x < TT && (int)threadIdx.x < a.T) {
+        const int t = threadIdx.x;
+        a.part[(size_t)t * a.E + e] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+    }
+}
+
+}  // namespace moe

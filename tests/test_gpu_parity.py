@@ -67,6 +67,8 @@ SMALL = [
              top_p=0.5, router_std=0.125, bias_amp=0.05),
     S.custom("onetok", hidden=512, n_experts=32, ffn=256, shared_ffn=256, top_k=4, tokens=1,
              routed_scale=2.5),
+    S.custom("onetok_noshared", hidden=256, n_experts=16, ffn=128, shared_ffn=0, top_k=4, tokens=1,
+             top_p=0.9),
     S.custom("twotok", hidden=2048, n_experts=64, ffn=512, shared_ffn=512, top_k=8, tokens=2,
              router_std=1 / 45.25),
     # few tokens with routed and shared FFN widths that split the down projection into two
