@@ -61,9 +61,18 @@ __device__ __forceinline__ uint32_t bf16_rne_u(float f) {
 // the order 0,4,1,5,2,6,3,7; and nsx[row][G] = -136 * sum of (hi + lo) over the
 // group.  Rows are NGp groups long (whole chunks).  One thread per word; the 8
 // words of a group are 8 adjacent lanes.
-__global__ __launch_bounds__(256) void prep_frag_kernel(const float *src, int rows, int K,
-                                                       uint8_t *frag, float *nsx) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // word index
+struct PrepJob {
+    const float *src;
+    int rows, K;
+    uint8_t *frag;
+    float *nsx;
+    int blocks;  // workgroups of 256 threads this job takes
+};
+
+__device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
+    const float *src = j.src;
+    const int rows = j.rows, K = j.K;
+    const long i = (long)blk * blockDim.x + threadIdx.x;  // word index
     const long nwd = (long)rows * (K / 8);
     const bool live = i < nwd;
     const long ii = live ? i : nwd - 1;
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(256) void prep_frag_kernel(const float *src, int ro
         part += hi + __uint_as_float(lb[s] << 16);
     }
     const int G = b / 8, w = b % 8;
-    uint8_t *grp = frag + ((size_t)row * NGp + G) * kGroupBytes;
+    uint8_t *grp = j.frag + ((size_t)row * NGp + G) * kGroupBytes;
     if (live) {
         *reinterpret_cast<uint4 *>(grp + 16 * w) =
             make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
@@ -96,25 +105,28 @@ __global__ __launch_bounds__(256) void prep_frag_kernel(const float *src, int ro
     // group sum over the 8 words = 8 adjacent lanes (K is a multiple of 64)
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) part += __shfl_xor(part, m, kWave);
-    if (live && w == 0) nsx[(size_t)row * NGp + G] = -kMfmaCodeOffset * part;
+    if (live && w == 0) j.nsx[(size_t)row * NGp + G] = -kMfmaCodeOffset * part;
 }
 
-hipError_t launch_prep_frag(const float *src, int rows, int K, uint8_t *frag, float *nsx,
-                            hipStream_t st) {
-    if (rows <= 0) return hipSuccess;
-    const long nwd = (long)rows * (K / 8);
-    ProfScope prof("prep_frag", st);
-    prep_frag_kernel<<<(unsigned)((nwd + 255) / 256), 256, 0, st>>>(src, rows, K, frag, nsx);
-    return hipGetLastError();
+static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *nsx) {
+    PrepJob j;
+    j.src = src;
+    j.rows = rows;
+    j.K = K;
+    j.frag = frag;
+    j.nsx = nsx;
+    const long nwd = rows > 0 ? (long)rows * (K / 8) : 0;
+    j.blocks = (int)((nwd + 255) / 256);
+    return j;
 }
 
 // ------------------------------------------------------------------ work list
 // Items in union order: expert uniq[u] with c rows gets ceil(c / 16) items of
 // consecutive rows.  One workgroup of 256 threads, one thread per union slot
 // (E <= 256); an exclusive scan of the item counts places each expert's items.
-__global__ __launch_bounds__(256) void mfma_items_kernel(const int32_t *n_uniq, const int32_t *uniq,
-                                                        const int32_t *off, int E, int32_t *items,
-                                                        int32_t *n_items) {
+__device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int32_t *uniq,
+                                                const int32_t *off, int E, int32_t *items,
+                                                int32_t *n_items) {
     __shared__ int wsum[256 / kWave];
     const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
     const int nu = n_uniq[0];
@@ -142,6 +154,34 @@ __global__ __launch_bounds__(256) void mfma_items_kernel(const int32_t *n_uniq, 
         it[3] = 0;
     }
     if (u == blockDim.x - 1) n_items[0] = base + ni;
+}
+
+// Up to two fragment preparations and, optionally, the work list, in one launch:
+// workgroups [0, j0.blocks) prepare job 0, the next j1.blocks job 1, and one more
+// builds the work list when `items` is set.
+struct ItemsJob {
+    const int32_t *n_uniq, *uniq, *off;
+    int E;
+    int32_t *items, *n_items;
+};
+
+__global__ __launch_bounds__(256) void prep_kernel(PrepJob j0, PrepJob j1, ItemsJob it) {
+    const int b = blockIdx.x;
+    if (b < j0.blocks)
+        prep_frag_body(j0, b);
+    else if (b < j0.blocks + j1.blocks)
+        prep_frag_body(j1, b - j0.blocks);
+    else if (it.items)
+        mfma_items_body(it.n_uniq, it.uniq, it.off, it.E, it.items, it.n_items);
+}
+
+static hipError_t launch_prep(const PrepJob &j0, const PrepJob &j1, const ItemsJob &it,
+                              const char *name, hipStream_t st) {
+    const int blocks = j0.blocks + j1.blocks + (it.items ? 1 : 0);
+    if (blocks == 0) return hipSuccess;
+    ProfScope prof(name, st);
+    prep_kernel<<<blocks, 256, 0, st>>>(j0, j1, it);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ grouped GEMM
@@ -427,16 +467,20 @@ __global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
     }
 }
 
-// x prepared once; the work list; gate/up for every item; h prepared; down.
+// x prepared once with the work list; gate/up for every item; the routed and shared
+// h prepared together; down.
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     hipError_t e;
-    e = launch_prep_frag(a.x, a.T, a.H, a.x_frag, a.x_nsx, st);
+    const PrepJob none = prep_job(nullptr, 0, 64, nullptr, nullptr);
+    ItemsJob it;
+    it.n_uniq = a.n_uniq;
+    it.uniq = a.uniq;
+    it.off = a.off;
+    it.E = a.E;
+    it.items = a.with_routed ? a.items : nullptr;
+    it.n_items = a.n_items;
+    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_nsx), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
-    if (a.with_routed) {
-        ProfScope prof("mfma_items", st);
-        mfma_items_kernel<<<1, 256, 0, st>>>(a.n_uniq, a.uniq, a.off, a.E, a.items, a.n_items);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
     const int nmax = a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F;
     {
@@ -447,14 +491,12 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     }
     // h rows in fragment order: the routed rows (as many as the largest union can
     // have) and the shared rows
-    if (a.with_routed) {
-        e = launch_prep_frag(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_nsx, st);
-        if (e != hipSuccess) return e;
-    }
-    if (a.with_shared) {
-        e = launch_prep_frag(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx, st);
-        if (e != hipSuccess) return e;
-    }
+    ItemsJob no_items = it;
+    no_items.items = nullptr;
+    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_nsx) : none,
+                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx) : none,
+                    no_items, "prep_h", st);
+    if (e != hipSuccess) return e;
     {
         dim3 grid((a.H + 255) / 256, a.max_items + shared_items);
         ProfScope prof("ffn_down_mfma", st);

@@ -31,8 +31,10 @@ RouterSplit router_split(int T, int E, int H) {
     }
     const int tiles = ((T + kRouterTile - 1) / kRouterTile) * ((E + kRouterTile - 1) / kRouterTile);
     const int chunks = H / kRouterKC;
+    // enough H slices that the launch has about one workgroup per CU (the slices'
+    // partial logits are summed in slice order by the selection)
     int S = (256 + tiles - 1) / tiles;
-    if (S > 16) S = 16;
+    if (S > 64) S = 64;
     if (S > chunks) S = chunks;
     if (S < 1) S = 1;
     const int per = (chunks + S - 1) / S;
@@ -124,19 +126,22 @@ hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ selection
+// One workgroup per token: each thread sums one expert's logit over the router's
+// slices (coalesced over experts), then one wave selects from LDS.
 __global__ __launch_bounds__(256) void route_select_kernel(SelectArgs a) {
-    __shared__ PickScratch ps[256 / kWave];
-    const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
-    const int t = blockIdx.x * 4 + wv;
-    if (t >= a.T) return;  // whole wave leaves together
-    select_token(a, t, lane, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.keff + t, nullptr,
-                 nullptr, &ps[wv]);
+    __shared__ PickScratch ps;
+    __shared__ double lg[MOE_MAX_EXPERTS];
+    const int t = blockIdx.x;
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x) lg[e] = sum_partials(a, t, e);
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;
+    select_token(a, t, threadIdx.x, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.keff + t,
+                 nullptr, nullptr, &ps, lg);
 }
 
 hipError_t launch_route_select(const SelectArgs &a, hipStream_t st) {
     ProfScope prof("route_select", st);
-    route_select_kernel<<<(a.T + 3) / 4, 256, 0, st>>>(a);
+    route_select_kernel<<<a.T, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -144,21 +149,25 @@ hipError_t launch_route_select(const SelectArgs &a, hipStream_t st) {
 // union from the picks it keeps in LDS, saving a launch and a round trip.
 __global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionArgs u) {
     __shared__ PickScratch ps[kSelectUnionTokens];
-    extern __shared__ uint32_t lds[];
-    int32_t *ids_l = reinterpret_cast<int32_t *>(lds);
+    extern __shared__ double lds_d[];
+    double *lg = lds_d;  // [T][E] logits, summed over the router's slices by all threads
+    int32_t *ids_l = reinterpret_cast<int32_t *>(lg + (size_t)s.T * s.E);
     int32_t *keff_l = ids_l + s.T * s.k;
     uint32_t *scratch = reinterpret_cast<uint32_t *>(keff_l + s.T);
+    for (int i = threadIdx.x; i < s.T * s.E; i += blockDim.x) lg[i] = sum_partials(s, i / s.E, i % s.E);
+    __syncthreads();
     const int lane = threadIdx.x % kWave;
     const int t = threadIdx.x / kWave;
     if (t < s.T)
         select_token(s, t, lane, s.ids + (size_t)t * s.k, s.w + (size_t)t * s.k, s.keff + t,
-                     ids_l + t * s.k, keff_l + t, &ps[t]);
+                     ids_l + t * s.k, keff_l + t, &ps[t], lg + (size_t)t * s.E);
     __syncthreads();
     union_block(u, ids_l, keff_l, scratch);
 }
 
 hipError_t launch_select_union(const SelectArgs &s, const UnionArgs &u, hipStream_t st) {
-    const size_t lds = ((size_t)s.T * s.k + s.T + union_lds_words(u.E, u.T)) * sizeof(uint32_t);
+    const size_t lds = (size_t)s.T * s.E * sizeof(double) +
+                       ((size_t)s.T * s.k + s.T + union_lds_words(u.E, u.T)) * sizeof(uint32_t);
     ProfScope prof("select_union", st);
     // a wave per token, at least four waves for the union
     const int threads = max(256, kWave * s.T);

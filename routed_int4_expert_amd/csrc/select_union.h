@@ -51,9 +51,26 @@ __device__ __forceinline__ void wave_lds_sync() {
 // descending, lower id first).
 // Lane j < k ends up holding pick j.  Writes ids/w (this token's k slots) and
 // *keff; when ids_copy/keff_copy are given, the ids and keff are written there too.
+// The logit of (t, e): the router's slice partials added in slice order.
+__device__ __forceinline__ double sum_partials(const SelectArgs &a, int t, int e) {
+    double l = 0.0;
+    int s = 0;
+    for (; s + 8 <= a.S; s += 8) {  // loads issued eight at a time
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = a.part[((size_t)(s + u) * a.T + t) * a.E + e];
+#pragma unroll
+        for (int u = 0; u < 8; u++) l += v[u];
+    }
+    for (; s < a.S; s++) l += a.part[((size_t)s * a.T + t) * a.E + e];
+    return l;
+}
+
+// lg: this token's E logits already summed (in LDS), or null to sum them here.
 __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
                                              float *w, int32_t *keff_out, int32_t *ids_copy,
-                                             int32_t *keff_copy, PickScratch *ps) {
+                                             int32_t *keff_copy, PickScratch *ps,
+                                             const double *lg = nullptr) {
     constexpr int EPL = MOE_MAX_EXPERTS / kWave;  // experts per lane (4)
     double sig[EPL];
     unsigned long long key[EPL];
@@ -63,17 +80,7 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         sig[i] = 0.0;
         key[i] = 0ull;  // below every live key
         if (e < a.E) {
-            // slice partials added in slice order; loads issued eight at a time
-            double l = 0.0;
-            int s = 0;
-            for (; s + 8 <= a.S; s += 8) {
-                double v[8];
-#pragma unroll
-                for (int u = 0; u < 8; u++) v[u] = a.part[((size_t)(s + u) * a.T + t) * a.E + e];
-#pragma unroll
-                for (int u = 0; u < 8; u++) l += v[u];
-            }
-            for (; s < a.S; s++) l += a.part[((size_t)s * a.T + t) * a.E + e];
+            const double l = lg ? lg[e] : sum_partials(a, t, e);
             sig[i] = 1.0 / (1.0 + exp(-l));
             const double b = a.bias ? (double)a.bias[e] : 0.0;
             const double c = sig[i] + b;
