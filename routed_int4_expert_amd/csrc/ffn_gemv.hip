@@ -81,47 +81,117 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Selection and union for the few tokens of a decode step, by one workgroup into
-// LDS ([R] §1.1-§1.3; select_token and union_block as in the select+union kernel):
-// lds = ids[T*k] w[T*k] keff[T] n_uniq[1] uniq[E] off[E+1] row_tok[T*k] pick_row[T*k]
-// scratch.  Workgroup (0,0) also writes them to global memory for the later launches.
-// Compiled into the one-row kernels only (one token), where it adds no register spills.
-__device__ __forceinline__ void select_and_union_lds(const FfnArgs &a, int32_t *lds, bool writer) {
-    __shared__ PickScratch ps_sel[kGemvMaxTokens];
-    const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
+// Selection and union of a one-token decode step, by wave 0 into LDS ([R] §1.1-§1.3;
+// select_token as in the selection kernels).  One token picks an expert at most once,
+// so the union is its kept picks in increasing expert order, one row each, and needs
+// no block-wide passes.  LDS layout (the general one at T = 1):
+// ids[k] w[k] keff[1] n_uniq[1] uniq[E] off[E+1] row_tok[k] pick_row[k].
+// With `writer` the wave also writes them to global memory for the later launches.
+__device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds, bool writer) {
+    __shared__ PickScratch ps_sel;
+    const int k = a.sel.k, E = a.sel.E;
+    const int lane = threadIdx.x % kWave;
     int32_t *ids_l = lds;
-    float *w_l = reinterpret_cast<float *>(ids_l + T * k);
-    int32_t *keff_l = reinterpret_cast<int32_t *>(w_l + T * k);
-    int32_t *nu_l = keff_l + T;
+    float *w_l = reinterpret_cast<float *>(ids_l + k);
+    int32_t *keff_l = reinterpret_cast<int32_t *>(w_l + k);
+    int32_t *nu_l = keff_l + 1;
     int32_t *uniq_l = nu_l + 1;
     int32_t *off_l = uniq_l + E;
     int32_t *rt_l = off_l + E + 1;
-    int32_t *pick_l = rt_l + T * k;
-    uint32_t *scr = reinterpret_cast<uint32_t *>(pick_l + T * k);
-    const int t = threadIdx.x / kWave;
-    if (t < T)
-        select_token(a.sel, t, threadIdx.x % kWave, ids_l + t * k, w_l + t * k, keff_l + t, nullptr,
-                     nullptr, &ps_sel[t]);
-    __syncthreads();
-    UnionArgs u = a.uni;
-    u.n_uniq = nu_l;
-    u.uniq = uniq_l;
-    u.off = off_l;
-    u.row_tok = rt_l;
-    u.pick_row = pick_l;
-    union_block(u, ids_l, keff_l, scr);
-    __syncthreads();
+    int32_t *pick_l = rt_l + k;
+    // byte flags of the kept experts (in the pick scratch's place: the selection is done)
+    uint8_t *flag = reinterpret_cast<uint8_t *>(&ps_sel);
+    static_assert(sizeof(PickScratch) >= MOE_MAX_EXPERTS, "flag bytes fit the scratch");
+    select_token(a.sel, 0, lane, ids_l, w_l, keff_l, nullptr, nullptr, &ps_sel);
+    wave_lds_sync();
+    const int keff = *keff_l;
+    const int my = lane < keff ? ids_l[lane] : -1;
+    reinterpret_cast<uint32_t *>(flag)[lane] = 0u;  // 256 bytes
+    wave_lds_sync();
+    if (my >= 0) flag[my] = 1;
+    wave_lds_sync();
+    // lane l owns experts 4l .. 4l+3: off[e] = kept experts below e, from the flags'
+    // ballots (flags of expert 4l + m are bit l of ballot m)
+    const uint32_t f4 = reinterpret_cast<const uint32_t *>(flag)[lane];
+    unsigned long long bm[4];
+    int before = 0;  // kept experts in lanes below this one
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        bm[m] = __ballot((f4 >> (8 * m)) & 1u);
+        before += __popcll(bm[m] & ((1ull << lane) - 1ull));
+    }
+    int run = before;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const int e = 4 * lane + m;
+        const bool kept = (f4 >> (8 * m)) & 1u;
+        if (e < E) {
+            off_l[e] = run;
+            if (kept) uniq_l[run] = e;
+        }
+        run += kept ? 1 : 0;
+    }
+    for (int i = keff + lane; i < E; i += kWave) uniq_l[i] = -1;
+    if (lane == 0) {
+        off_l[E] = keff;
+        nu_l[0] = keff;
+    }
+    wave_lds_sync();
+    if (lane < k) {  // a kept pick's row: its expert's offset
+        pick_l[lane] = my >= 0 ? off_l[my] : -1;
+        rt_l[lane] = my >= 0 ? 0 : -1;
+    }
+    wave_lds_sync();
     if (writer) {
-        for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+        for (int i = lane; i < k; i += kWave) {
             a.sel.ids[i] = ids_l[i];
             a.sel.w[i] = w_l[i];
             a.uni.row_tok[i] = rt_l[i];
             a.uni.pick_row[i] = pick_l[i];
         }
-        for (int i = threadIdx.x; i < T; i += blockDim.x) a.sel.keff[i] = keff_l[i];
-        for (int i = threadIdx.x; i < E; i += blockDim.x) a.uni.uniq[i] = uniq_l[i];
-        for (int i = threadIdx.x; i <= E; i += blockDim.x) a.uni.off[i] = off_l[i];
-        if (threadIdx.x == 0) a.uni.n_uniq[0] = nu_l[0];
+        for (int i = lane; i < E; i += kWave) a.uni.uniq[i] = uniq_l[i];
+        for (int i = lane; i <= E; i += kWave) a.uni.off[i] = off_l[i];
+        if (lane == 0) {
+            a.sel.keff[0] = keff;
+            a.uni.n_uniq[0] = keff;
+        }
+    }
+}
+
+// Stages R input rows as bf16 hi/lo pairs in dot order, with each 32-element chunk's
+// sum of the staged values, by threads [t0, t0 + nt) of the block (t0, nt multiples of
+// 4): a thread per 8 elements; the 4 threads of a chunk are adjacent lanes and add
+// their partial sums with two shuffles.
+__device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
+                                           const int32_t *rt, int rc, int R, int K, int t0, int nt) {
+    uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
+    const int n8 = R * (K / 8);
+    for (int i = (int)threadIdx.x - t0; i < n8; i += nt) {
+        const int r = i / (K / 8), g = i % (K / 8);
+        const int src = rt ? rt[rc + r] : rc + r;
+        const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
+        const float4 v0 = px[0], v1 = px[1];
+        const float xe[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint32_t hb[8], lb[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            hb[e] = bf16_rne_bits(xe[e]);
+            lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
+            ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
+        }
+        uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
+        w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
+        w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
+        w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
+        w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
+        uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
+        uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
+        dst[0] = w0;
+        dst[1] = w1;
+        ps += __shfl_xor(ps, 1, kWave);
+        ps += __shfl_xor(ps, 2, kWave);
+        if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
     }
 }
 
@@ -145,16 +215,23 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
     extern __shared__ float xs[];  // [RM][C * kChunkPitch] (+ selection and union, when fused)
     const int H = a.H;
 
-    // ---- the union: from global memory, or selected here ([R] §1.1-§1.3) into LDS
+    // ---- the union: from global memory, or, for one token, selected here ([R] §1.1-§1.3)
+    // into LDS by wave 0 while the other waves stage the token's row
     const int32_t *n_uniq_p = a.n_uniq, *uniq_p = a.uniq, *off_p = a.off, *row_tok_p = a.row_tok;
+    bool staged = false;
     if constexpr (GU && RM == 1) if (a.fuse_select && unit < a.max_units && a.with_routed) {
-        int32_t *lds = reinterpret_cast<int32_t *>(xs + (size_t)RM * (H / 32) * kChunkPitch);
-        select_and_union_lds(a, lds, bx == 0 && unit == 0);
-        const int T = a.sel.T, k = a.sel.k, E = a.sel.E;
-        n_uniq_p = lds + 2 * T * k + T;
+        int32_t *lds = reinterpret_cast<int32_t *>(xs + (size_t)(H / 32) * kChunkPitch);
+        if (threadIdx.x < kWave)
+            select_union_one(a, lds, bx == 0 && unit == 0);
+        else
+            stage_rows(xs, (H / 32) * kChunkPitch, a.x, nullptr, 0, 1, H, kWave, blockDim.x - kWave);
+        __syncthreads();
+        const int k = a.sel.k, E = a.sel.E;
+        n_uniq_p = lds + 2 * k + 1;
         uniq_p = n_uniq_p + 1;
         off_p = uniq_p + E;
         row_tok_p = off_p + E + 1;
+        staged = true;
     }
 
     // ---- the unit: a routed expert of the union, or the shared expert
@@ -243,44 +320,11 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
 
     for (int rc = 0; rc < nrows; rc += RM) {
         const int R = min(RM, nrows - rc);
-        __syncthreads();  // previous rows fully consumed
-        // stage R input rows as bf16 hi/lo pairs in dot order: one thread per 8 elements
-        uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
-        for (int i = tid; i < R * (K / 8); i += blockDim.x) {
-            const int r = i / (K / 8), g = i % (K / 8);
-            const int src = rt ? rt[rc + r] : rc + r;
-            const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
-            const float4 v0 = px[0], v1 = px[1];
-            const float xe[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t hb[8], lb[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                hb[e] = bf16_rne_bits(xe[e]);
-                lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
-            }
-            uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
-            w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
-            w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
-            w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
-            w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
-            uint4 *dst = reinterpret_cast<uint4 *>(xw + r * rowpitch + (g / 4) * kChunkPitch + (g % 4) * 8);
-            dst[0] = w0;
-            dst[1] = w1;
+        if (!(staged && rc == 0)) {
+            __syncthreads();  // previous rows fully consumed
+            stage_rows(xs, rowpitch, xin, rt, rc, R, K, 0, blockDim.x);
+            __syncthreads();
         }
-        __syncthreads();
-        // per chunk: the sum of the staged values (hi + lo), fp32
-        for (int i = tid; i < R * C; i += blockDim.x) {
-            const int r = i / C, c = i % C;
-            const uint32_t *p = xw + r * rowpitch + c * kChunkPitch;
-            float sacc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 32; j++) {
-                const uint32_t v = p[j];
-                sacc += bf16_to_f32(v & 0xFFFFu) + bf16_to_f32(v >> 16);
-            }
-            xs[r * rowpitch + c * kChunkPitch + 32] = sacc;
-        }
-        __syncthreads();
 
         if (rc > 0) load_step(0, q, sc);  // rows beyond the first RM restart the weight stream
         // one step: prefetch the next step's rows into (qn, scn), compute with (qc, scc)

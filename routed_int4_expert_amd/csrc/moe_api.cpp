@@ -127,6 +127,10 @@ Plan make_plan(const moe_layer &L, int T) {
         return at;
     };
     p.part = take(router_part_bytes(L, (int)Tz));
+    if (Tz <= (size_t)kRouterGemvTokens) {  // the one-slice router also gives gates and keys
+        p.sig = take(Tz * E * 8);
+        p.key = take(Tz * E * 8);
+    }
     p.ids = take(Tz * k * 4);
     p.w = take(Tz * k * 4);
     p.keff = take(Tz * 4);
@@ -168,6 +172,8 @@ static SelectArgs select_args(const moe_layer &L, const Plan &p, int T, int32_t 
     SelectArgs sa;
     sa.part = at<double>(ws, p.part);
     sa.bias = L.router_bias;
+    sa.sig_in = p.sig ? at<double>(ws, p.sig) : nullptr;
+    sa.key_in = p.sig ? at<unsigned long long>(ws, p.key) : nullptr;
     sa.ids = ids;
     sa.w = w;
     sa.keff = keff;
@@ -204,6 +210,9 @@ static hipError_t run_logits(const moe_layer &L, const Plan &p, const float *x, 
     la.x = x;
     la.wr = L.router_w;
     la.part = at<double>(ws, p.part);
+    la.bias = L.router_bias;
+    la.sig = p.sig ? at<double>(ws, p.sig) : nullptr;
+    la.key = p.sig ? at<unsigned long long>(ws, p.key) : nullptr;
     la.T = T;
     la.E = L.n_experts;
     la.H = L.hidden;

@@ -34,6 +34,7 @@ struct Plan {
     RouterSplit rs;
     int max_units;   // routed units a launch must cover: min(E, T*k)
     size_t part;     // fp64 [S][T][E] router partial logits
+    size_t sig, key; // fp64 / u64 [T][E] gates and choice keys (router of a few tokens), or 0
     size_t ids, w, keff;                           // routing, when the caller gives none
     size_t n_uniq, uniq, off, row_tok, pick_row;   // union, when the caller gives none
     size_t h_routed;  // fp32 [T*k][F]  SiLU(gate) * up per routed row
@@ -52,12 +53,19 @@ struct LogitsArgs {
     const float *x;       // [T][H]
     const float *wr;      // [E][H]
     double *part;         // [S][T][E]
+    // complete logits only (S = 1): the sigmoid gate and choice key of every (t, e),
+    // or nullptr
+    const float *bias;    // [E] or nullptr
+    double *sig;          // [T][E]
+    unsigned long long *key;  // [T][E]
     int T, E, H, kslice;
 };
 
 struct SelectArgs {
     const double *part;   // [S][T][E]
     const float *bias;    // [E] or nullptr
+    const double *sig_in;  // [T][E] gates and choice keys from the router, or nullptr
+    const unsigned long long *key_in;
     int32_t *ids;         // [T][k]
     float *w;             // [T][k]
     int32_t *keff;        // [T]

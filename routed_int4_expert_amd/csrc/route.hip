@@ -132,8 +132,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(SelectArgs a) {
     __shared__ PickScratch ps;
     __shared__ double lg[MOE_MAX_EXPERTS];
     const int t = blockIdx.x;
-    for (int e = threadIdx.x; e < a.E; e += blockDim.x) lg[e] = sum_partials(a, t, e);
-    __syncthreads();
+    if (!a.key_in) {
+        for (int e = threadIdx.x; e < a.E; e += blockDim.x) lg[e] = sum_partials(a, t, e);
+        __syncthreads();
+    }
     if (threadIdx.x >= kWave) return;
     select_token(a, t, threadIdx.x, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.keff + t,
                  nullptr, nullptr, &ps, lg);
@@ -154,8 +156,10 @@ __global__ __launch_bounds__(1024) void select_union_kernel(SelectArgs s, UnionA
     int32_t *ids_l = reinterpret_cast<int32_t *>(lg + (size_t)s.T * s.E);
     int32_t *keff_l = ids_l + s.T * s.k;
     uint32_t *scratch = reinterpret_cast<uint32_t *>(keff_l + s.T);
-    for (int i = threadIdx.x; i < s.T * s.E; i += blockDim.x) lg[i] = sum_partials(s, i / s.E, i % s.E);
-    __syncthreads();
+    if (!s.key_in) {
+        for (int i = threadIdx.x; i < s.T * s.E; i += blockDim.x) lg[i] = sum_partials(s, i / s.E, i % s.E);
+        __syncthreads();
+    }
     const int lane = threadIdx.x % kWave;
     const int t = threadIdx.x / kWave;
     if (t < s.T)

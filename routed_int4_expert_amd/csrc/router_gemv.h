@@ -3,10 +3,11 @@
 // Its four waves split H, every lane issues all its float4 loads of the router row
 // at once, the row is applied to every token with exact fp32 products summed in
 // fp64, and the four wave sums are added in a fixed order.  Complete logits, a
-// single slice (S = 1).
+// single slice (S = 1); with `sig` set, also each logit's sigmoid gate and choice key.
 #pragma once
 
 #include "moe_internal.h"
+#include "select_union.h"
 
 namespace moe {
 
@@ -49,7 +50,15 @@ __device__ __forceinline__ void router_gemv_body(const LogitsArgs &a, int e) {
     __syncthreads();
     if (threadIdx.x < TT && (int)threadIdx.x < a.T) {
         const int t = threadIdx.x;
-        a.part[(size_t)t * a.E + e] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+        const double l = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+        a.part[(size_t)t * a.E + e] = l;
+        if (a.sig) {  // the logit is complete: its gate and choice key too
+            double sg;
+            unsigned long long ky;
+            gate_and_key(l, a.bias, e, sg, ky);
+            a.sig[(size_t)t * a.E + e] = sg;
+            a.key[(size_t)t * a.E + e] = ky;
+        }
     }
 }
 

@@ -29,12 +29,40 @@ __device__ __forceinline__ unsigned long long mono_key(double v) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Per-wave LDS scratch of select_token: the k picks, compacted.
+// The sigmoid gate of a logit and the monotone key of its choice score ([R] §1.1:
+// sig = 1 / (1 + exp(-logit)), choice = sig + bias), fp64.
+__device__ __forceinline__ void gate_and_key(double l, const float *bias, int e, double &sig,
+                                             unsigned long long &key) {
+    sig = 1.0 / (1.0 + exp(-l));
+    const double b = bias ? (double)bias[e] : 0.0;
+    const double c = sig + b;
+    key = mono_key(isnan(c) ? -INFINITY : c);
+}
+
+// Per-wave LDS scratch of select_token: the k picks, compacted (expert order).
 struct PickScratch {
     unsigned long long key[MOE_MAX_TOPK];
     double sig[MOE_MAX_TOPK];
     int id[MOE_MAX_TOPK];
 };
+
+__device__ __forceinline__ unsigned long long wave_and_u64(unsigned long long v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+        v &= ((unsigned long long)hi << 32) | lo;
+    }
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_or_u64(unsigned long long v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+        v |= ((unsigned long long)hi << 32) | lo;
+    }
+    return v;
+}
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -66,7 +94,8 @@ __device__ __forceinline__ double sum_partials(const SelectArgs &a, int t, int e
     return l;
 }
 
-// lg: this token's E logits already summed (in LDS), or null to sum them here.
+// lg: this token's E logits already summed (in LDS), or null to sum them here; both
+// unused when the router gave the gates and keys.
 __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
                                              float *w, int32_t *keff_out, int32_t *ids_copy,
                                              int32_t *keff_copy, PickScratch *ps,
@@ -80,20 +109,34 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         sig[i] = 0.0;
         key[i] = 0ull;  // below every live key
         if (e < a.E) {
-            const double l = lg ? lg[e] : sum_partials(a, t, e);
-            sig[i] = 1.0 / (1.0 + exp(-l));
-            const double b = a.bias ? (double)a.bias[e] : 0.0;
-            const double c = sig[i] + b;
-            key[i] = mono_key(isnan(c) ? -INFINITY : c);
+            if (a.key_in) {  // computed by the router
+                sig[i] = a.sig_in[(size_t)t * a.E + e];
+                key[i] = a.key_in[(size_t)t * a.E + e];
+            } else {
+                gate_and_key(lg ? lg[e] : sum_partials(a, t, e), a.bias, e, sig[i], key[i]);
+            }
         }
     }
 
     // thr = the k-th largest key: the largest value with at least k keys >= it, built
     // bit by bit.  As soon as exactly k keys are >= a candidate, those k are the picks
-    // (no key equal to the k-th is left out), which ends the search early.
-    unsigned long long thr = 0ull;
+    // (no key equal to the k-th is left out), which ends the search early.  Bits above
+    // the highest one in which the live keys differ are the same in all of them, so
+    // thr starts with them and the search starts below (there are at least k live keys).
+    unsigned long long kand = ~0ull, kor = 0ull;
+#pragma unroll
+    for (int i = 0; i < EPL; i++)
+        if (lane + kWave * i < a.E) {
+            kand &= key[i];
+            kor |= key[i];
+        }
+    kand = wave_and_u64(kand);
+    kor = wave_or_u64(kor);
+    const unsigned long long diff = kand ^ kor;
+    const int top = diff ? 63 - __clzll((long long)diff) : -1;  // highest differing bit
+    unsigned long long thr = top >= 63 ? 0ull : kor & ~((2ull << top) - 1ull);
     bool exact = false;
-    for (int bit = 63; bit >= 0; bit--) {
+    for (int bit = top; bit >= 0; bit--) {
         const unsigned long long cand = thr | (1ull << bit);
         int cnt = 0;
 #pragma unroll
@@ -138,6 +181,10 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         base += __popcll(sm);
     }
     wave_lds_sync();
+    // rank of pick j (choice descending, equal choices by lower id): the k <= 16 picks
+    // sit in lanes 0-15 (the rest padded with key 0 and the largest id, which no pick
+    // ranks below), and each lane compares its pick with the other 15 lanes of that
+    // row, rotated past it
     unsigned long long mk = 0ull;
     int mid = 0x7fffffff;
     double msig = 0.0;
@@ -146,28 +193,32 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         mid = ps->id[lane];
         msig = ps->sig[lane];
     }
-    // rank of pick j (choice descending, equal choices by lower id), the other picks
-    // read from their lanes through scalar registers
+    const int mk_lo = (int)(uint32_t)mk, mk_hi = (int)(uint32_t)(mk >> 32);
     int rank = 0;
-    for (int i = 0; i < a.k; i++) {
-        const unsigned long long ok =
-            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(mk >> 32), i) << 32) |
-            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mk, i);
-        const int oid = __builtin_amdgcn_readlane(mid, i);
-        rank += (ok > mk || (ok == mk && oid < mid)) ? 1 : 0;
+    // DPP row_ror:r (control 0x120 + r) gives each lane the value of lane (l + r) mod 16
+    // of its row
+#define MOE_RANK_STEP(r)                                                                \
+    {                                                                                   \
+        const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp(mk_lo, 0x120 + (r), 0xF, 0xF, false); \
+        const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp(mk_hi, 0x120 + (r), 0xF, 0xF, false); \
+        const int oid = __builtin_amdgcn_mov_dpp(mid, 0x120 + (r), 0xF, 0xF, false);  \
+        const unsigned long long ok = ((unsigned long long)ohi << 32) | olo;            \
+        rank += (ok > mk || (ok == mk && oid < mid)) ? 1 : 0;                           \
     }
-    // slot r takes the pick of rank r: find it with a ballot per slot
+    MOE_RANK_STEP(1) MOE_RANK_STEP(2) MOE_RANK_STEP(3) MOE_RANK_STEP(4) MOE_RANK_STEP(5)
+    MOE_RANK_STEP(6) MOE_RANK_STEP(7) MOE_RANK_STEP(8) MOE_RANK_STEP(9) MOE_RANK_STEP(10)
+    MOE_RANK_STEP(11) MOE_RANK_STEP(12) MOE_RANK_STEP(13) MOE_RANK_STEP(14) MOE_RANK_STEP(15)
+#undef MOE_RANK_STEP
+    // slot r takes the pick of rank r: each pick is pushed to lane `rank`
+    const int dst = lane < a.k ? rank : lane;
+    const int my_id_p = __builtin_amdgcn_ds_permute(4 * dst, mid);
+    const int sg_lo = __builtin_amdgcn_ds_permute(4 * dst, __double2loint(msig));
+    const int sg_hi = __builtin_amdgcn_ds_permute(4 * dst, __double2hiint(msig));
     int my_id = -1;
     double my_sig = 0.0;
-    for (int r = 0; r < a.k; r++) {
-        const unsigned long long m = __ballot(lane < a.k && rank == r);
-        const int src = __ffsll((long long)m) - 1;
-        const int id_r = __builtin_amdgcn_readlane(mid, src);
-        const double sig_r = readlane_f64(msig, src);
-        if (lane == r) {
-            my_id = id_r;
-            my_sig = sig_r;
-        }
+    if (lane < a.k) {
+        my_id = my_id_p;
+        my_sig = __hiloint2double(sg_hi, sg_lo);
     }
 
     // adaptive top-p: rank of each pick by sig descending (equal sigs in slot order);
