@@ -160,38 +160,55 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
 
 // Stages R input rows as bf16 hi/lo pairs in dot order, with each 32-element chunk's
 // sum of the staged values, by threads [t0, t0 + nt) of the block (t0, nt multiples of
-// 4): a thread per 8 elements; the 4 threads of a chunk are adjacent lanes and add
-// their partial sums with two shuffles.
+// 4): a thread per 8 elements, loads issued four items at a time before any is
+// converted; the 4 threads of a chunk are adjacent lanes and add their partial sums
+// with two shuffles.
 __device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
                                            const int32_t *rt, int rc, int R, int K, int t0, int nt) {
+    constexpr int B = 4;
     uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
     const int n8 = R * (K / 8);
-    for (int i = (int)threadIdx.x - t0; i < n8; i += nt) {
-        const int r = i / (K / 8), g = i % (K / 8);
-        const int src = rt ? rt[rc + r] : rc + r;
-        const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
-        const float4 v0 = px[0], v1 = px[1];
-        const float xe[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        uint32_t hb[8], lb[8];
-        float ps = 0.f;
+    for (int i0 = (int)threadIdx.x - t0; i0 < n8; i0 += B * nt) {
+        float4 v[B][2];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            hb[e] = bf16_rne_bits(xe[e]);
-            lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
-            ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
+        for (int b = 0; b < B; b++) {
+            const int i = i0 + b * nt;
+            if (i < n8) {
+                const int r = i / (K / 8), g = i % (K / 8);
+                const int src = rt ? rt[rc + r] : rc + r;
+                const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
+                v[b][0] = px[0];
+                v[b][1] = px[1];
+            }
         }
-        uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
-        w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
-        w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
-        w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
-        w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
-        uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
-        uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
-        dst[0] = w0;
-        dst[1] = w1;
-        ps += __shfl_xor(ps, 1, kWave);
-        ps += __shfl_xor(ps, 2, kWave);
-        if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const int i = i0 + b * nt;
+            if (i >= n8) continue;  // the same for the 4 lanes of a chunk
+            const int r = i / (K / 8), g = i % (K / 8);
+            const float xe[8] = {v[b][0].x, v[b][0].y, v[b][0].z, v[b][0].w,
+                                 v[b][1].x, v[b][1].y, v[b][1].z, v[b][1].w};
+            uint32_t hb[8], lb[8];
+            float ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                hb[e] = bf16_rne_bits(xe[e]);
+                lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
+                ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
+            }
+            uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
+            w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
+            w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
+            w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
+            w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
+            uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
+            uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
+            dst[0] = w0;
+            dst[1] = w1;
+            ps += __shfl_xor(ps, 1, kWave);
+            ps += __shfl_xor(ps, 2, kWave);
+            if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
+        }
     }
 }
 

@@ -407,6 +407,17 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
         e = run_route(*L, p, x, T, ids, w, keff, ws, st);
         if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
     }
+    CombineArgs c;
+    c.w = w;
+    c.keff = keff;
+    c.pick_row = pick_row;
+    c.y_routed = y_routed;
+    c.y_shared = L->shared_ffn > 0 ? at<float>(ws, p.y_shared) : nullptr;
+    c.out = out;
+    c.T = T;
+    c.H = L->hidden;
+    c.k = L->top_k;
+    c.out_bf16 = out_dtype == MOE_BF16;
     if (e == hipSuccess) {
         if (sel_in_ffn) {
             a.fuse_select = 1;
@@ -415,20 +426,7 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
         }
         e = run_ffn(a, p, L->n_experts, L->top_k, ws, st);
     }
-    if (e == hipSuccess) {
-        CombineArgs c;
-        c.w = w;
-        c.keff = keff;
-        c.pick_row = pick_row;
-        c.y_routed = y_routed;
-        c.y_shared = L->shared_ffn > 0 ? at<float>(ws, p.y_shared) : nullptr;
-        c.out = out;
-        c.T = T;
-        c.H = L->hidden;
-        c.k = L->top_k;
-        c.out_bf16 = out_dtype == MOE_BF16;
-        e = launch_combine(c, st);
-    }
+    if (e == hipSuccess) e = launch_combine(c, st);
     return launched(e);
 }
 

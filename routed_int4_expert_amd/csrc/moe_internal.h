@@ -82,6 +82,16 @@ struct UnionArgs {
 
 // One "unit" of expert work: a routed expert of the union (unit < max_units),
 // or the shared expert (unit == max_units, rows = all T tokens).
+struct CombineArgs {
+    const float *w;         // [T][k]
+    const int32_t *keff;    // [T]
+    const int32_t *pick_row;// [T][k]
+    const float *y_routed;  // [rows][H]
+    const float *y_shared;  // [T][H] or nullptr
+    void *out;              // [T][H] fp32 or bf16
+    int T, H, k, out_bf16;
+};
+
 struct FfnArgs {
     const float *x;                  // [T][H] tokens
     const int32_t *n_uniq, *uniq, *off, *row_tok;
@@ -140,15 +150,6 @@ inline int mfma_max_items(int max_units, int max_rows) {
 
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
 
-struct CombineArgs {
-    const float *w;         // [T][k]
-    const int32_t *keff;    // [T]
-    const int32_t *pick_row;// [T][k]
-    const float *y_routed;  // [rows][H]
-    const float *y_shared;  // [T][H] or nullptr
-    void *out;              // [T][H] fp32 or bf16
-    int T, H, k, out_bf16;
-};
 
 // Bracketing HIP events around one kernel launch while moe_prof_begin() is active.
 struct ProfScope {
