@@ -201,270 +201,340 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Persistent grouped GEMM.  A workgroup of eight waves runs per CU and loops over work
+// items (16-row item, output block) wi = blockIdx.x + k * gridDim.x.  Waves 0-3
+// compute, waves 4-7 load.  For each 4-group K chunk the loaders place, in one of two
+// LDS buffers, the chunk's weight codes (regrouped so that a compute lane's operand
+// words are one 8-byte read), its group scales and its activation tile; the compute
+// waves work on the other buffer.  Compute wave w takes the outputs of column set w.
+// The loaders keep the next three chunks in flight in a ring of register sets, across
+// work-item boundaries (under full load a chunk's loads take about two chunk times to
+// return); one barrier per chunk.
+constexpr int kColSets = 4;
+constexpr int kCompWaves = kColSets;
+constexpr int kLoadWaves = 4;
+constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);
+constexpr int kLoadThreads = kWave * kLoadWaves;                // 256: one per weight row of a chunk
+constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
+constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
+constexpr int kBufAct = kTileBytes;                            // [16 rows][1040 B]
+constexpr int kBufNs = kMfmaItemRows * 4 * 4;                  // [16 rows][4 groups] fp32
+constexpr int kBufBytes = kBufCodes + kBufScales + kBufAct + kBufNs;
+constexpr int kMaxWorkPerWg = 64;
+
+struct WorkDesc {
+    int e;      // expert, -1: shared
+    int nb0;    // first output of the block
+    int nch;    // K chunks (0: the block lies past this unit's outputs)
+    int R;      // rows
+    int row0;   // first row: union row (routed) or token (shared)
+    int srow[kMfmaItemRows];  // activation source row of each row (rows past R repeat R-1)
+};
+
+
+// the weight row (output) and matrix of loader row r (0..255) of a chunk
 template <bool GU>
-__global__ __launch_bounds__(256, 2) void q4_mfma_kernel(MfmaArgs a) {
-    // activation chunks, double-buffered: [row][1 KB + 16] and [row][4 groups]
-    __shared__ __attribute__((aligned(16))) uint8_t at0[kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t at1[kTileBytes];
-    __shared__ __attribute__((aligned(16))) float ns0[kMfmaItemRows * 4];  // -136*sum(x)
-    __shared__ __attribute__((aligned(16))) float ns1[kMfmaItemRows * 4];
-    __shared__ __attribute__((aligned(16))) uint8_t cbuf[4][kCodeBytes];  // per wave
+__device__ __forceinline__ int load_row_output(int r, int nb0, bool &second) {
+    const int wv = r / 64, lr = r % 64, bb = lr / 16, jj = lr % 16;
+    second = GU && bb >= 2;
+    return GU ? nb0 + 32 * wv + (bb % 2) * 16 + jj : nb0 + 64 * wv + 16 * bb + jj;
+}
 
-    // ---- the item: rows [row0, row0 + R) of a routed expert e, or of the shared expert (e < 0)
-    const int item = blockIdx.y;
-    int e, row0, R;
-    if (item < a.max_items) {
-        if (!a.with_routed || item >= a.n_items[0]) return;
-        e = a.items[4 * item];
-        row0 = a.items[4 * item + 1];
-        R = a.items[4 * item + 2];
-    } else {
-        if (!a.with_shared) return;
-        e = -1;
-        row0 = (item - a.max_items) * kMfmaItemRows;
-        R = min(kMfmaItemRows, a.T - row0);
-        if (R <= 0) return;
-    }
-    const int H = a.H;
-    const int Fu = e >= 0 ? a.F : a.Fs;
-    const int K = GU ? H : Fu;
-    const int N = GU ? Fu : H;
-    const int NG = K / 64;
-    const int NGp = mfma_groups_padded(K);
-    constexpr int kWaveOut = GU ? 32 : 64;
-    const int nb0 = blockIdx.x * (4 * kWaveOut);
-    if (nb0 >= N) return;
+struct ChunkRegs {
+    u32x4_t q[8];
+    float s[4];
+    uint4 a[4];
+    uint4 n;
+};
 
-    moe_q4 m0, m1;
-    const int32_t *rt = nullptr;  // token of each row (routed gate/up), else rows are contiguous
-    const uint8_t *afrag;
-    const float *ansx;
-    float *out;
-    if (e >= 0) {
-        if (GU) {
-            const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
-            m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
-            m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
-            rt = a.row_tok + row0;
-            afrag = a.x_frag;
-            ansx = a.x_nsx;
-            out = a.h_routed + (size_t)row0 * N;
-        } else {
-            const size_t dq = (size_t)e * H * (Fu / 2), ds = (size_t)e * H * (Fu / 64);
-            m0.q = a.down.q + dq; m0.s = a.down.s + ds;
-            m1 = m0;
-            afrag = a.hr_frag + (size_t)row0 * NGp * kGroupBytes;
-            ansx = a.hr_nsx + (size_t)row0 * NGp;
-            out = a.y_routed + (size_t)row0 * N;
-        }
-    } else {
-        if (GU) {
-            m0 = a.sh_gate; m1 = a.sh_up;
-            afrag = a.x_frag + (size_t)row0 * NGp * kGroupBytes;
-            ansx = a.x_nsx + (size_t)row0 * NGp;
-            out = a.h_shared + (size_t)row0 * N;
-        } else {
-            m0 = a.sh_down; m1 = m0;
-            afrag = a.hs_frag + (size_t)row0 * NGp * kGroupBytes;
-            ansx = a.hs_nsx + (size_t)row0 * NGp;
-            out = a.y_shared + (size_t)row0 * N;
-        }
-    }
-
+template <bool GU>
+__global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    WorkDesc *work = reinterpret_cast<WorkDesc *>(lds + 2 * kBufBytes);
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int j = lane % 16, p = lane / 16;
-    const int nchunks = (NG + kCG - 1) / kCG;
+    constexpr int kBlk = GU ? 128 : 256;  // outputs per work item
 
-    // ---- B blocks: GU -> (gate, cols 0-15), (gate, 16-31), (up, 0-15), (up, 16-31) of the
-    // wave's 32 outputs; down -> 4 x 16 of its 64 outputs.  A lane's column, clamped for
-    // loads (never stored past N).
-    int ncol[4];
-    uint32_t soff[4];
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-        const int cb = GU ? b % 2 : b;
-        ncol[b] = nb0 + wv * kWaveOut + cb * 16 + j;
-        soff[b] = (uint32_t)min(ncol[b], N - 1) * (uint32_t)NG;
-    }
-    // code loads are coalesced: for a block of 16 rows, load i (0, 1) gives lane l row
-    // 8i + l/8 and bytes 16 (l % 8) of the row's 128-byte chunk (4 groups); rows past N
-    // re-read row N-1 (never stored)
-    constexpr int kColBlocks = GU ? 2 : 4;
-    uint32_t qrow[kColBlocks][2];
-#pragma unroll
-    for (int cb = 0; cb < kColBlocks; cb++)
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int n = min(nb0 + wv * kWaveOut + cb * 16 + 8 * i + lane / 8, N - 1);
-            qrow[cb][i] = (uint32_t)n * (uint32_t)(K / 2);
+    // ---- this workgroup's work items, described in LDS
+    const int n_routed = a.with_routed ? a.n_items[0] : 0;
+    const int n_sh = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
+    const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
+    const int nb = (nmax + kBlk - 1) / kBlk;
+    const int total = (n_routed + n_sh) * nb;
+    const int G = gridDim.x, g = blockIdx.x;
+    const int nwi = g < total ? min((total - g + G - 1) / G, kMaxWorkPerWg) : 0;
+    for (int idx = tid; idx < nwi * kMfmaItemRows; idx += kMfmaThreads) {
+        const int k = idx / kMfmaItemRows, r = idx % kMfmaItemRows;
+        const int wi = g + k * G, y = wi / nb, b = wi % nb;
+        int e, row0, R;
+        if (y < n_routed) {
+            e = a.items[4 * y];
+            row0 = a.items[4 * y + 1];
+            R = a.items[4 * y + 2];
+        } else {
+            e = -1;
+            row0 = (y - n_routed) * kMfmaItemRows;
+            R = min(kMfmaItemRows, a.T - row0);
         }
-    const uint32_t qlast = (uint32_t)(K / 2 - 16);  // last 16-byte piece of a row
-    auto qbase = [&](int b) { return (GU && b >= 2) ? m1.q : m0.q; };
-    auto sbase = [&](int b) { return (GU && b >= 2) ? m1.s : m0.s; };
-
-    // ---- activation staging: wave wv moves rows wv + 4i (16 bytes per lane of each
-    // row's 1-KB chunk), lanes 0-15 the group sums of rows 0-15.  Rows past R repeat
-    // row R-1 (cached, finite; their outputs are never stored), so staging has no branches.
-    constexpr int kRowsPerWave = kMfmaItemRows / 4;
-    int srow[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; i++) {
-        const int r = min(wv + 4 * i, R - 1);
-        srow[i] = rt ? rt[r] : r;
-    }
-    const int lr = min(lane % kMfmaItemRows, R - 1);
-    const int nsrow = rt ? rt[lr] : lr;
-    struct Staged {
-        uint4 a[kRowsPerWave];
-        uint4 n;
-    };
-    // values are returned, not kept in a captured array, so they stay in registers
-    auto stage_load = [&](int c) __attribute__((always_inline)) {
-        const int g0 = c * kCG;
-        Staged v;
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; i++)
-            v.a[i] = *reinterpret_cast<const uint4 *>(
-                afrag + ((size_t)srow[i] * NGp + g0) * kGroupBytes + 16 * lane);
-        v.n = *reinterpret_cast<const uint4 *>(ansx + (size_t)nsrow * NGp + g0);
-        return v;
-    };
-    auto stage_store = [&](const Staged &v, uint8_t *tile, float *nst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; i++)
-            *reinterpret_cast<uint4 *>(tile + (wv + 4 * i) * kRowPitch + 16 * lane) = v.a[i];
-        if (wv == 0 && lane < kMfmaItemRows) *reinterpret_cast<uint4 *>(nst + 4 * lane) = v.n;
-    };
-
-    u32x4_t cq[3][4][2];
-    float cs[3][4];
-    auto fetch = [&](int c, u32x4_t (&q)[4][2], float (&s)[4]) __attribute__((always_inline)) {
-        const int g0 = min(c, nchunks - 1) * kCG;  // past the end: re-fetch the last chunk
-        // past the row's end (a last chunk of fewer than 4 groups): re-read its last piece
-        const uint32_t off = min((uint32_t)(32 * g0 + 16 * (lane % 8)), qlast);
-#pragma unroll
-        for (int b = 0; b < 4; b++)
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                q[b][i] = *reinterpret_cast<const u32x4_t *>(qbase(b) + (qrow[GU ? b % 2 : b][i] + off));
-        // lane (j, p) fetches its column's scale of group g0 + p
-#pragma unroll
-        for (int b = 0; b < 4; b++) s[b] = sbase(b)[soff[b] + (uint32_t)min(g0 + p, NG - 1)];
-    };
-
-    f32x4_t acc[4];
-#pragma unroll
-    for (int b = 0; b < 4; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint8_t *cw = cbuf[wv];
-    auto compute = [&](int c, const uint8_t *tile, const float *nst, const u32x4_t (&q)[4][2],
-                       const float (&s)[4]) __attribute__((always_inline)) {
-        const int ng = min(kCG, NG - c * kCG);
-        // regroup the chunk's codes: row-major into this wave's LDS area, then each lane
-        // reads its column's words 2p, 2p+1 of every group
-#pragma unroll
-        for (int b = 0; b < 4; b++)
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                *reinterpret_cast<u32x4_t *>(cw + (16 * b + 8 * i + lane / 8) * kCodePitch + 16 * (lane % 8)) = q[b][i];
-#pragma unroll
-        for (int gi = 0; gi < kCG; gi++) {
-            if (gi >= ng) break;
-            // the column's group scale sits in lane j + 16 gi
-            float sg[4];
-#pragma unroll
-            for (int b = 0; b < 4; b++) sg[b] = __shfl(s[b], j + 16 * gi, kWave);
-            // group accumulators start at -136 * sum(x) of rows 4p .. 4p+3
-            f32x4_t ga;
-#pragma unroll
-            for (int v = 0; v < 4; v++) ga[v] = nst[(4 * p + v) * 4 + gi];
-            f32x4_t g[4];
-#pragma unroll
-            for (int b = 0; b < 4; b++) g[b] = ga;
-            uint2 w[4];
-#pragma unroll
-            for (int b = 0; b < 4; b++)
-                w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
-                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(ar);
-                const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(ar + 128);
-                bf16x8_t bo[4];
-#pragma unroll
-                for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? w[b].y : w[b].x);
-#pragma unroll
-                for (int b = 0; b < 4; b++) g[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[b], g[b], 0, 0, 0);
-#pragma unroll
-                for (int b = 0; b < 4; b++) g[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[b], g[b], 0, 0, 0);
-            }
-#pragma unroll
-            for (int b = 0; b < 4; b++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) acc[b][v] = fmaf(sg[b], g[b][v], acc[b][v]);
+        const int N = GU ? (e >= 0 ? a.F : a.Fs) : a.H;
+        const int K = GU ? a.H : (e >= 0 ? a.F : a.Fs);
+        const int rr = min(r, R - 1);
+        work[k].srow[r] = (GU && e >= 0) ? a.row_tok[row0 + rr] : row0 + rr;
+        if (r == 0) {
+            work[k].e = e;
+            work[k].nb0 = b * kBlk;
+            work[k].nch = b * kBlk < N ? (K / 64 + kCG - 1) / kCG : 0;
+            work[k].R = R;
+            work[k].row0 = row0;
         }
-    };
-
-    // One chunk step.  Loads are issued so that no wait covers data needed later:
-    // the activations of chunk c+2 (before the codes of c+2, so writing them to LDS two
-    // steps later never waits for codes that are still ahead of use), then the codes
-    // of c+2 into the slot just freed.  The activations of c+1, loaded a step ago, go to
-    // the other LDS buffer after the compute.  Staging register sets alternate.
-    Staged stg0, stg1;
-    auto step = [&](int c, int slot, Staged &ld, const Staged &st) __attribute__((always_inline)) {
-        const bool odd = c & 1;
-        lds_barrier();
-        ld = stage_load(min(c + 2, nchunks - 1));  // past the end: re-load the last chunk (not stored)
-        fetch(c + 2, cq[(slot + 2) % 3], cs[(slot + 2) % 3]);
-        compute(c, odd ? at1 : at0, odd ? ns1 : ns0, cq[slot], cs[slot]);
-        if (c + 1 < nchunks) stage_store(st, odd ? at0 : at1, odd ? ns0 : ns1);
-    };
-
-    {
-        const Staged first = stage_load(0);
-        fetch(0, cq[0], cs[0]);
-        stg1 = stage_load(min(1, nchunks - 1));
-        fetch(1, cq[1], cs[1]);
-        stage_store(first, at0, ns0);
     }
-    // whole turns of both rings (codes: 3 slots, staging: 2 sets) without branches
-    // inside, then the rest
-    int c = 0;
-    for (; c + 6 <= nchunks; c += 6) {
-        step(c, 0, stg0, stg1);
-        step(c + 1, 1, stg1, stg0);
-        step(c + 2, 2, stg0, stg1);
-        step(c + 3, 0, stg1, stg0);
-        step(c + 4, 1, stg0, stg1);
-        step(c + 5, 2, stg1, stg0);
-    }
-    if (c < nchunks) step(c, 0, stg0, stg1);
-    if (c + 1 < nchunks) step(c + 1, 1, stg1, stg0);
-    if (c + 2 < nchunks) step(c + 2, 2, stg0, stg1);
-    if (c + 3 < nchunks) step(c + 3, 0, stg1, stg0);
-    if (c + 4 < nchunks) step(c + 4, 1, stg0, stg1);
+    __syncthreads();
+    int S = 0;  // chunks of all the work items, in order
+    for (int k = 0; k < nwi; k++) S += work[k].nch;
 
-    // ---- epilogue.  D layout: register v of lane (j, p) is row 4p + v, column j of the block
-#pragma unroll
-    for (int b = 0; b < (GU ? 2 : 4); b++) {
-        const int n = ncol[b];
-        if (n >= N) continue;
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int r = 4 * p + v;
-            if (r >= R) continue;
-            float val;
+    if (wv >= kCompWaves) {
+        // ================= loader waves
+        const int t = tid - kCompWaves * kWave;  // 0..255
+        int lk = 0, lc = 0;                      // the next chunk to load: (work item, chunk)
+        while (lk < nwi && work[lk].nch == 0) lk++;
+        auto load = [&](ChunkRegs &v) __attribute__((always_inline)) {
+            const int k = lk, c = lc;  // always a chunk that exists
+            const WorkDesc &d = work[k];
+            const int e = d.e;
+            moe_q4 m0, m1;
+            const uint8_t *afrag;
+            const float *ansx;
+            int K, N;
             if (GU) {
-                const float gg = acc[b][v], uu = acc[b + 2][v];
-                val = gg / (1.0f + expf(-gg)) * uu;
+                K = a.H;
+                N = e >= 0 ? a.F : a.Fs;
+                if (e >= 0) {
+                    const size_t gq = (size_t)e * a.F * (a.H / 2), gs = (size_t)e * a.F * (a.H / 64);
+                    m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
+                    m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
+                } else {
+                    m0 = a.sh_gate;
+                    m1 = a.sh_up;
+                }
+                afrag = a.x_frag;
+                ansx = a.x_nsx;
             } else {
-                val = acc[b][v];
+                K = e >= 0 ? a.F : a.Fs;
+                N = a.H;
+                if (e >= 0) {
+                    const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
+                    m0.q = a.down.q + dq; m0.s = a.down.s + ds;
+                    afrag = a.hr_frag;
+                    ansx = a.hr_nsx;
+                } else {
+                    m0 = a.sh_down;
+                    afrag = a.hs_frag;
+                    ansx = a.hs_nsx;
+                }
+                m1 = m0;
             }
-            out[(size_t)r * N + n] = val;
+            const int NG = K / 64, NGp = mfma_groups_padded(K);
+            const uint32_t qlast = (uint32_t)(K / 2 - 16);
+            const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                bool second;
+                const int n = min(load_row_output<GU>(t / 8 + 32 * i, d.nb0, second), N - 1);
+                v.q[i] = *reinterpret_cast<const u32x4_t *>((second ? m1.q : m0.q) + (size_t)n * (K / 2) + off);
+            }
+            // scales: lane t takes group t % 4 of columns t / 4 + 64 i, so four adjacent
+            // lanes read one column's four consecutive group scales
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                bool second;
+                const int n = min(load_row_output<GU>(t / 4 + 64 * i, d.nb0, second), N - 1);
+                v.s[i] = (second ? m1.s : m0.s)[(size_t)n * NG + min(kCG * c + t % 4, NG - 1)];
+            }
+            const int ar = t / 16;
+            const uint8_t *arow = afrag + ((size_t)d.srow[ar] * NGp + kCG * c) * kGroupBytes;
+#pragma unroll
+            for (int i = 0; i < 4; i++) v.a[i] = *reinterpret_cast<const uint4 *>(arow + 16 * (t % 16 + 16 * i));
+            const int nr = t % kMfmaItemRows;  // (only lanes t < 16 store it)
+            v.n = *reinterpret_cast<const uint4 *>(ansx + (size_t)d.srow[nr] * NGp + kCG * c);
+            // advance; past the last chunk the head stays there (that chunk is loaded again)
+            int nk = lk, nc = lc + 1;
+            if (nc >= work[nk].nch) {
+                nc = 0;
+                nk++;
+                while (nk < nwi && work[nk].nch == 0) nk++;
+            }
+            if (nk < nwi) {
+                lk = nk;
+                lc = nc;
+            }
+            (void)N;
+        };
+        auto store = [&](const ChunkRegs &v, int buf) __attribute__((always_inline)) {
+            uint8_t *B = lds + (size_t)buf * kBufBytes;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int r = t / 8 + 32 * i;
+                *reinterpret_cast<u32x4_t *>(B + (r / 64) * 64 * kCodePitch + (r % 64) * kCodePitch + 16 * (t % 8)) = v.q[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * (t / 4 + 64 * i) + t % 4] = v.s[i];
+            const int ar = t / 16;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * i)) = v.a[i];
+            if (t < kMfmaItemRows) *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + kBufAct + 16 * t) = v.n;
+        };
+        ChunkRegs r0, r1, r2;
+        if (S > 0) {
+            load(r0);
+            load(r1);
+            load(r2);
+            store(r0, 0);
+        }
+        lds_barrier();
+        // chunk m sits in register set m % 3 and LDS buffer m % 2; at step s the set of
+        // chunk s (already stored) takes chunk s + 3, and chunk s + 1 is stored
+        int s = 0;
+        for (; s + 6 <= S; s += 6) {
+            load(r0); store(r1, 1); lds_barrier();
+            load(r1); store(r2, 0); lds_barrier();
+            load(r2); store(r0, 1); lds_barrier();
+            load(r0); store(r1, 0); lds_barrier();
+            load(r1); store(r2, 1); lds_barrier();
+            load(r2); store(r0, 0); lds_barrier();
+        }
+        if (s < S) { load(r0); store(r1, 1); lds_barrier(); }
+        if (s + 1 < S) { load(r1); store(r2, 0); lds_barrier(); }
+        if (s + 2 < S) { load(r2); store(r0, 1); lds_barrier(); }
+        if (s + 3 < S) { load(r0); store(r1, 0); lds_barrier(); }
+        if (s + 4 < S) { load(r1); store(r2, 1); lds_barrier(); }
+    } else {
+        // ================= compute waves
+        const int j = lane % 16, p = lane / 16;
+        const int cs = wv;
+        f32x4_t acc[4];
+        int ck = 0, cc = 0;  // the chunk being computed
+        while (ck < nwi && work[ck].nch == 0) ck++;
+        // outputs of work item k
+        auto epilogue = [&](int k) __attribute__((always_inline)) {
+            const WorkDesc &d = work[k];
+            const int e = d.e, R = d.R, row0 = d.row0;
+            const int N = GU ? (e >= 0 ? a.F : a.Fs) : a.H;
+            float *out = GU ? (e >= 0 ? a.h_routed : a.h_shared) : (e >= 0 ? a.y_routed : a.y_shared);
+            out += (size_t)row0 * N;
+            const f32x4_t *tot = acc;
+            // D layout: register v of lane (j, p) is row 4p + v, column j
+#pragma unroll
+            for (int b = 0; b < (GU ? 2 : 4); b++) {
+                const int n = GU ? d.nb0 + 32 * cs + b * 16 + j : d.nb0 + 64 * cs + 16 * b + j;
+                if (n >= N) continue;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const int r = 4 * p + v;
+                    if (r >= R) continue;
+                    float val;
+                    if (GU) {
+                        const float gg = tot[b][v], uu = tot[b + 2][v];
+                        val = gg / (1.0f + expf(-gg)) * uu;
+                    } else {
+                        val = tot[b][v];
+                    }
+                    out[(size_t)r * N + n] = val;
+                }
+            }
+        };
+        lds_barrier();
+        for (int s = 0; s < S; s++) {
+            const uint8_t *B = lds + (size_t)(s & 1) * kBufBytes;
+            const WorkDesc &d = work[ck];
+            const int K = GU ? a.H : (d.e >= 0 ? a.F : a.Fs);
+            const int NG = K / 64;
+            const int ng = min(kCG, NG - kCG * cc);
+            if (cc == 0) {
+#pragma unroll
+                for (int b = 0; b < 4; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            const uint8_t *cw = B + cs * 64 * kCodePitch;
+            const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
+            const uint8_t *tile = B + kBufCodes + kBufScales;
+            const float *nst = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
+            f32x4_t sc4[4], ns4[4];
+#pragma unroll
+            for (int b = 0; b < 4; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
+#pragma unroll
+            for (int v = 0; v < 4; v++) ns4[v] = *reinterpret_cast<const f32x4_t *>(nst + 4 * (4 * p + v));
+#pragma unroll
+            for (int gi = 0; gi < kCG; gi++) {
+                if (gi >= ng) break;
+                f32x4_t gacc[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++) gacc[b][v] = ns4[v][gi];
+                uint2 w[4];
+#pragma unroll
+                for (int b = 0; b < 4; b++)
+                    w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) {
+                    const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
+                    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(ar);
+                    const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(ar + 128);
+                    bf16x8_t bo[4];
+#pragma unroll
+                    for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? w[b].y : w[b].x);
+#pragma unroll
+                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[b], gacc[b], 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[b], gacc[b], 0, 0, 0);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; b++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++) acc[b][v] = fmaf(sc4[b][gi], gacc[b][v], acc[b][v]);
+            }
+            if (++cc >= d.nch) {
+                epilogue(ck);
+                cc = 0;
+                ck++;
+                while (ck < nwi && work[ck].nch == 0) ck++;
+            }
+            lds_barrier();
         }
     }
+}
+
+static int mfma_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+        (void)hipGetLastError();
+    }
+    return cus;
+}
+
+template <bool GU>
+static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
+    const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
+    const int nb = (nmax + (GU ? 127 : 255)) / (GU ? 128 : 256);
+    const long total_max = (long)((a.with_routed ? a.max_items : 0) + shared_items) * nb;
+    if (total_max == 0) return hipSuccess;
+    // one workgroup per CU, more if a workgroup's table would overflow
+    long G = mfma_cus();
+    if ((total_max + G - 1) / G > kMaxWorkPerWg) G = (total_max + kMaxWorkPerWg - 1) / kMaxWorkPerWg;
+    const size_t lds = 2 * (size_t)kBufBytes + kMaxWorkPerWg * sizeof(WorkDesc);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipGetLastError();
+    ProfScope prof(name, st);
+    q4_mfma_kernel<GU><<<(int)G, kMfmaThreads, lds, st>>>(a);
+    return hipGetLastError();
 }
 
 // x prepared once with the work list; gate/up for every item; the routed and shared
@@ -482,13 +552,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_nsx), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
-    const int nmax = a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F;
-    {
-        dim3 grid((nmax + 127) / 128, a.max_items + shared_items);
-        ProfScope prof("ffn_gateup_mfma", st);
-        q4_mfma_kernel<true><<<grid, 256, 0, st>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
     // h rows in fragment order: the routed rows (as many as the largest union can
     // have) and the shared rows
     ItemsJob no_items = it;
@@ -497,12 +561,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
                     a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx) : none,
                     no_items, "prep_h", st);
     if (e != hipSuccess) return e;
-    {
-        dim3 grid((a.H + 255) / 256, a.max_items + shared_items);
-        ProfScope prof("ffn_down_mfma", st);
-        q4_mfma_kernel<false><<<grid, 256, 0, st>>>(a);
-        return hipGetLastError();
-    }
+    return launch_gemm<false>(a, shared_items, "ffn_down_mfma", st);
 }
 
 }  // namespace moe
