@@ -298,65 +298,86 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         const int t = tid - kCompWaves * kWave;  // 0..255
         int lk = 0, lc = 0;                      // the next chunk to load: (work item, chunk)
         while (lk < nwi && work[lk].nch == 0) lk++;
-        auto load = [&](ChunkRegs &v) __attribute__((always_inline)) {
-            const int k = lk, c = lc;  // always a chunk that exists
+        // this lane's row offsets in the current work item (set when the item changes),
+        // from wave-uniform matrix bases.  Code row t/8 + 32i is a gate row for even i and
+        // an up row for odd i (gate/up), whatever the lane; so is scale column sc_col(i).
+        int pk = -1;
+        const uint8_t *qb0 = nullptr, *qb1 = nullptr, *abase = nullptr;
+        const float *sb0 = nullptr, *sb1 = nullptr, *nbase = nullptr;
+        uint32_t qo[8], so[4], no = 0;
+        const uint8_t *arow = nullptr;  // 64-bit: union rows x fragment bytes can pass 2^32
+        uint32_t qlast = 0;
+        int NG = 1;
+        auto sc_col = [&](int i) __attribute__((always_inline)) {
+            const int q = t / 4;
+            return (q % 32) + 32 * (i & 1) + 64 * ((q / 32) + 2 * (i >> 1));
+        };
+        auto rows_of = [&](int k) __attribute__((always_inline)) {
             const WorkDesc &d = work[k];
-            const int e = d.e;
-            moe_q4 m0, m1;
-            const uint8_t *afrag;
-            const float *ansx;
+            const int e = __builtin_amdgcn_readfirstlane(d.e);
+            const int nb0 = __builtin_amdgcn_readfirstlane(d.nb0);
             int K, N;
             if (GU) {
                 K = a.H;
                 N = e >= 0 ? a.F : a.Fs;
                 if (e >= 0) {
                     const size_t gq = (size_t)e * a.F * (a.H / 2), gs = (size_t)e * a.F * (a.H / 64);
-                    m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
-                    m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
+                    qb0 = a.gate.q + gq; sb0 = a.gate.s + gs;
+                    qb1 = a.up.q + gq;   sb1 = a.up.s + gs;
                 } else {
-                    m0 = a.sh_gate;
-                    m1 = a.sh_up;
+                    qb0 = a.sh_gate.q; sb0 = a.sh_gate.s;
+                    qb1 = a.sh_up.q;   sb1 = a.sh_up.s;
                 }
-                afrag = a.x_frag;
-                ansx = a.x_nsx;
+                abase = a.x_frag;
+                nbase = a.x_nsx;
             } else {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
                 if (e >= 0) {
                     const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
-                    m0.q = a.down.q + dq; m0.s = a.down.s + ds;
-                    afrag = a.hr_frag;
-                    ansx = a.hr_nsx;
+                    qb0 = a.down.q + dq; sb0 = a.down.s + ds;
+                    abase = a.hr_frag;
+                    nbase = a.hr_nsx;
                 } else {
-                    m0 = a.sh_down;
-                    afrag = a.hs_frag;
-                    ansx = a.hs_nsx;
+                    qb0 = a.sh_down.q; sb0 = a.sh_down.s;
+                    abase = a.hs_frag;
+                    nbase = a.hs_nsx;
                 }
-                m1 = m0;
+                qb1 = qb0;
+                sb1 = sb0;
             }
-            const int NG = K / 64, NGp = mfma_groups_padded(K);
-            const uint32_t qlast = (uint32_t)(K / 2 - 16);
-            const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
+            NG = K / 64;
+            const int NGp = mfma_groups_padded(K);
+            qlast = (uint32_t)(K / 2 - 16);
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 bool second;
-                const int n = min(load_row_output<GU>(t / 8 + 32 * i, d.nb0, second), N - 1);
-                v.q[i] = *reinterpret_cast<const u32x4_t *>((second ? m1.q : m0.q) + (size_t)n * (K / 2) + off);
+                const int n = min(load_row_output<GU>(t / 8 + 32 * i, nb0, second), N - 1);
+                qo[i] = (uint32_t)n * (uint32_t)(K / 2);
             }
-            // scales: lane t takes group t % 4 of columns t / 4 + 64 i, so four adjacent
-            // lanes read one column's four consecutive group scales
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 bool second;
-                const int n = min(load_row_output<GU>(t / 4 + 64 * i, d.nb0, second), N - 1);
-                v.s[i] = (second ? m1.s : m0.s)[(size_t)n * NG + min(kCG * c + t % 4, NG - 1)];
+                const int n = min(load_row_output<GU>(sc_col(i), nb0, second), N - 1);
+                so[i] = (uint32_t)n * (uint32_t)NG;
             }
-            const int ar = t / 16;
-            const uint8_t *arow = afrag + ((size_t)d.srow[ar] * NGp + kCG * c) * kGroupBytes;
+            arow = abase + (size_t)d.srow[t / 16] * NGp * kGroupBytes + 16 * (t % 16);
+            no = (uint32_t)d.srow[t % kMfmaItemRows] * (uint32_t)NGp;  // (only lanes t < 16 store it)
+            pk = k;
+        };
+        auto load = [&](ChunkRegs &v) __attribute__((always_inline)) {
+            const int k = lk, c = lc;  // always a chunk that exists
+            if (k != pk) rows_of(k);
+            const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
 #pragma unroll
-            for (int i = 0; i < 4; i++) v.a[i] = *reinterpret_cast<const uint4 *>(arow + 16 * (t % 16 + 16 * i));
-            const int nr = t % kMfmaItemRows;  // (only lanes t < 16 store it)
-            v.n = *reinterpret_cast<const uint4 *>(ansx + (size_t)d.srow[nr] * NGp + kCG * c);
+            for (int i = 0; i < 8; i++) v.q[i] = *reinterpret_cast<const u32x4_t *>(((i & 1) ? qb1 : qb0) + (qo[i] + off));
+            const uint32_t sg = (uint32_t)min(kCG * c + t % 4, NG - 1);
+#pragma unroll
+            for (int i = 0; i < 4; i++) v.s[i] = ((i & 1) ? sb1 : sb0)[so[i] + sg];
+            const uint8_t *ac = arow + (uint32_t)(kCG * c * kGroupBytes);
+#pragma unroll
+            for (int i = 0; i < 4; i++) v.a[i] = *reinterpret_cast<const uint4 *>(ac + 256 * i);
+            v.n = *reinterpret_cast<const uint4 *>(nbase + (no + kCG * c));
             // advance; past the last chunk the head stays there (that chunk is loaded again)
             int nk = lk, nc = lc + 1;
             if (nc >= work[nk].nch) {
@@ -368,7 +389,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 lk = nk;
                 lc = nc;
             }
-            (void)N;
         };
         auto store = [&](const ChunkRegs &v, int buf) __attribute__((always_inline)) {
             uint8_t *B = lds + (size_t)buf * kBufBytes;
@@ -378,7 +398,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 *reinterpret_cast<u32x4_t *>(B + (r / 64) * 64 * kCodePitch + (r % 64) * kCodePitch + 16 * (t % 8)) = v.q[i];
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * (t / 4 + 64 * i) + t % 4] = v.s[i];
+            for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * sc_col(i) + t % 4] = v.s[i];
             const int ar = t / 16;
 #pragma unroll
             for (int i = 0; i < 4; i++)
