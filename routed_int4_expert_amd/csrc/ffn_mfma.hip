@@ -218,7 +218,7 @@ constexpr int kLoadThreads = kWave * kLoadWaves;                // 256: one per 
 constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
 constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
 constexpr int kBufAct = kTileBytes;                            // [16 rows][1040 B]
-constexpr int kBufNs = kMfmaItemRows * 4 * 4;                  // [16 rows][4 groups] fp32
+constexpr int kBufNs = kMfmaItemRows * 4 * 4;                  // [4 groups][16 rows] fp32
 constexpr int kBufBytes = kBufCodes + kBufScales + kBufAct + kBufNs;
 constexpr int kMaxWorkPerWg = 64;
 
@@ -403,7 +403,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * i)) = v.a[i];
-            if (t < kMfmaItemRows) *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + kBufAct + 16 * t) = v.n;
+            if (t < kMfmaItemRows) {  // transposed, [group][row]: a lane's four rows of a group are one read
+                float *nsb = reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct);
+                nsb[0 * kMfmaItemRows + t] = __uint_as_float(v.n.x);
+                nsb[1 * kMfmaItemRows + t] = __uint_as_float(v.n.y);
+                nsb[2 * kMfmaItemRows + t] = __uint_as_float(v.n.z);
+                nsb[3 * kMfmaItemRows + t] = __uint_as_float(v.n.w);
+            }
         };
         ChunkRegs r0, r1, r2;
         if (S > 0) {
@@ -479,19 +485,23 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
             const uint8_t *tile = B + kBufCodes + kBufScales;
             const float *nst = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
-            f32x4_t sc4[4], ns4[4];
+            // the chunk's group scales of this lane's four columns and the -136 sum(x) start
+            // values of its rows (one 16-byte read per group); then the groups, with the
+            // next group's code words and A fragments read before this group's products
+            f32x4_t sc4[4], ga4[kCG];
 #pragma unroll
             for (int b = 0; b < 4; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
 #pragma unroll
-            for (int v = 0; v < 4; v++) ns4[v] = *reinterpret_cast<const f32x4_t *>(nst + 4 * (4 * p + v));
-#pragma unroll
-            for (int gi = 0; gi < kCG; gi++) {
-                if (gi >= ng) break;
-                f32x4_t gacc[4];
-#pragma unroll
-                for (int b = 0; b < 4; b++)
-#pragma unroll
-                    for (int v = 0; v < 4; v++) gacc[b][v] = ns4[v][gi];
+            for (int gi = 0; gi < kCG; gi++) ga4[gi] = *reinterpret_cast<const f32x4_t *>(nst + gi * kMfmaItemRows + 4 * p);
+            // Per group: issue its 16 MFMAs, then (while they run) read and convert the next
+            // group's operands, then scale-accumulate this group's results.  Scheduling
+            // barriers keep that order, so the conversion overlaps the matrix pipe.
+            struct Opnd {
+                bf16x8_t bo[2][4];  // [ks][block] code pairs
+                bf16x8_t a[2][2];   // [ks][hi, lo]
+            };
+            auto read_group = [&](int gi) __attribute__((always_inline)) {
+                Opnd o;
                 uint2 w[4];
 #pragma unroll
                 for (int b = 0; b < 4; b++)
@@ -499,20 +509,37 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) {
                     const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
-                    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(ar);
-                    const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(ar + 128);
-                    bf16x8_t bo[4];
-#pragma unroll
-                    for (int b = 0; b < 4; b++) bo[b] = code_pairs(ks ? w[b].y : w[b].x);
-#pragma unroll
-                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[b], gacc[b], 0, 0, 0);
-#pragma unroll
-                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[b], gacc[b], 0, 0, 0);
+                    o.a[ks][0] = *reinterpret_cast<const bf16x8_t *>(ar);
+                    o.a[ks][1] = *reinterpret_cast<const bf16x8_t *>(ar + 128);
                 }
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                    for (int b = 0; b < 4; b++) o.bo[ks][b] = code_pairs(ks ? w[b].y : w[b].x);
+                return o;
+            };
+            Opnd cur = read_group(0);
+#pragma unroll
+            for (int gi = 0; gi < kCG; gi++) {
+                if (gi >= ng) break;
+                f32x4_t gacc[4];
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+                    for (int b = 0; b < 4; b++)
+                        gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[ks][0], cur.bo[ks][b], ks ? gacc[b] : ga4[gi], 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[ks][1], cur.bo[ks][b], gacc[b], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                Opnd nxt;
+                if (gi + 1 < kCG) nxt = read_group(min(gi + 1, ng - 1));
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int b = 0; b < 4; b++)
 #pragma unroll
                     for (int v = 0; v < 4; v++) acc[b][v] = fmaf(sc4[b][gi], gacc[b][v], acc[b][v]);
+                if (gi + 1 < kCG) cur = nxt;
             }
             if (++cc >= d.nch) {
                 epilogue(ck);
