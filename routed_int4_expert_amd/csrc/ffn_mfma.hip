@@ -17,17 +17,18 @@
 //    starts at -136 * sum(x) (the unsigned-offset identity of §2.2, K1) and its
 //    result is scaled by the fp32 group scale into the fp32 running sum.
 //
-// Work item = up to 16 rows of one expert (one 16-row MFMA block) x a block
-// of outputs: 4 waves x 32 outputs (gate and up for the same columns) or
-// 4 waves x 64 outputs (down).  Experts with more rows, and the shared expert,
-// span several items.  K advances in chunks of 4 groups.  The weight stream is
-// kept in flight by a ring of three register slots (the chunk being computed
-// and the next two).  Activation chunks are loaded into registers two steps
-// ahead and written to the other of two LDS buffers after each compute; the
-// barrier between steps waits only for those LDS writes, and loads are issued
-// in an order where no wait for one covers data needed later (completions are
-// counted in issue order), so the weight loads stay in flight across steps.  Every output has one owner:
-// the result is deterministic.
+// Work item = up to 16 rows of one expert (one 16-row MFMA block) x a block of
+// outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
+// outputs (down).  Experts with more rows, and the shared expert, span several
+// items.  The kernel is persistent (one workgroup of 8 waves per CU, looping over
+// (item, output block) pairs) and splits loading from computing: 4 loader waves keep
+// three 4-group K chunks in flight in registers and place each one in one of two LDS
+// buffers (codes regrouped for the operand reads, scales, the activation tile and the
+// group start values); 4 compute waves, one per column set, run the MFMAs on the
+// other buffer, issuing a group's MFMAs before converting the next group's codes so
+// that the conversion overlaps the matrix pipe.  One barrier per chunk.  Every
+// output has one owner: the result is deterministic.
+
 #include <math.h>
 
 #include "moe_internal.h"
@@ -45,10 +46,9 @@ constexpr int kCG = 4;                          // groups per K chunk
 constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 1 KB, one wave-wide LDS copy
 constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
 constexpr int kTileBytes = kMfmaItemRows * kRowPitch;
-// a wave's weight codes of one chunk, regrouped through LDS: 4 B blocks x 16 rows x
-// 128 B, rows 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
+// a column set's weight codes of one chunk in LDS: 4 B blocks x 16 rows x 128 B, rows
+// 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
 constexpr int kCodePitch = 144;
-constexpr int kCodeBytes = 4 * 16 * kCodePitch;
 
 __device__ __forceinline__ uint32_t bf16_rne_u(float f) {
     const uint32_t b = __float_as_uint(f);
