@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include "moe_internal.h"
+#include "select_union.h"
 
 namespace moe {
 
@@ -163,24 +164,72 @@ struct ItemsJob {
     const int32_t *n_uniq, *uniq, *off;
     int E;
     int32_t *items, *n_items;
+    int with_union;  // build the union first (uni), in this workgroup
+    UnionArgs uni;
 };
 
+// The work list from the union's per-expert counts and offsets in LDS (union_block's
+// layout): the same items, in the same (increasing expert) order, as mfma_items_body.
+__device__ __forceinline__ void mfma_items_from_counts(const int32_t *cnt, const int32_t *offs, int E,
+                                                       int32_t *items, int32_t *n_items) {
+    __shared__ int wsum[256 / kWave];
+    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
+    const int c = u < E ? cnt[u] : 0;
+    const int ni = (c + kMfmaItemRows - 1) / kMfmaItemRows;
+    int inc = ni;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) wsum[wv] = inc;
+    __syncthreads();
+    int base = inc - ni;
+    for (int v = 0; v < wv; v++) base += wsum[v];
+    for (int i = 0; i < ni; i++) {
+        int32_t *it = items + 4 * (base + i);
+        it[0] = u;
+        it[1] = offs[u] + kMfmaItemRows * i;
+        it[2] = min(kMfmaItemRows, c - kMfmaItemRows * i);
+        it[3] = 0;
+    }
+    if (u == blockDim.x - 1) n_items[0] = base + ni;
+}
+
 __global__ __launch_bounds__(256) void prep_kernel(PrepJob j0, PrepJob j1, ItemsJob it) {
+    extern __shared__ uint32_t prep_lds[];
     const int b = blockIdx.x;
-    if (b < j0.blocks)
+    if (b < j0.blocks) {
         prep_frag_body(j0, b);
-    else if (b < j0.blocks + j1.blocks)
+    } else if (b < j0.blocks + j1.blocks) {
         prep_frag_body(j1, b - j0.blocks);
-    else if (it.items)
-        mfma_items_body(it.n_uniq, it.uniq, it.off, it.E, it.items, it.n_items);
+    } else if (it.items) {
+        if (it.with_union) {
+            // the union ([R] §1.3), then the work list from its counts in LDS
+            union_block(it.uni, it.uni.ids, it.uni.keff, prep_lds);
+            __syncthreads();
+            const int E = it.uni.E, W = (it.uni.T + 31) / 32, W8 = (W + 7) / 8;
+            const int32_t *cnt = reinterpret_cast<const int32_t *>(prep_lds + (size_t)E * W + (size_t)E * W8);
+            mfma_items_from_counts(cnt, cnt + E, E, it.items, it.n_items);
+        } else {
+            mfma_items_body(it.n_uniq, it.uniq, it.off, it.E, it.items, it.n_items);
+        }
+    }
+}
+
+// (a 256-thread workgroup places at most about four picks per thread; larger batches keep
+// the union's own 1024-thread launch)
+bool union_in_prep_fits(int E, int T, int k) {
+    return (long)T * k <= 1024 && union_lds_words(E, T) * sizeof(uint32_t) <= 64 * 1024;
 }
 
 static hipError_t launch_prep(const PrepJob &j0, const PrepJob &j1, const ItemsJob &it,
                               const char *name, hipStream_t st) {
     const int blocks = j0.blocks + j1.blocks + (it.items ? 1 : 0);
     if (blocks == 0) return hipSuccess;
+    const size_t lds = it.items && it.with_union ? union_lds_words(it.uni.E, it.uni.T) * sizeof(uint32_t) : 0;
     ProfScope prof(name, st);
-    prep_kernel<<<blocks, 256, 0, st>>>(j0, j1, it);
+    prep_kernel<<<blocks, 256, lds, st>>>(j0, j1, it);
     return hipGetLastError();
 }
 
@@ -596,6 +645,8 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     it.E = a.E;
     it.items = a.with_routed ? a.items : nullptr;
     it.n_items = a.n_items;
+    it.with_union = a.union_in_prep;
+    it.uni = a.uni;
     e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_nsx), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
@@ -604,6 +655,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     // have) and the shared rows
     ItemsJob no_items = it;
     no_items.items = nullptr;
+    no_items.with_union = 0;
     e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_nsx) : none,
                     a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx) : none,
                     no_items, "prep_h", st);

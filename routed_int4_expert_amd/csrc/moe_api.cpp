@@ -268,6 +268,8 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     m.max_items = p.max_items;
     m.with_routed = f.with_routed;
     m.with_shared = f.with_shared;
+    m.union_in_prep = f.union_in_prep;
+    m.uni = f.uni;
     return m;
 }
 
@@ -305,6 +307,7 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     a.with_routed = 1;
     a.with_shared = L.shared_ffn > 0 ? 1 : 0;
     a.fuse_select = 0;
+    a.union_in_prep = 0;
     memset(&a.sel, 0, sizeof(a.sel));
     memset(&a.uni, 0, sizeof(a.uni));
     return a;
@@ -405,7 +408,13 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
                                     union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
     } else {
         e = run_route(*L, p, x, T, ids, w, keff, ws, st);
-        if (e == hipSuccess) e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+        // the union inside the first matrix-core preparation launch when it fits there
+        if (union_in_prep_fits(L->n_experts, T, L->top_k)) {
+            a.union_in_prep = 1;
+            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
+        } else if (e == hipSuccess) {
+            e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+        }
     }
     CombineArgs c;
     c.w = w;

@@ -109,6 +109,9 @@ struct FfnArgs {
     int fuse_select;
     SelectArgs sel;
     UnionArgs uni;
+    // Matrix-core path: the union (uni) built by the work-list workgroup of the first
+    // preparation launch instead of a launch of its own (union_in_prep_fits).
+    int union_in_prep;
 };
 
 // LDS words of the in-launch selection and union for T tokens of top-k over E experts.
@@ -137,6 +140,8 @@ struct MfmaArgs {
     float *y_routed, *y_shared;      // [rows][H], [T][H]
     int T, H, F, Fs, E, max_units, max_rows, max_items;
     int with_routed, with_shared;
+    int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
+    UnionArgs uni;
 };
 
 // Matrix-core work items: at most this many rows of one expert (one 16-row MFMA block).
@@ -149,6 +154,9 @@ inline int mfma_max_items(int max_units, int max_rows) {
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
+// Whether the union of T tokens (top-k) is built by the work-list workgroup: few picks,
+// and its LDS fits what that workgroup may take.
+bool union_in_prep_fits(int E, int T, int k);
 
 
 // Bracketing HIP events around one kernel launch while moe_prof_begin() is active.
