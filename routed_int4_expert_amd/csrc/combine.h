@@ -15,26 +15,44 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-// outputs n .. n+3 of token t (n a multiple of 4, H a multiple of 64)
+// outputs n .. n+3 of token t (n a multiple of 4, H a multiple of 64).  The slots'
+// rows and weights are read first, then all the rows' values, so the loads take two
+// round trips whatever k is; the sum runs in slot order.
 __device__ __forceinline__ void combine4(const CombineArgs &a, int t, int n) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const int ke = min(max(a.keff[t], 0), a.k);
-    for (int j = 0; j < ke; j++) {
-        const int r = a.pick_row[(size_t)t * a.k + j];
-        if (r < 0) continue;
-        const float wj = a.w[(size_t)t * a.k + j];
-        const float4 y = *reinterpret_cast<const float4 *>(a.y_routed + (size_t)r * a.H + n);
-        acc.x = fmaf(wj, y.x, acc.x);
-        acc.y = fmaf(wj, y.y, acc.y);
-        acc.z = fmaf(wj, y.z, acc.z);
-        acc.w = fmaf(wj, y.w, acc.w);
+    // loads are unconditional (clamped slot, row 0 for an empty slot), so they are all
+    // in flight together; empty slots are masked out of the sum
+    int rj[MOE_MAX_TOPK];
+    float wj[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; j++) {
+        const size_t sj = (size_t)t * a.k + min(j, a.k - 1);
+        rj[j] = a.pick_row[sj];
+        wj[j] = a.w[sj];
+    }
+    float4 yj[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; j++)
+        yj[j] = *reinterpret_cast<const float4 *>(a.y_routed + (size_t)max(rj[j], 0) * a.H + n);
+    float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.y_shared) ys = *reinterpret_cast<const float4 *>(a.y_shared + (size_t)t * a.H + n);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; j++) {
+        const bool live = j < ke && rj[j] >= 0;
+        const float w = live ? wj[j] : 0.f;
+        if (live) {
+            acc.x = fmaf(w, yj[j].x, acc.x);
+            acc.y = fmaf(w, yj[j].y, acc.y);
+            acc.z = fmaf(w, yj[j].z, acc.z);
+            acc.w = fmaf(w, yj[j].w, acc.w);
+        }
     }
     if (a.y_shared) {
-        const float4 y = *reinterpret_cast<const float4 *>(a.y_shared + (size_t)t * a.H + n);
-        acc.x += y.x;
-        acc.y += y.y;
-        acc.z += y.z;
-        acc.w += y.w;
+        acc.x += ys.x;
+        acc.y += ys.y;
+        acc.z += ys.z;
+        acc.w += ys.w;
     }
     if (a.out_bf16) {
         uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (size_t)t * a.H + n;
