@@ -75,6 +75,11 @@ SMALL = [
     # launches (the combine then runs on its own)
     S.custom("raggedfew", hidden=320, n_experts=24, ffn=192, shared_ffn=64, top_k=5, tokens=3,
              top_p=0.8, routed_scale=2.5, bias_amp=0.3),
+    # more than 16 tokens with at most 1024 picks: the union is built inside the first
+    # matrix-core preparation launch; K = 320 leaves a partial 4-group chunk, top-p keeps
+    # fewer than k, and the shared expert is narrower than the routed ones
+    S.custom("midtok", hidden=320, n_experts=48, ffn=128, shared_ffn=64, top_k=6, tokens=40,
+             top_p=0.85, routed_scale=1.5, bias_amp=0.2),
 ]
 
 
