@@ -76,15 +76,17 @@ def cpu_baseline(sh, bank, routers, xs_host, seconds, per_token_layers=1):
     import oracle as R
     from routed_int4_expert_amd import synth as S
 
-    n, t0 = 0, time.time()
     Ls = []
     for l in range(per_token_layers):
         d = S.make_layer(sh, seed=0, layer=l, bank=bank)
         d["router_w"], d["router_bias"] = routers[l]
         Ls.append(R.Layer(d))
-    while n == 0 or (time.time() - t0 < seconds and n < xs_host.shape[0]):
+    # tokens of the pool in turn until the time budget is spent (timing excludes set-up)
+    n, t0 = 0, time.time()
+    while n == 0 or time.time() - t0 < seconds:
+        i = n % xs_host.shape[0]
         for L in Ls:
-            R.layer_forward(L, xs_host[n:n + 1])
+            R.layer_forward(L, xs_host[i:i + 1])
         n += 1
     dt = time.time() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
