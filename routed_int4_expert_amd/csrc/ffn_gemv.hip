@@ -432,11 +432,20 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
     }
 }
 
-// a.passes: passes per workgroup, chosen on the host so the grid fits in one
-// round of resident workgroups
+// One-dimensional grid: workgroups [0, nsh) take the shared expert with passes_sh
+// passes each, the rest the routed units, gx workgroups of `passes` passes per unit.
+// The counts are chosen on the host so the grid fits in one round of resident
+// workgroups.
 template <int LPR, int RM, bool GU>
-__global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes) {
-    gemv_body<LPR, RM, GU>(a, passes, blockIdx.y, blockIdx.x);
+__global__ __launch_bounds__(256, 4) void q4_gemv_kernel(FfnArgs a, int passes, int passes_sh, int nsh,
+                                                         int gx) {
+    const int w = blockIdx.x;
+    if (w < nsh) {
+        gemv_body<LPR, RM, GU>(a, passes_sh, a.max_units, w);
+    } else {
+        const int r = w - nsh;
+        gemv_body<LPR, RM, GU>(a, passes, r / gx, r % gx);
+    }
 }
 
 static int lanes_per_row(int K) {
@@ -482,13 +491,28 @@ static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     int per_cu = 4;
     while (per_cu > 1 && (size_t)per_cu * (lds + 2048) > 160 * 1024) per_cu--;  // + static LDS
     const long cap = (long)device_cus() * per_cu;
-    const int units = a.max_units + 1;
     const int blocks1 = (N + S::BF - 1) / S::BF;  // workgroups per unit at one pass each
-    int passes = 1;
-    while ((long)((blocks1 + passes - 1) / passes) * units > cap && passes < blocks1) passes++;
-    dim3 grid((blocks1 + passes - 1) / passes, units);
+    int passes = 1, passes_sh = 1, nsh = 0, gx;
+    if (GU && RM == 1 && a.fuse_select && a.with_shared) {
+        // one token: the routed units cannot start before the selection, the shared
+        // expert can; give it one-pass workgroups in the slots the routed grid leaves,
+        // so its weights stream during the selection
+        const int sh1 = (a.Fs + S::BF - 1) / S::BF;
+        while ((long)((blocks1 + passes - 1) / passes) * a.max_units + 1 > cap && passes < blocks1) passes++;
+        gx = (blocks1 + passes - 1) / passes;
+        const long left = cap - (long)gx * a.max_units;
+        while ((long)((sh1 + passes_sh - 1) / passes_sh) > left && passes_sh < sh1) passes_sh++;
+        nsh = (sh1 + passes_sh - 1) / passes_sh;
+    } else {
+        const int units = a.max_units + 1;
+        while ((long)((blocks1 + passes - 1) / passes) * units > cap && passes < blocks1) passes++;
+        gx = (blocks1 + passes - 1) / passes;
+        passes_sh = passes;
+        nsh = a.with_shared ? gx : 0;
+    }
+    const long blocks = nsh + (long)gx * a.max_units;
     ProfScope prof(GU ? "ffn_gateup" : "ffn_down", st);
-    q4_gemv_kernel<LPR, RM, GU><<<grid, 256, lds, st>>>(a, passes);
+    q4_gemv_kernel<LPR, RM, GU><<<(unsigned)blocks, 256, lds, st>>>(a, passes, passes_sh, nsh, gx);
     return hipGetLastError();
 }
 
