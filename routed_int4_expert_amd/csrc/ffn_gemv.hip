@@ -159,56 +159,73 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
 }
 
 // Stages R input rows as bf16 hi/lo pairs in dot order, with each 32-element chunk's
-// sum of the staged values, by threads [t0, t0 + nt) of the block (t0, nt multiples of
-// 4): a thread per 8 elements, loads issued four items at a time before any is
-// converted; the 4 threads of a chunk are adjacent lanes and add their partial sums
-// with two shuffles.
-__device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
-                                           const int32_t *rt, int rc, int R, int K, int t0, int nt) {
-    constexpr int B = 4;
-    uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
-    const int n8 = R * (K / 8);
-    for (int i0 = (int)threadIdx.x - t0; i0 < n8; i0 += B * nt) {
-        float4 v[B][2];
+// sum of the staged values, by nt threads of the block (nt a multiple of 4; thread
+// number i of them starts at item i): a thread per 8 elements, in batches of four
+// items per thread whose loads are all issued (stage_issue) before any is converted and
+// stored (stage_commit); the 4 threads of a chunk are adjacent lanes and add their
+// partial sums with two shuffles.
+constexpr int kStageBatch = 4;
+struct StageBatch {
+    float4 v[kStageBatch][2];
+};
+
+__device__ __forceinline__ void stage_issue(StageBatch &sb, const float *xin, const int32_t *rt, int rc,
+                                            int K, int n8, int i0, int nt) {
 #pragma unroll
-        for (int b = 0; b < B; b++) {
-            const int i = i0 + b * nt;
-            if (i < n8) {
-                const int r = i / (K / 8), g = i % (K / 8);
-                const int src = rt ? rt[rc + r] : rc + r;
-                const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
-                v[b][0] = px[0];
-                v[b][1] = px[1];
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            const int i = i0 + b * nt;
-            if (i >= n8) continue;  // the same for the 4 lanes of a chunk
+    for (int b = 0; b < kStageBatch; b++) {
+        const int i = i0 + b * nt;
+        if (i < n8) {
             const int r = i / (K / 8), g = i % (K / 8);
-            const float xe[8] = {v[b][0].x, v[b][0].y, v[b][0].z, v[b][0].w,
-                                 v[b][1].x, v[b][1].y, v[b][1].z, v[b][1].w};
-            uint32_t hb[8], lb[8];
-            float ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                hb[e] = bf16_rne_bits(xe[e]);
-                lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
-                ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
-            }
-            uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
-            w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
-            w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
-            w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
-            w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
-            uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
-            uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
-            dst[0] = w0;
-            dst[1] = w1;
-            ps += __shfl_xor(ps, 1, kWave);
-            ps += __shfl_xor(ps, 2, kWave);
-            if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
+            const int src = rt ? rt[rc + r] : rc + r;
+            const float4 *px = reinterpret_cast<const float4 *>(xin + (size_t)src * K + 8 * g);
+            sb.v[b][0] = px[0];
+            sb.v[b][1] = px[1];
         }
+    }
+}
+
+__device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, int rowpitch, int K, int n8,
+                                             int i0, int nt) {
+    uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
+#pragma unroll
+    for (int b = 0; b < kStageBatch; b++) {
+        const int i = i0 + b * nt;
+        if (i >= n8) continue;  // the same for the 4 lanes of a chunk
+        const int r = i / (K / 8), g = i % (K / 8);
+        const float xe[8] = {sb.v[b][0].x, sb.v[b][0].y, sb.v[b][0].z, sb.v[b][0].w,
+                             sb.v[b][1].x, sb.v[b][1].y, sb.v[b][1].z, sb.v[b][1].w};
+        uint32_t hb[8], lb[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            hb[e] = bf16_rne_bits(xe[e]);
+            lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
+            ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
+        }
+        uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
+        w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
+        w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
+        w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
+        w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
+        uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
+        uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
+        dst[0] = w0;
+        dst[1] = w1;
+        ps += __shfl_xor(ps, 1, kWave);
+        ps += __shfl_xor(ps, 2, kWave);
+        if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
+    }
+}
+
+// The thread's batches from item `first` on (its number among the nt threads, for a
+// whole staging).
+__device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
+                                           const int32_t *rt, int rc, int R, int K, int first, int nt) {
+    const int n8 = R * (K / 8);
+    for (int i0 = first; i0 < n8; i0 += kStageBatch * nt) {
+        StageBatch sb;
+        stage_issue(sb, xin, rt, rc, K, n8, i0, nt);
+        stage_commit(sb, xs, rowpitch, K, n8, i0, nt);
     }
 }
 
@@ -241,7 +258,8 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         if (threadIdx.x < kWave)
             select_union_one(a, lds, bx == 0 && unit == 0);
         else
-            stage_rows(xs, (H / 32) * kChunkPitch, a.x, nullptr, 0, 1, H, kWave, blockDim.x - kWave);
+            stage_rows(xs, (H / 32) * kChunkPitch, a.x, nullptr, 0, 1, H, (int)threadIdx.x - kWave,
+                       blockDim.x - kWave);
         __syncthreads();
         const int k = a.sel.k, E = a.sel.E;
         n_uniq_p = lds + 2 * k + 1;
@@ -259,8 +277,11 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
     float *out;         // output rows
     size_t out_row0;    // first output row index
     if (unit < a.max_units) {
-        if (!a.with_routed || unit >= n_uniq_p[0]) return;
+        if (!a.with_routed) return;
+        // both loads at once: uniq holds max_units <= E entries, -1 past the union
+        const int nu = n_uniq_p[0];
         const int e = uniq_p[unit];
+        if ((unit >= nu) | (e < 0)) return;  // (either test alone suffices; both keep the loads together)
         const int r0 = off_p[e];
         nrows = off_p[e + 1] - r0;
         Fu = a.F;
@@ -332,14 +353,26 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
             }
         }
     };
-    // the first step's codes do not depend on the staged rows: issue them before staging
-    load_step(0, q, sc);
+    // The first batch of the first rows' activation loads goes out first, then the first
+    // step's codes (independent of the staged rows), so the rows are converted while the
+    // codes are in flight.
+    if (staged) {
+        load_step(0, q, sc);
+    } else {
+        const int n80 = min(RM, nrows) * (K / 8);
+        StageBatch sb0;
+        stage_issue(sb0, xin, rt, 0, K, n80, tid, blockDim.x);
+        load_step(0, q, sc);
+        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x);
+        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x);
+        __syncthreads();
+    }
 
     for (int rc = 0; rc < nrows; rc += RM) {
         const int R = min(RM, nrows - rc);
-        if (!(staged && rc == 0)) {
+        if (rc > 0) {
             __syncthreads();  // previous rows fully consumed
-            stage_rows(xs, rowpitch, xin, rt, rc, R, K, 0, blockDim.x);
+            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x);
             __syncthreads();
         }
 

@@ -1,7 +1,7 @@
 // router_gemv.h -- step 1 of the MoE layer ("MoE 路由与专家流式加载" §1.1) for a
 // few tokens: the logits of one expert, logit[t][e] = Wr[e]·x[t], by one workgroup.
 // Its four waves split H, every lane issues all its float4 loads of the router row
-// at once, the row is applied to every token with exact fp32 products summed in
+// before using any, the row is applied to every token with exact fp32 products summed in
 // fp64, and the four wave sums are added in a fixed order.  Complete logits, a
 // single slice (S = 1); with `sig` set, also each logit's sigmoid gate and choice key.
 #pragma once
@@ -19,6 +19,10 @@ __device__ __forceinline__ double router_shfl_xor_f64(double v, int m) {
 
 template <int TT>
 __device__ __forceinline__ void router_gemv_body(const LogitsArgs &a, int e) {
+    // float4 loads of the router row per lane issued before the first is used (all of
+    // a row of up to 8192 values); indices past the row re-read its last float4 and
+    // are not accumulated, so no load waits behind a branch
+    constexpr int U = 8;
     __shared__ double red[4][TT];
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     const int n4 = a.H / 4;
@@ -27,17 +31,24 @@ __device__ __forceinline__ void router_gemv_body(const LogitsArgs &a, int e) {
     double acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) acc[t] = 0.0;
-#pragma unroll 8
-    for (int j = threadIdx.x; j < n4; j += 256) {
-        const float4 w = w4[j];
+    for (int j0 = threadIdx.x; j0 < n4; j0 += 256 * U) {
+        float4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) w[u] = w4[min(j0 + 256 * u, n4 - 1)];
 #pragma unroll
         for (int t = 0; t < TT; t++) {
-            if (t < a.T) {
-                const float4 v = x4[(size_t)t * n4 + j];
-                acc[t] = fma((double)v.x, (double)w.x, acc[t]);
-                acc[t] = fma((double)v.y, (double)w.y, acc[t]);
-                acc[t] = fma((double)v.z, (double)w.z, acc[t]);
-                acc[t] = fma((double)v.w, (double)w.w, acc[t]);
+            const float4 *xt = x4 + (size_t)min(t, a.T - 1) * n4;  // rows past T: not written
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) v[u] = xt[min(j0 + 256 * u, n4 - 1)];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (j0 + 256 * u < n4) {
+                    acc[t] = fma((double)v[u].x, (double)w[u].x, acc[t]);
+                    acc[t] = fma((double)v[u].y, (double)w[u].y, acc[t]);
+                    acc[t] = fma((double)v[u].z, (double)w[u].z, acc[t]);
+                    acc[t] = fma((double)v[u].w, (double)w[u].w, acc[t]);
+                }
             }
         }
     }
