@@ -282,8 +282,10 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         const int nu = n_uniq_p[0];
         const int e = uniq_p[unit];
         if ((unit >= nu) | (e < 0)) return;  // (either test alone suffices; both keep the loads together)
-        const int r0 = off_p[e];
-        nrows = off_p[e + 1] - r0;
+        // one token: each union expert has one row, in union order, so unit u is row u
+        // (no offset lookup, one round trip less before the first weight load)
+        const int r0 = a.T == 1 ? unit : off_p[e];
+        nrows = a.T == 1 ? 1 : off_p[e + 1] - r0;
         Fu = a.F;
         if (GU) {
             const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
@@ -527,11 +529,14 @@ static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     const int blocks1 = (N + S::BF - 1) / S::BF;  // workgroups per unit at one pass each
     int passes = 1, passes_sh = 1, nsh = 0, gx;
     if (GU && RM == 1 && a.fuse_select && a.with_shared) {
-        // one token: the routed units cannot start before the selection, the shared
-        // expert can; give it one-pass workgroups in the slots the routed grid leaves,
-        // so its weights stream during the selection
+        // One token: the routed units cannot start before the selection, the shared
+        // expert can; it gets one-pass workgroups, so its weights stream during the
+        // selection.  The routed grid is sized so that, with them, every CU holds
+        // at most three workgroups: a fourth workgroup on some CUs starts its
+        // selection later and streams slower than the rest, and sets the end.
         const int sh1 = (a.Fs + S::BF - 1) / S::BF;
-        while ((long)((blocks1 + passes - 1) / passes) * a.max_units + 1 > cap && passes < blocks1) passes++;
+        const long cap3 = (long)device_cus() * 3;
+        while ((long)((blocks1 + passes - 1) / passes) * a.max_units + sh1 > cap3 && passes < blocks1) passes++;
         gx = (blocks1 + passes - 1) / passes;
         const long left = cap - (long)gx * a.max_units;
         while ((long)((sh1 + passes_sh - 1) / passes_sh) > left && passes_sh < sh1) passes_sh++;
