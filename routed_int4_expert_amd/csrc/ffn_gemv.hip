@@ -102,6 +102,10 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
     // byte flags of the kept experts (in the pick scratch's place: the selection is done)
     uint8_t *flag = reinterpret_cast<uint8_t *>(&ps_sel);
     static_assert(sizeof(PickScratch) >= MOE_MAX_EXPERTS, "flag bytes fit the scratch");
+    // The selection is on the critical path of every routed workgroup and shares its
+    // SIMD with older workgroups' streaming waves, which the arbiter would favour:
+    // the selecting wave runs at raised issue priority until the union is built.
+    __builtin_amdgcn_s_setprio(3);
     select_token(a.sel, 0, lane, ids_l, w_l, keff_l, nullptr, nullptr, &ps_sel);
     wave_lds_sync();
     const int keff = *keff_l;
@@ -142,6 +146,7 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
         rt_l[lane] = my >= 0 ? 0 : -1;
     }
     wave_lds_sync();
+    __builtin_amdgcn_s_setprio(0);
     if (writer) {
         for (int i = lane; i < k; i += kWave) {
             a.sel.ids[i] = ids_l[i];

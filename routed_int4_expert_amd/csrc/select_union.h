@@ -46,22 +46,44 @@ struct PickScratch {
     int id[MOE_MAX_TOPK];
 };
 
-__device__ __forceinline__ unsigned long long wave_and_u64(unsigned long long v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-        v &= ((unsigned long long)hi << 32) | lo;
-    }
+// AND and OR of a 64-bit value over a whole wave (all 64 lanes active), as
+// wave-uniform values: within each row of 16 lanes by DPP moves (swap neighbours,
+// swap pairs, rotate by 4, rotate by 8), then the four rows' results read from lanes
+// 0, 16, 32 and 48.  No LDS round trip; the results live in scalar registers.
+__device__ __forceinline__ uint32_t row_reduce_and(uint32_t v) {
+    v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);  // row_ror 4
+    v &= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror 8
     return v;
 }
 
-__device__ __forceinline__ unsigned long long wave_or_u64(unsigned long long v) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-        v |= ((unsigned long long)hi << 32) | lo;
-    }
+__device__ __forceinline__ uint32_t row_reduce_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
     return v;
+}
+
+__device__ __forceinline__ uint32_t rows_and(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) & (uint32_t)__builtin_amdgcn_readlane((int)v, 16) &
+           (uint32_t)__builtin_amdgcn_readlane((int)v, 32) & (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+__device__ __forceinline__ uint32_t rows_or(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) | (uint32_t)__builtin_amdgcn_readlane((int)v, 16) |
+           (uint32_t)__builtin_amdgcn_readlane((int)v, 32) | (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+__device__ __forceinline__ unsigned long long wave_and_u64(unsigned long long v) {
+    const uint32_t lo = rows_and(row_reduce_and((uint32_t)v)), hi = rows_and(row_reduce_and((uint32_t)(v >> 32)));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long wave_or_u64(unsigned long long v) {
+    const uint32_t lo = rows_or(row_reduce_or((uint32_t)v)), hi = rows_or(row_reduce_or((uint32_t)(v >> 32)));
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
