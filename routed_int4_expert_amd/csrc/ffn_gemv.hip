@@ -51,6 +51,13 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// the value of each lane's DPP source lane (CTRL: a quad_perm or row_ror control, for
+// which every source lane is in the same row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // sum over 32 codes of (136 + q_i) * x_i, x staged as 8 uint4 of bf16 pairs
 __device__ __forceinline__ float dot32_bf16(const uint4 q, const uint4 *xv) {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
@@ -74,11 +81,28 @@ __device__ __forceinline__ float dot32_bf16(const uint4 q, const uint4 *xv) {
     return a0 + a1;
 }
 
+// Sum over each group of LPR lanes, in a fixed order (deterministic); the group's
+// first lane holds the total.  A whole wave (LPR = 64, all lanes active): each row
+// of 16 lanes by DPP moves (swap neighbours, swap pairs, rotate by 4, rotate by 8),
+// then the four row sums read from lanes 0, 16, 32 and 48 -- no LDS round trip.
+// Narrower groups: butterfly shuffles.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LPR == kWave) {
+        v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+        v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+        v += dpp_f32<0x124>(v);  // row_ror 4
+        v += dpp_f32<0x128>(v);  // row_ror 8
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+        return (r0 + r1) + (r2 + r3);
+    } else {
 #pragma unroll
-    for (int m = LPR / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+        for (int m = LPR / 2; m > 0; m >>= 1) v += __shfl_xor(v, m, kWave);
+        return v;
+    }
 }
 
 // Selection and union of a one-token decode step, by wave 0 into LDS ([R] §1.1-§1.3;
@@ -167,8 +191,8 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
 // sum of the staged values, by nt threads of the block (nt a multiple of 4; thread
 // number i of them starts at item i): a thread per 8 elements, in batches of four
 // items per thread whose loads are all issued (stage_issue) before any is converted and
-// stored (stage_commit); the 4 threads of a chunk are adjacent lanes and add their
-// partial sums with two shuffles.
+// stored (stage_commit); the 4 threads of a chunk form an aligned quad of lanes and
+// add their partial sums with two DPP moves.
 constexpr int kStageBatch = 4;
 struct StageBatch {
     float4 v[kStageBatch][2];
@@ -216,8 +240,8 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
         dst[0] = w0;
         dst[1] = w1;
-        ps += __shfl_xor(ps, 1, kWave);
-        ps += __shfl_xor(ps, 2, kWave);
+        ps += dpp_f32<0xB1>(ps);  // the chunk's four lanes form an aligned quad
+        ps += dpp_f32<0x4E>(ps);
         if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
     }
 }

@@ -11,10 +11,28 @@
 
 namespace moe {
 
-__device__ __forceinline__ double router_shfl_xor_f64(double v, int m) {
-    const int lo = __shfl_xor(__double2loint(v), m, kWave);
-    const int hi = __shfl_xor(__double2hiint(v), m, kWave);
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
     return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double readlane_lane_f64(double v, int lane) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                            __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+
+// Sum over the 64 lanes of a wave (all active), in a fixed order: rows of 16 lanes by
+// DPP moves (swap neighbours, swap pairs, rotate by 4, rotate by 8), then the four
+// row sums from lanes 0, 16, 32 and 48, wave-uniform.
+__device__ __forceinline__ double router_wave_sum_f64(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x124>(v);
+    v += dpp_f64<0x128>(v);
+    return (readlane_lane_f64(v, 0) + readlane_lane_f64(v, 16)) +
+           (readlane_lane_f64(v, 32) + readlane_lane_f64(v, 48));
 }
 
 template <int TT>
@@ -54,8 +72,7 @@ __device__ __forceinline__ void router_gemv_body(const LogitsArgs &a, int e) {
     }
 #pragma unroll
     for (int t = 0; t < TT; t++) {
-#pragma unroll
-        for (int m = kWave / 2; m > 0; m >>= 1) acc[t] += router_shfl_xor_f64(acc[t], m);
+        acc[t] = router_wave_sum_f64(acc[t]);
         if (lane == 0) red[wv][t] = acc[t];
     }
     __syncthreads();
