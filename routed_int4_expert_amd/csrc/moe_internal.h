@@ -104,8 +104,9 @@ struct FfnArgs {
     int T, H, F, Fs, max_units;
     int with_routed, with_shared;
     // Selection and union inside the gate/up launch (one token): every routed
-    // workgroup selects and builds the union in LDS from the router logits; workgroup
-    // (0,0) also writes them out through sel (ids, w, keff) and uni (union arrays).
+    // workgroup selects and builds the union in LDS from the router logits; the
+    // first routed workgroup also writes them out through sel (ids, w, keff) and uni
+    // (union arrays).
     int fuse_select;
     SelectArgs sel;
     UnionArgs uni;
