@@ -10,17 +10,17 @@
 // wave's load covers LPR*16 contiguous bytes of one row.
 //
 // Codes: a byte holds elements 2j (low nibble) and 2j+1 (high nibble) as
-// two's-complement int4 ("colibrì 深度拆解" §5.2).  Shifting a 32-bit word of 8
-// codes right by 4s and keeping bits 0-3 and 16-19 gives the codes of elements
-// s and s+4; XOR with 0x4308 in each half turns code q into the bf16 bit pattern
-// of 136 + q (0x4300 is 128.0 and q XOR 8 = q + 8 in [0, 15] is the low mantissa),
-// so one bit operation yields a bf16 pair exactly.  Activations are staged as
-// bf16 pairs x = hi + lo (hi = bf16(x), lo = bf16(x - hi), 16 significant bits),
-// and v_dot2 accumulates (136 + q)(hi + lo) in fp32; products are exact.  Per 32
-// elements the offset is removed with the staged sum of x,
-//   sum(q x) = sum((136 + q) x) - 136 sum(x)
-// (the unsigned-offset identity of "colibri 开发演进实录" §2.2, K1), and the
-// fp32 gs64 scale multiplies each 32-element partial (two per 64-group).
+// two's-complement int4 ("colibrì 深度拆解" §5.2).  XOR with 8 in every nibble turns
+// code q into u = q + 8 in [0, 15]; masking a 32-bit word of 8 codes with 0x0F0F0F0F
+// (and the word shifted right by 4) gives the even (odd) elements as four unsigned
+// bytes, three bit operations for eight codes.  Activations are staged per 32-element
+// chunk in 16-bit fixed point: x16 = rint(x * 32639 / max|x|), split into two signed
+// bytes x16 = 256 hi + lo; v_dot4_i32_i8 accumulates u * hi and u * lo exactly in
+// int32, and per chunk
+//   sum(q x16) = 256 sum(u hi) + sum(u lo) - 8 sum(x16)
+// (the unsigned-offset identity of "colibri 开发演进实录" §2.2, K1), times the chunk's
+// step max|x| / 32639 and the fp32 gs64 scale (two chunks per 64-group).  The only
+// rounding before the fp32 accumulation is x16: at most max|x| / 65278 per element.
 //
 // The gate/up kernel finishes with the fused SiLU(g) * u epilogue and writes
 // h [rows][F]; the down kernel writes the unweighted y [rows][H].  Each output
@@ -32,24 +32,13 @@
 
 namespace moe {
 
-// LDS row layout: per 32-element chunk 36 dwords -- 32 dwords of bf16 pairs in
-// dot order ([d][s][hi,lo] for 8-element group d and pair s = elements 8d+s and
-// 8d+s+4), the chunk's sum of x at dword 32, then padding so the 16-byte reads
-// of 8 consecutive lanes hit distinct banks.
-constexpr int kChunkPitch = 36;
-constexpr uint32_t kBf16Offset = 0x43084308u;
-constexpr float kCodeOffset = 136.0f;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x2_t as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    const uint32_t b = __float_as_uint(f);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// LDS row layout: per 32-element chunk 20 dwords -- for each 8-element group d four
+// dwords of signed bytes (hi of elements 8d+0,2,4,6; hi of 8d+1,3,5,7; lo of the
+// even ones; lo of the odd ones), the chunk's step max|x|/32639 (fp32) at dword 16
+// and 8 sum(x16) (int32) at dword 17, then padding: the 16-byte reads of 8
+// consecutive lanes (80 bytes apart) hit distinct banks.
+constexpr int kChunkPitch = 20;
+constexpr float kX16Max = 32639.0f;  // 127 * 256 + 127: both bytes of x16 stay in [-128, 127]
 
 // the value of each lane's DPP source lane (CTRL: a quad_perm or row_ror control, for
 // which every source lane is in the same row)
@@ -58,27 +47,21 @@ __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// sum over 32 codes of (136 + q_i) * x_i, x staged as 8 uint4 of bf16 pairs
-__device__ __forceinline__ float dot32_bf16(const uint4 q, const uint4 *xv) {
+// sum over 32 codes of (q_i + 8) * x16_i, the chunk staged as 4 uint4 of byte limbs
+__device__ __forceinline__ int dot32_i8(const uint4 q, const uint4 *xv) {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-    float a0 = 0.f, a1 = 0.f;
+    int ah = 0, al = 0;
 #pragma unroll
     for (int d = 0; d < 4; d++) {
-        const uint4 x01 = xv[2 * d], x23 = xv[2 * d + 1];
-        const uint32_t p0 = (wd[d] & 0x000F000Fu) ^ kBf16Offset;
-        const uint32_t p1 = ((wd[d] >> 4) & 0x000F000Fu) ^ kBf16Offset;
-        const uint32_t p2 = ((wd[d] >> 8) & 0x000F000Fu) ^ kBf16Offset;
-        const uint32_t p3 = ((wd[d] >> 12) & 0x000F000Fu) ^ kBf16Offset;
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p0), as_bf2(x01.x), a0, false);
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p0), as_bf2(x01.y), a0, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p1), as_bf2(x01.z), a1, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p1), as_bf2(x01.w), a1, false);
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p2), as_bf2(x23.x), a0, false);
-        a0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p2), as_bf2(x23.y), a0, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p3), as_bf2(x23.z), a1, false);
-        a1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(p3), as_bf2(x23.w), a1, false);
+        const uint32_t ev = (wd[d] ^ 0x08080808u) & 0x0F0F0F0Fu;         // u of elements 0,2,4,6
+        const uint32_t od = ((wd[d] >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;  // u of elements 1,3,5,7
+        const uint4 x = xv[d];
+        ah = __builtin_amdgcn_sdot4((int)ev, (int)x.x, ah, false);
+        ah = __builtin_amdgcn_sdot4((int)od, (int)x.y, ah, false);
+        al = __builtin_amdgcn_sdot4((int)ev, (int)x.z, al, false);
+        al = __builtin_amdgcn_sdot4((int)od, (int)x.w, al, false);
     }
-    return a0 + a1;
+    return (ah << 8) + al;  // |.| < 2^25: 32 products of at most 15 * 32639
 }
 
 // Sum over each group of LPR lanes, in a fixed order (deterministic); the group's
@@ -187,12 +170,12 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
     }
 }
 
-// Stages R input rows as bf16 hi/lo pairs in dot order, with each 32-element chunk's
-// sum of the staged values, by nt threads of the block (nt a multiple of 4; thread
-// number i of them starts at item i): a thread per 8 elements, in batches of four
-// items per thread whose loads are all issued (stage_issue) before any is converted and
-// stored (stage_commit); the 4 threads of a chunk form an aligned quad of lanes and
-// add their partial sums with two DPP moves.
+// Stages R input rows in the 16-bit fixed-point chunk format above, by nt threads of
+// the block (nt a multiple of 4; thread number i of them starts at item i): a thread
+// per 8 elements, in batches of four items per thread whose loads are all issued
+// (stage_issue) before any is converted and stored (stage_commit).  The 4 threads of
+// a chunk form an aligned quad of lanes and combine their max|x| and sum(x16) with
+// two DPP moves each.
 constexpr int kStageBatch = 4;
 struct StageBatch {
     float4 v[kStageBatch][2];
@@ -213,6 +196,17 @@ __device__ __forceinline__ void stage_issue(StageBatch &sb, const float *xin, co
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// four signed bytes (a, b, c, d) as one word, a in the low byte
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)d << 24);
+}
+
 __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, int rowpitch, int K, int n8,
                                              int i0, int nt) {
     uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
@@ -223,26 +217,39 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         const int r = i / (K / 8), g = i % (K / 8);
         const float xe[8] = {sb.v[b][0].x, sb.v[b][0].y, sb.v[b][0].z, sb.v[b][0].w,
                              sb.v[b][1].x, sb.v[b][1].y, sb.v[b][1].z, sb.v[b][1].w};
-        uint32_t hb[8], lb[8];
-        float ps = 0.f;
+        // chunk max of |x| as an unsigned bit pattern (NaN and infinity order above
+        // every finite value, so they are not lost)
+        uint32_t mb = 0;
+#pragma unroll
+        for (int e = 0; e < 8; e++) mb = max(mb, __float_as_uint(xe[e]) & 0x7FFFFFFFu);
+        mb = max(mb, dpp_u32<0xB1>(mb));
+        mb = max(mb, dpp_u32<0x4E>(mb));
+        const bool finite = mb < 0x7F800000u;
+        const float mx = __uint_as_float(mb);
+        const float inv = (finite && mb != 0u) ? kX16Max / mx : 0.0f;
+        int x16[8], hi[8], lo[8];
+        int ps = 0;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            hb[e] = bf16_rne_bits(xe[e]);
-            lb[e] = bf16_rne_bits(xe[e] - bf16_to_f32(hb[e]));
-            ps += bf16_to_f32(hb[e]) + bf16_to_f32(lb[e]);
+            x16[e] = (int)fminf(fmaxf(rintf(xe[e] * inv), -kX16Max), kX16Max);
+            hi[e] = (x16[e] + 128) >> 8;
+            lo[e] = x16[e] - (hi[e] << 8);
+            ps += x16[e];
         }
-        uint4 w0, w1;  // [s][hi, lo] for s = 0..3: pair (e = s, e = s + 4)
-        w0.x = hb[0] | (hb[4] << 16); w0.y = lb[0] | (lb[4] << 16);
-        w0.z = hb[1] | (hb[5] << 16); w0.w = lb[1] | (lb[5] << 16);
-        w1.x = hb[2] | (hb[6] << 16); w1.y = lb[2] | (lb[6] << 16);
-        w1.z = hb[3] | (hb[7] << 16); w1.w = lb[3] | (lb[7] << 16);
+        uint4 w;  // hi of the even and odd elements, lo of the even and odd elements
+        w.x = pack_i8x4(hi[0], hi[2], hi[4], hi[6]);
+        w.y = pack_i8x4(hi[1], hi[3], hi[5], hi[7]);
+        w.z = pack_i8x4(lo[0], lo[2], lo[4], lo[6]);
+        w.w = pack_i8x4(lo[1], lo[3], lo[5], lo[7]);
         uint32_t *chunk = xw + r * rowpitch + (g / 4) * kChunkPitch;
-        uint4 *dst = reinterpret_cast<uint4 *>(chunk + (g % 4) * 8);
-        dst[0] = w0;
-        dst[1] = w1;
-        ps += dpp_f32<0xB1>(ps);  // the chunk's four lanes form an aligned quad
-        ps += dpp_f32<0x4E>(ps);
-        if (g % 4 == 0) reinterpret_cast<float *>(chunk)[32] = ps;
+        *reinterpret_cast<uint4 *>(chunk + (g % 4) * 4) = w;
+        ps += (int)dpp_u32<0xB1>((uint32_t)ps);
+        ps += (int)dpp_u32<0x4E>((uint32_t)ps);
+        if (g % 4 == 0) {
+            // step of x16 (a NaN step carries a non-finite input into every product)
+            chunk[16] = finite ? __float_as_uint(mx / kX16Max) : 0x7FC00000u;
+            chunk[17] = (uint32_t)(8 * ps);
+        }
     }
 }
 
@@ -430,16 +437,19 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
                 for (int r = 0; r < RM; r++) {
                     if (r < R) {
                         const float *px = xs + r * rowpitch + c * kChunkPitch;
-                        uint4 xv[8];
+                        uint4 xv[4];
 #pragma unroll
-                        for (int v = 0; v < 8; v++) xv[v] = *reinterpret_cast<const uint4 *>(px + 4 * v);
-                        const float sxo = kCodeOffset * px[32];
+                        for (int v = 0; v < 4; v++) xv[v] = *reinterpret_cast<const uint4 *>(px + 4 * v);
+                        const float2 sc2 = *reinterpret_cast<const float2 *>(px + 16);
+                        const float sx = sc2.x;                    // step of x16
+                        const int c8 = __float_as_int(sc2.y);     // 8 sum(x16)
 #pragma unroll
                         for (int f = 0; f < S::NF; f++)
 #pragma unroll
                             for (int m = 0; m < S::NM; m++) {
-                                acc[f][m][r] = fmaf(scc[f][m], dot32_bf16(qc[f][m], xv) - sxo, acc[f][m][r]);
-                                // one row at a time: keeps the bf16 pair temporaries of a single row live
+                                const int iv = dot32_i8(qc[f][m], xv) - c8;  // sum(q x16), exact
+                                acc[f][m][r] = fmaf(scc[f][m] * sx, (float)iv, acc[f][m][r]);
+                                // one row at a time: keeps the unpacked codes of a single row live
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                     }
