@@ -69,6 +69,12 @@ SMALL = [
              routed_scale=2.5),
     S.custom("onetok_noshared", hidden=256, n_experts=16, ffn=128, shared_ffn=0, top_k=4, tokens=1,
              top_p=0.9),
+    # one token, the other two combinations of top-p and a shared expert: which workgroup
+    # of the gate/up launch runs the whole selection and writes the routing out differs
+    S.custom("onetok_topp", hidden=512, n_experts=32, ffn=256, shared_ffn=256, top_k=4, tokens=1,
+             top_p=0.7, bias_amp=0.2),
+    S.custom("onetok_noshared_nop", hidden=256, n_experts=16, ffn=128, shared_ffn=0, top_k=4,
+             tokens=1, norm_topk=0),
     S.custom("twotok", hidden=2048, n_experts=64, ffn=512, shared_ffn=512, top_k=8, tokens=2,
              router_std=1 / 45.25),
     # few tokens with routed and shared FFN widths that split the down projection into two
