@@ -280,7 +280,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the expert FFNs' arithmetic: int8 x int8 dot products into int32 (decode GEMV,
+        # T <= 4) or bf16 matrix-core products into fp32 (T > 4); fp32 accumulation
+        "dtype": "i8" if T <= 4 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: {WORKLOADS[wl]}",
