@@ -126,6 +126,10 @@ int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32
 /* Step 4 ([R] §1.3, expert compute): for every row r < off[E] of the union, the
  * SwiGLU FFN of expert e(r) on token row_tok[r]:
  *   y_rows[r] = Wd_e (silu(Wg_e x) * (Wu_e x)),   fp32 accumulation, unweighted.
+ * The int4 codes enter the products exactly; the activations (x, and the SwiGLU
+ * output before the down projection) with 16 significant bits: for T <= 4 as 16-bit
+ * fixed point per 32 consecutive values (one rounding of at most max|x| / 65278 per
+ * value, exact int32 dot products), for larger T as bf16 hi + lo pairs.
  * Inputs n_uniq/uniq/off/row_tok as produced by moe_union (device).
  * Output: y_rows [T*k][H] fp32; rows past off[E] are left untouched. */
 int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,

@@ -5,9 +5,9 @@
 //
 // Work unit = (expert of the union or the shared expert, block of output rows).
 // The unit's token rows (at most RM at a time) are staged once per workgroup in
-// LDS as fp32; each weight row is streamed from HBM exactly once per RM rows,
-// with LPR lanes per row each issuing coalesced 16-byte loads of 32 codes, so a
-// wave's load covers LPR*16 contiguous bytes of one row.
+// LDS (16-bit fixed point, below); each weight row is streamed from HBM exactly once
+// per RM rows, with LPR lanes per row each issuing coalesced 16-byte loads of 32
+// codes, so a wave's load covers LPR*16 contiguous bytes of one row.
 //
 // Codes: a byte holds elements 2j (low nibble) and 2j+1 (high nibble) as
 // two's-complement int4 ("colibrì 深度拆解" §5.2).  XOR with 8 in every nibble turns
