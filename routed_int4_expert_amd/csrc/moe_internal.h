@@ -19,7 +19,7 @@ constexpr int kWave = 64;
 // Router logits are a [T][E] x [E][H]^T product in fp64, tiled 64 tokens x 64
 // experts per workgroup with a split over H so small batches still cover the chip.
 constexpr int kRouterTile = 64;
-constexpr int kRouterKC = 32;  // H elements staged per LDS step
+constexpr int kRouterKC = 64;  // H elements staged per LDS step
 constexpr int kRouterGemvTokens = 8;  // at most this many tokens: one wave per expert instead
 
 struct RouterSplit {

@@ -5,10 +5,10 @@
 // row once (lanes across H) and applies it to every token, accumulating in fp64
 // (fp32 x fp32 products are exact in fp64).
 // Logits, more tokens: each workgroup owns a 64-token x 64-expert tile and one
-// slice of H; fp32 tiles of x and Wr are staged through LDS and every thread
-// accumulates a 4x4 register micro-tile in fp64.  The per-slice partial sums go
-// to the workspace and are added, in slice order, by the selection kernel, so
-// the result does not depend on scheduling.
+// slice of H; fp32 tiles of x and Wr are staged through LDS and the fp64 matrix
+// cores accumulate their exact products.  The per-slice partial sums go to the
+// workspace and are added, in slice order, by the selection kernel, so the result
+// does not depend on scheduling.
 //
 // Selection: one wave per token.  Each lane holds up to four experts' sigmoid
 // and biased choice score in fp64; the k picks are k wave-wide argmax
@@ -45,61 +45,96 @@ RouterSplit router_split(int T, int E, int H) {
 }
 
 // ------------------------------------------------------------------ logits
-__global__ __launch_bounds__(256) void router_logits_kernel(LogitsArgs a) {
-    __shared__ float xs[kRouterKC][kRouterTile + 1];
-    __shared__ float wsh[kRouterKC][kRouterTile + 1];
-    const int tid = threadIdx.x;
+// More tokens: each workgroup owns a 64-token x 64-expert tile and one slice of H.
+// fp32 tiles of x and Wr (64 H values per step) are staged through two LDS buffers:
+// the next step's loads are issued before the current step's products, and one
+// barrier per step hands a buffer over.  The fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64) take the values converted to fp64 (exact) and accumulate
+// their exact products in fp64.
+// Wave w owns tokens 16w .. 16w+15 of the tile and all 64 experts (four 16x16 blocks).
+// Operand layouts: A (tokens x K) lane l holds [l % 16][l / 16], B (K x experts) lane
+// l holds [l / 16][l % 16]; register v of lane l holds the result's row l / 16 + 4v,
+// column l % 16 (rows interleaved across the lane groups, unlike the fp32 16x16 layouts).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// loader mapping: 64 rows x 64 columns = 1024 float4 per operand, 4 per thread
+constexpr int kRouterLoads = kRouterTile * kRouterKC / 4 / 256;
+
+struct RouterStage {
+    float4 x[kRouterLoads], w[kRouterLoads];
+};
+
+__device__ __forceinline__ void router_stage_load(const LogitsArgs &a, int t0, int e0, int h0,
+                                                  RouterStage &r) {
+#pragma unroll
+    for (int rep = 0; rep < kRouterLoads; rep++) {
+        const int idx = threadIdx.x + rep * 256;
+        const int row = idx / (kRouterKC / 4), c4 = (idx % (kRouterKC / 4)) * 4;
+        const int t = t0 + row, e = e0 + row;
+        r.x[rep] = make_float4(0.f, 0.f, 0.f, 0.f);
+        r.w[rep] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < a.T) r.x[rep] = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h0 + c4);
+        if (e < a.E) r.w[rep] = *reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.H + h0 + c4);
+    }
+}
+
+__device__ __forceinline__ void router_stage_store(const RouterStage &r,
+                                                   float (*xs)[kRouterTile + 1],
+                                                   float (*wsh)[kRouterTile + 1]) {
+#pragma unroll
+    for (int rep = 0; rep < kRouterLoads; rep++) {
+        const int idx = threadIdx.x + rep * 256;
+        const int row = idx / (kRouterKC / 4), c4 = (idx % (kRouterKC / 4)) * 4;
+        xs[c4 + 0][row] = r.x[rep].x; xs[c4 + 1][row] = r.x[rep].y;
+        xs[c4 + 2][row] = r.x[rep].z; xs[c4 + 3][row] = r.x[rep].w;
+        wsh[c4 + 0][row] = r.w[rep].x; wsh[c4 + 1][row] = r.w[rep].y;
+        wsh[c4 + 2][row] = r.w[rep].z; wsh[c4 + 3][row] = r.w[rep].w;
+    }
+}
+
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(LogitsArgs a) {
+    __shared__ float xs[2][kRouterKC][kRouterTile + 1];
+    __shared__ float wsh[2][kRouterKC][kRouterTile + 1];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     const int t0 = blockIdx.x * kRouterTile;
     const int e0 = blockIdx.y * kRouterTile;
     const int s = blockIdx.z;
     const int h_begin = s * a.kslice;
     const int h_end = min(a.H, h_begin + a.kslice);
-    const int ty = tid / 16, tx = tid % 16;
-
-    double acc[4][4];
+    f64x4_t acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = 0.0;
-
-    // loader mapping: 64 rows x 32 columns = 512 float4 per operand, 2 per thread
+    for (int b = 0; b < 4; b++) acc[b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    RouterStage r;
+    router_stage_load(a, t0, e0, h_begin, r);
+    router_stage_store(r, xs[0], wsh[0]);
+    __syncthreads();
+    int cur = 0;
     for (int h0 = h_begin; h0 < h_end; h0 += kRouterKC) {
+        const bool more = h0 + kRouterKC < h_end;
+        if (more) router_stage_load(a, t0, e0, h0 + kRouterKC, r);
 #pragma unroll
-        for (int rep = 0; rep < 2; rep++) {
-            const int idx = tid + rep * 256;   // 0..511
-            const int row = idx / 8;            // tile row 0..63
-            const int c4 = (idx % 8) * 4;       // column 0,4,...,28
-            float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
-            float4 vw = make_float4(0.f, 0.f, 0.f, 0.f);
-            const int t = t0 + row, e = e0 + row;
-            if (t < a.T) vx = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h0 + c4);
-            if (e < a.E) vw = *reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.H + h0 + c4);
-            xs[c4 + 0][row] = vx.x; xs[c4 + 1][row] = vx.y; xs[c4 + 2][row] = vx.z; xs[c4 + 3][row] = vx.w;
-            wsh[c4 + 0][row] = vw.x; wsh[c4 + 1][row] = vw.y; wsh[c4 + 2][row] = vw.z; wsh[c4 + 3][row] = vw.w;
+        for (int kk = 0; kk < kRouterKC; kk += 4) {
+            const int k = kk + lane / 16, i = lane % 16;
+            const double av = (double)xs[cur][k][16 * wv + i];
+            double bv[4];
+#pragma unroll
+            for (int b = 0; b < 4; b++) bv[b] = (double)wsh[cur][k][16 * b + i];
+#pragma unroll
+            for (int b = 0; b < 4; b++) acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv[b], acc[b], 0, 0, 0);
         }
+        // the other buffer was last read before the previous barrier
+        if (more) router_stage_store(r, xs[cur ^ 1], wsh[cur ^ 1]);
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < kRouterKC; kk++) {
-            double xv[4], wv[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) xv[i] = (double)xs[kk][ty + 16 * i];
-#pragma unroll
-            for (int j = 0; j < 4; j++) wv[j] = (double)wsh[kk][tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = fma(xv[i], wv[j], acc[i][j]);
-        }
-        __syncthreads();
+        cur ^= 1;
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int t = t0 + ty + 16 * i;
-        if (t >= a.T) continue;
+    for (int b = 0; b < 4; b++) {
+        const int e = e0 + 16 * b + lane % 16;
+        if (e >= a.E) continue;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int e = e0 + tx + 16 * j;
-            if (e < a.E) a.part[((size_t)s * a.T + t) * a.E + e] = acc[i][j];
+        for (int v = 0; v < 4; v++) {
+            const int t = t0 + 16 * wv + (lane / 16) + 4 * v;
+            if (t < a.T) a.part[((size_t)s * a.T + t) * a.E + e] = acc[b][v];
         }
     }
 }
@@ -121,7 +156,7 @@ hipError_t launch_router_logits(const LogitsArgs &a, int S, hipStream_t st) {
         return hipGetLastError();
     }
     dim3 grid((a.T + kRouterTile - 1) / kRouterTile, (a.E + kRouterTile - 1) / kRouterTile, S);
-    router_logits_kernel<<<grid, 256, 0, st>>>(a);
+    router_logits_mfma_kernel<<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
