@@ -4,18 +4,23 @@
 // each expert's weights read once for all rows routed to it; §1.4: the shared
 // expert on every token).
 //
-// D[rows][outputs] = X[rows][K] * W[outputs][K]^T with v_mfma_f32_16x16x32_bf16.
+// D[rows][outputs] = X[rows][K] * W[outputs][K]^T with v_mfma_i32_16x16x64_i8.
 //  - B (weights): for one 64-group of one output row, lane (column j, part p)
-//    holds words 2p and 2p+1 (8 bytes, 16 codes).  Each 32-bit word of 8 codes
-//    becomes 4 bf16 pairs of (136 + q) by one bit operation per pair (0x4300 is
-//    128.0; q XOR 8 = q + 8), so the codes enter the matrix core exactly
-//    ("colibrì 深度拆解" §5.2 packing).  Word 2p+ks feeds K-step ks.
-//  - A (activations): prepared once as bf16 hi + lo (16 significant bits) in
-//    the codes' element order (per word: elements 0,4,1,5,2,6,3,7), 256 bytes
-//    per row and group; hi and lo are two MFMAs on the same B.
-//  - per 64-group ("colibri 开发演进实录" §2.1 gs64) the group accumulator
-//    starts at -136 * sum(x) (the unsigned-offset identity of §2.2, K1) and its
-//    result is scaled by the fp32 group scale into the fp32 running sum.
+//    holds words 2p and 2p+1 (8 bytes, 16 codes).  A code nibble masked in the
+//    high half of its byte is 16 q as a signed byte: the odd elements of a word
+//    are w AND 0xF0F0F0F0, the even ones (w << 4) AND 0xF0F0F0F0, so the codes
+//    enter the matrix core exactly ("colibrì 深度拆解" §5.2 packing).
+//  - A (activations): prepared once per row and 256-element K chunk as 16-bit
+//    fixed point, x16 = rint(x * 32639 / max|x|), split into signed bytes
+//    x16 = 256 hi + lo (the unsigned-offset and split identities of
+//    "colibri 开发演进实录" §2.2, K1, with the offset removed by the sign-carrying
+//    codes), in the codes' element order (per word: 0,2,4,6 then 1,3,5,7),
+//    128 bytes per row and group; hi and lo are two MFMAs on the same B, each an
+//    exact int32 sum.
+//  - per 64-group ("colibri 开发演进实录" §2.1 gs64) 256 hi + lo is converted to
+//    fp32 and scaled by the group scale into the chunk's sum, which the row's
+//    chunk step (max|x| / 32639, over 16 for the codes' factor) scales into the
+//    fp32 running sum.  The one rounding of x is x16 itself.
 //
 // Work item = up to 16 rows of one expert (one 16-row MFMA block) x a block of
 // outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
@@ -36,87 +41,93 @@
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kPairOffset = 0x43084308u;   // bf16 pair (136 + q) from a code pair
-constexpr float kMfmaCodeOffset = 136.0f;
-constexpr int kGroupBytes = 256;                // one row's 64-group: 8 x 16 B hi, then 8 x 16 B lo
+constexpr uint32_t kHighNibbles = 0xF0F0F0F0u;  // 16 q per byte
+constexpr float kX16Max = 32639.0f;             // 127 * 256 + 127: hi and lo stay signed bytes
+constexpr int kGroupBytes = 128;                // one row's 64-group: 4 x 16 B hi, then 4 x 16 B lo
 constexpr int kCG = 4;                          // groups per K chunk
-constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 1 KB, one wave-wide LDS copy
+constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 512 B
 constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
 constexpr int kTileBytes = kMfmaItemRows * kRowPitch;
 // a column set's weight codes of one chunk in LDS: 4 B blocks x 16 rows x 128 B, rows
 // 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
 constexpr int kCodePitch = 144;
 
-__device__ __forceinline__ uint32_t bf16_rne_u(float f) {
-    const uint32_t b = __float_as_uint(f);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 // ------------------------------------------------------------------ prep
-// Rows of K fp32 values -> per 64-group G: 256 bytes, word w (elements
-// 64G + 8w .. +7) as 8 bf16 hi at 16w and 8 bf16 lo at 128 + 16w, elements in
-// the order 0,4,1,5,2,6,3,7; and nsx[row][G] = -136 * sum of (hi + lo) over the
-// group.  Rows are NGp groups long (whole chunks).  One thread per word; the 8
-// words of a group are 8 adjacent lanes.
+// Rows of K fp32 values -> per 256-element chunk c: step[row][c] = max|x| / 32639
+// (NaN if the chunk holds a non-finite value, 0 if it is all zero) and, per 64-group
+// G, 128 bytes: for word w (elements 64G + 8w .. +7) the hi bytes of its even
+// elements (0,2,4,6) and of its odd ones at 8w, the lo bytes likewise at 64 + 8w.
+// Rows are NGp groups long (whole chunks).  One thread per word, the 32 words of a
+// chunk in 32 adjacent lanes (threads of words past K write nothing).
 struct PrepJob {
     const float *src;
     int rows, K;
     uint8_t *frag;
-    float *nsx;
+    float *step;
     int blocks;  // workgroups of 256 threads this job takes
 };
 
-__device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
-    const float *src = j.src;
-    const int rows = j.rows, K = j.K;
-    const long i = (long)blk * blockDim.x + threadIdx.x;  // word index
-    const long nwd = (long)rows * (K / 8);
-    const bool live = i < nwd;
-    const long ii = live ? i : nwd - 1;
-    const int row = (int)(ii / (K / 8)), b = (int)(ii % (K / 8));
-    const int NGp = mfma_groups_padded(K);
-    const float4 *p = reinterpret_cast<const float4 *>(src + (size_t)row * K + 8 * b);
-    const float4 v0 = p[0], v1 = p[1];
-    const float e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const int ord[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    uint32_t hb[8], lb[8];
-    float part = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-        const float x = e[ord[s]];
-        hb[s] = bf16_rne_u(x);
-        const float hi = __uint_as_float(hb[s] << 16);
-        lb[s] = bf16_rne_u(x - hi);
-        part += hi + __uint_as_float(lb[s] << 16);
-    }
-    const int G = b / 8, w = b % 8;
-    uint8_t *grp = j.frag + ((size_t)row * NGp + G) * kGroupBytes;
-    if (live) {
-        *reinterpret_cast<uint4 *>(grp + 16 * w) =
-            make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                       hb[6] | (hb[7] << 16));
-        *reinterpret_cast<uint4 *>(grp + 128 + 16 * w) =
-            make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                       lb[6] | (lb[7] << 16));
-    }
-    // group sum over the 8 words = 8 adjacent lanes (K is a multiple of 64)
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) part += __shfl_xor(part, m, kWave);
-    if (live && w == 0) j.nsx[(size_t)row * NGp + G] = -kMfmaCodeOffset * part;
+__device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)d << 24);
 }
 
-static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *nsx) {
+__device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
+    const int rows = j.rows, K = j.K;
+    const int NGp = mfma_groups_padded(K), NC = NGp / kCG;
+    const long i = (long)blk * blockDim.x + threadIdx.x;  // (row, chunk, word of the chunk)
+    const long n = (long)rows * NC * 32;
+    const bool in_rows = i < n;
+    const long ii = in_rows ? i : n - 1;
+    const int row = (int)(ii / (NC * 32)), c = (int)(ii / 32 % NC), w = (int)(ii % 32);
+    const int b = 32 * c + w;  // word of the row
+    const bool live = in_rows && b < K / 8;
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        const float4 *p = reinterpret_cast<const float4 *>(j.src + (size_t)row * K + 8 * b);
+        const float4 v0 = p[0], v1 = p[1];
+        e[0] = v0.x; e[1] = v0.y; e[2] = v0.z; e[3] = v0.w;
+        e[4] = v1.x; e[5] = v1.y; e[6] = v1.z; e[7] = v1.w;
+    }
+    // the chunk's largest magnitude as bits (an integer max, so NaN and Inf count)
+    uint32_t mb = 0;
+#pragma unroll
+    for (int s = 0; s < 8; s++) mb = max(mb, __float_as_uint(e[s]) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, m, kWave));
+    const bool finite = mb < 0x7F800000u;
+    const float mx = __uint_as_float(mb);
+    const float r = finite && mb ? kX16Max / mx : 0.0f;
+    int hi[8], lo[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+        const int x16 = (int)rintf(e[s] * r);
+        hi[s] = (x16 + 128) >> 8;
+        lo[s] = x16 - 256 * hi[s];
+    }
+    if (live) {
+        const int G = b / 8, wg = b % 8;
+        uint8_t *grp = j.frag + ((size_t)row * NGp + G) * kGroupBytes;
+        *reinterpret_cast<uint2 *>(grp + 8 * wg) =
+            make_uint2(pack_bytes(hi[0], hi[2], hi[4], hi[6]), pack_bytes(hi[1], hi[3], hi[5], hi[7]));
+        *reinterpret_cast<uint2 *>(grp + 64 + 8 * wg) =
+            make_uint2(pack_bytes(lo[0], lo[2], lo[4], lo[6]), pack_bytes(lo[1], lo[3], lo[5], lo[7]));
+    }
+    if (in_rows && w == 0) j.step[(size_t)row * NC + c] = finite ? mx / kX16Max : __builtin_nanf("");
+}
+
+static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step) {
     PrepJob j;
     j.src = src;
     j.rows = rows;
     j.K = K;
     j.frag = frag;
-    j.nsx = nsx;
-    const long nwd = rows > 0 ? (long)rows * (K / 8) : 0;
+    j.step = step;
+    const long nwd = rows > 0 ? (long)rows * (mfma_groups_padded(K) / kCG) * 32 : 0;
     j.blocks = (int)((nwd + 255) / 256);
     return j;
 }
@@ -234,14 +245,15 @@ static hipError_t launch_prep(const PrepJob &j0, const PrepJob &j1, const ItemsJ
 }
 
 // ------------------------------------------------------------------ grouped GEMM
-__device__ __forceinline__ bf16x8_t code_pairs(uint32_t w) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 v;
-    v.x = (w & 0x000F000Fu) ^ kPairOffset;
-    v.y = ((w >> 4) & 0x000F000Fu) ^ kPairOffset;
-    v.z = ((w >> 8) & 0x000F000Fu) ^ kPairOffset;
-    v.w = ((w >> 12) & 0x000F000Fu) ^ kPairOffset;
-    return __builtin_bit_cast(bf16x8_t, v);
+// 16 codes (two words) of one output row -> the 16 signed bytes 16 q of a B operand:
+// per word its even elements, then its odd ones.
+__device__ __forceinline__ i32x4_t code_bytes(uint2 w) {
+    i32x4_t v;
+    v.x = (int)((w.x << 4) & kHighNibbles);
+    v.y = (int)(w.x & kHighNibbles);
+    v.z = (int)((w.y << 4) & kHighNibbles);
+    v.w = (int)(w.y & kHighNibbles);
+    return v;
 }
 
 // The LDS writes of this wave are done; meet the other waves.  Written out so
@@ -266,8 +278,8 @@ constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);
 constexpr int kLoadThreads = kWave * kLoadWaves;                // 256: one per weight row of a chunk
 constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
 constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
-constexpr int kBufAct = kTileBytes;                            // [16 rows][1040 B]
-constexpr int kBufNs = kMfmaItemRows * 4 * 4;                  // [4 groups][16 rows] fp32
+constexpr int kBufAct = kTileBytes;                            // [16 rows][528 B]
+constexpr int kBufNs = kMfmaItemRows * 4;                      // [16 rows] fp32 chunk steps
 constexpr int kBufBytes = kBufCodes + kBufScales + kBufAct + kBufNs;
 constexpr int kMaxWorkPerWg = 64;
 
@@ -289,11 +301,13 @@ __device__ __forceinline__ int load_row_output(int r, int nb0, bool &second) {
     return GU ? nb0 + 32 * wv + (bb % 2) * 16 + jj : nb0 + 64 * wv + 16 * bb + jj;
 }
 
+constexpr int kActLoads = kMfmaItemRows * kChunkBytes / 16 / kLoadThreads;  // 16-byte loads per thread
+
 struct ChunkRegs {
     u32x4_t q[8];
     float s[4];
-    uint4 a[4];
-    uint4 n;
+    uint4 a[kActLoads];
+    float n;
 };
 
 template <bool GU>
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         // an up row for odd i (gate/up), whatever the lane; so is scale column sc_col(i).
         int pk = -1;
         const uint8_t *qb0 = nullptr, *qb1 = nullptr, *abase = nullptr;
-        const float *sb0 = nullptr, *sb1 = nullptr, *nbase = nullptr;
+        const float *sb0 = nullptr, *sb1 = nullptr, *nbase = nullptr;  // nbase: chunk steps
         uint32_t qo[8], so[4], no = 0;
         const uint8_t *arow = nullptr;  // 64-bit: union rows x fragment bytes can pass 2^32
         uint32_t qlast = 0;
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                     qb1 = a.sh_up.q;   sb1 = a.sh_up.s;
                 }
                 abase = a.x_frag;
-                nbase = a.x_nsx;
+                nbase = a.x_step;
             } else {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
@@ -386,11 +400,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                     const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
                     qb0 = a.down.q + dq; sb0 = a.down.s + ds;
                     abase = a.hr_frag;
-                    nbase = a.hr_nsx;
+                    nbase = a.hr_step;
                 } else {
                     qb0 = a.sh_down.q; sb0 = a.sh_down.s;
                     abase = a.hs_frag;
-                    nbase = a.hs_nsx;
+                    nbase = a.hs_step;
                 }
                 qb1 = qb0;
                 sb1 = sb0;
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 so[i] = (uint32_t)n * (uint32_t)NG;
             }
             arow = abase + (size_t)d.srow[t / 16] * NGp * kGroupBytes + 16 * (t % 16);
-            no = (uint32_t)d.srow[t % kMfmaItemRows] * (uint32_t)NGp;  // (only lanes t < 16 store it)
+            no = (uint32_t)d.srow[t % kMfmaItemRows] * (uint32_t)(NGp / kCG);  // (only lanes t < 16 store it)
             pk = k;
         };
         auto load = [&](ChunkRegs &v) __attribute__((always_inline)) {
@@ -423,10 +437,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const uint32_t sg = (uint32_t)min(kCG * c + t % 4, NG - 1);
 #pragma unroll
             for (int i = 0; i < 4; i++) v.s[i] = ((i & 1) ? sb1 : sb0)[so[i] + sg];
-            const uint8_t *ac = arow + (uint32_t)(kCG * c * kGroupBytes);
+            const uint8_t *ac = arow + (uint32_t)(c * kChunkBytes);
 #pragma unroll
-            for (int i = 0; i < 4; i++) v.a[i] = *reinterpret_cast<const uint4 *>(ac + 256 * i);
-            v.n = *reinterpret_cast<const uint4 *>(nbase + (no + kCG * c));
+            for (int i = 0; i < kActLoads; i++) v.a[i] = *reinterpret_cast<const uint4 *>(ac + 256 * i);
+            v.n = nbase[no + c];
             // advance; past the last chunk the head stays there (that chunk is loaded again)
             int nk = lk, nc = lc + 1;
             if (nc >= work[nk].nch) {
@@ -450,15 +464,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * sc_col(i) + t % 4] = v.s[i];
             const int ar = t / 16;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < kActLoads; i++)
                 *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * i)) = v.a[i];
-            if (t < kMfmaItemRows) {  // transposed, [group][row]: a lane's four rows of a group are one read
-                float *nsb = reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct);
-                nsb[0 * kMfmaItemRows + t] = __uint_as_float(v.n.x);
-                nsb[1 * kMfmaItemRows + t] = __uint_as_float(v.n.y);
-                nsb[2 * kMfmaItemRows + t] = __uint_as_float(v.n.z);
-                nsb[3 * kMfmaItemRows + t] = __uint_as_float(v.n.w);
-            }
+            if (t < kMfmaItemRows)  // a lane's four rows' steps are one read
+                reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct)[t] = v.n;
         };
         ChunkRegs r0, r1, r2;
         if (S > 0) {
@@ -533,21 +542,23 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const uint8_t *cw = B + cs * 64 * kCodePitch;
             const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
             const uint8_t *tile = B + kBufCodes + kBufScales;
-            const float *nst = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
-            // the chunk's group scales of this lane's four columns and the -136 sum(x) start
-            // values of its rows (one 16-byte read per group); then the groups, with the
-            // next group's code words and A fragments read before this group's products
-            f32x4_t sc4[4], ga4[kCG];
+            const float *stp = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
+            // the chunk's group scales of this lane's four columns and the steps of its
+            // four rows; then the groups, with the next group's code words and A fragments
+            // read before this group's products
+            f32x4_t sc4[4], csum[4];
 #pragma unroll
-            for (int b = 0; b < 4; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
-#pragma unroll
-            for (int gi = 0; gi < kCG; gi++) ga4[gi] = *reinterpret_cast<const f32x4_t *>(nst + gi * kMfmaItemRows + 4 * p);
-            // Per group: issue its 16 MFMAs, then (while they run) read and convert the next
+            for (int b = 0; b < 4; b++) {
+                sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
+                csum[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            const f32x4_t st4 = *reinterpret_cast<const f32x4_t *>(stp + 4 * p);
+            // Per group: issue its 8 MFMAs, then (while they run) read and convert the next
             // group's operands, then scale-accumulate this group's results.  Scheduling
             // barriers keep that order, so the conversion overlaps the matrix pipe.
             struct Opnd {
-                bf16x8_t bo[2][4];  // [ks][block] code pairs
-                bf16x8_t a[2][2];   // [ks][hi, lo]
+                i32x4_t bo[4];  // [block] 16 q bytes
+                i32x4_t a[2];   // hi, lo
             };
             auto read_group = [&](int gi) __attribute__((always_inline)) {
                 Opnd o;
@@ -555,31 +566,23 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int b = 0; b < 4; b++)
                     w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
+                const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * p;
+                o.a[0] = *reinterpret_cast<const i32x4_t *>(ar);
+                o.a[1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) {
-                    const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * (2 * p + ks);
-                    o.a[ks][0] = *reinterpret_cast<const bf16x8_t *>(ar);
-                    o.a[ks][1] = *reinterpret_cast<const bf16x8_t *>(ar + 128);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                    for (int b = 0; b < 4; b++) o.bo[ks][b] = code_pairs(ks ? w[b].y : w[b].x);
+                for (int b = 0; b < 4; b++) o.bo[b] = code_bytes(w[b]);
                 return o;
             };
+            const i32x4_t zero = {0, 0, 0, 0};
             Opnd cur = read_group(0);
 #pragma unroll
             for (int gi = 0; gi < kCG; gi++) {
                 if (gi >= ng) break;
-                f32x4_t gacc[4];
+                i32x4_t gh[4], gl[4];
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) {
+                for (int b = 0; b < 4; b++) gh[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[0], cur.bo[b], zero, 0, 0, 0);
 #pragma unroll
-                    for (int b = 0; b < 4; b++)
-                        gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[ks][0], cur.bo[ks][b], ks ? gacc[b] : ga4[gi], 0, 0, 0);
-#pragma unroll
-                    for (int b = 0; b < 4; b++) gacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[ks][1], cur.bo[ks][b], gacc[b], 0, 0, 0);
-                }
+                for (int b = 0; b < 4; b++) gl[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[1], cur.bo[b], zero, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 Opnd nxt;
                 if (gi + 1 < kCG) nxt = read_group(min(gi + 1, ng - 1));
@@ -587,9 +590,15 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int b = 0; b < 4; b++)
 #pragma unroll
-                    for (int v = 0; v < 4; v++) acc[b][v] = fmaf(sc4[b][gi], gacc[b][v], acc[b][v]);
+                    for (int v = 0; v < 4; v++)
+                        csum[b][v] = fmaf(sc4[b][gi], (float)(gh[b][v] * 256 + gl[b][v]), csum[b][v]);
                 if (gi + 1 < kCG) cur = nxt;
             }
+            // the chunk's sums times the row steps (over 16: the codes entered as 16 q)
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[b][v] = fmaf(csum[b][v], st4[v] * 0.0625f, acc[b][v]);
             if (++cc >= d.nch) {
                 epilogue(ck);
                 cc = 0;
@@ -647,7 +656,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     it.n_items = a.n_items;
     it.with_union = a.union_in_prep;
     it.uni = a.uni;
-    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_nsx), none, it, "prep_x+items", st);
+    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
     if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
@@ -656,8 +665,8 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     ItemsJob no_items = it;
     no_items.items = nullptr;
     no_items.with_union = 0;
-    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_nsx) : none,
-                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_nsx) : none,
+    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step) : none,
+                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step) : none,
                     no_items, "prep_h", st);
     if (e != hipSuccess) return e;
     return launch_gemm<false>(a, shared_items, "ffn_down_mfma", st);

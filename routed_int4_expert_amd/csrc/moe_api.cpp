@@ -147,12 +147,13 @@ Plan make_plan(const moe_layer &L, int T) {
         // fragment rows padded to whole 4-group chunks
         const size_t gh = mfma_groups_padded((int)H), gf = mfma_groups_padded((int)F),
                      gs = Fs ? mfma_groups_padded((int)Fs) : 0;
-        p.x_frag = take(Tz * gh * 256);
-        p.x_nsx = take(Tz * gh * 4);
-        p.hr_frag = take(Tz * k * gf * 256);
-        p.hr_nsx = take(Tz * k * gf * 4);
-        p.hs_frag = take(Tz * gs * 256);
-        p.hs_nsx = take(Tz * gs * 4);
+        // (128 bytes per row and group; one fp32 step per row and 4-group chunk)
+        p.x_frag = take(Tz * gh * 128);
+        p.x_step = take(Tz * gh);
+        p.hr_frag = take(Tz * k * gf * 128);
+        p.hr_step = take(Tz * k * gf);
+        p.hs_frag = take(Tz * gs * 128);
+        p.hs_step = take(Tz * gs);
         p.max_items = mfma_max_items(p.max_units, (int)(Tz * k));
         p.items = take((size_t)p.max_items * 16);
         p.n_items = take(4);
@@ -237,7 +238,7 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     MfmaArgs m;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
-    m.x_nsx = at<float>(ws, p.x_nsx);
+    m.x_step = at<float>(ws, p.x_step);
     m.items = at<int32_t>(ws, p.items);
     m.n_items = at<int32_t>(ws, p.n_items);
     m.n_uniq = f.n_uniq;
@@ -254,8 +255,8 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     m.h_shared = f.h_shared;
     m.hr_frag = at<uint8_t>(ws, p.hr_frag);
     m.hs_frag = at<uint8_t>(ws, p.hs_frag);
-    m.hr_nsx = at<float>(ws, p.hr_nsx);
-    m.hs_nsx = at<float>(ws, p.hs_nsx);
+    m.hr_step = at<float>(ws, p.hr_step);
+    m.hs_step = at<float>(ws, p.hs_step);
     m.y_routed = f.y_routed;
     m.y_shared = f.y_shared;
     m.T = f.T;

@@ -41,7 +41,7 @@ struct Plan {
     size_t h_shared;  // fp32 [T][Fs]
     size_t y_routed;  // fp32 [T*k][H]  unweighted expert outputs per routed row
     size_t y_shared;  // fp32 [T][H]
-    size_t x_frag, x_nsx, hr_frag, hr_nsx, hs_frag, hs_nsx;  // matrix-core path (T > kGemvMaxTokens)
+    size_t x_frag, x_step, hr_frag, hr_step, hs_frag, hs_step;  // matrix-core path (T > kGemvMaxTokens)
     size_t items, n_items;  // matrix-core work list
     int max_items;
     size_t total;
@@ -122,14 +122,15 @@ __host__ __device__ inline size_t select_lds_words(int E, int T, int k) {
 }
 
 // The matrix-core path (more than kGemvMaxTokens tokens): FfnArgs plus the
-// activations prepared in MFMA fragment order (bf16 hi/lo, 256 bytes per row and
-// 64-group) with their per-group sums.
+// activations prepared in MFMA fragment order (16-bit fixed point as hi and lo
+// signed bytes, 128 bytes per row and 64-group) with one step per row and
+// 4-group chunk.
 constexpr int kGemvMaxTokens = 4;
 
 struct MfmaArgs {
     const float *x;                  // [T][H]
-    uint8_t *x_frag;                 // [T][NGp(H)][256]
-    float *x_nsx;                    // [T][NGp(H)]  -136 * group sum
+    uint8_t *x_frag;                 // [T][NGp(H)][128]
+    float *x_step;                   // [T][NGp(H) / 4]  max|x| / 32639 per chunk
     const int32_t *n_uniq, *uniq, *off, *row_tok;
     int32_t *items;                  // [max_items][4]: expert, first row, rows, 0
     int32_t *n_items;
@@ -137,7 +138,7 @@ struct MfmaArgs {
     moe_q4 sh_gate, sh_up, sh_down;
     float *h_routed, *h_shared;      // [rows][F], [T][Fs]
     uint8_t *hr_frag, *hs_frag;      // h in fragment order
-    float *hr_nsx, *hs_nsx;
+    float *hr_step, *hs_step;
     float *y_routed, *y_shared;      // [rows][H], [T][H]
     int T, H, F, Fs, E, max_units, max_rows, max_items;
     int with_routed, with_shared;
