@@ -22,19 +22,22 @@
 //    chunk step (max|x| / 32639, over 16 for the codes' factor) scales into the
 //    fp32 running sum.  The one rounding of x is x16 itself.
 //
-// Work item = up to 16 rows of one expert (one 16-row MFMA block) x a block of
+// Work item = up to 32 rows of one expert (two 16-row MFMA blocks) x a block of
 // outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
 // outputs (down).  Experts with more rows, and the shared expert, span several
 // items.  The kernel is persistent (one workgroup of 8 waves per CU, looping over
 // (item, output block) pairs) and splits loading from computing: 4 loader waves keep
 // three 4-group K chunks in flight in registers and place each one in one of two LDS
 // buffers (codes regrouped for the operand reads, scales, the activation tile and the
-// group start values); 4 compute waves, one per column set, run the MFMAs on the
+// rows' chunk steps); 4 compute waves, one per column set, run the MFMAs on the
 // other buffer, issuing a group's MFMAs before converting the next group's codes so
-// that the conversion overlaps the matrix pipe.  One barrier per chunk.  Every
-// output has one owner: the result is deterministic.
+// that the conversion overlaps the matrix pipe; the converted codes serve both row
+// blocks of an item.  One barrier per chunk.  Every output has one owner: the result
+// is deterministic.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "moe_internal.h"
 #include "select_union.h"
@@ -51,7 +54,6 @@ constexpr int kGroupBytes = 128;                // one row's 64-group: 4 x 16 B 
 constexpr int kCG = 4;                          // groups per K chunk
 constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 512 B
 constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
-constexpr int kTileBytes = kMfmaItemRows * kRowPitch;
 // a column set's weight codes of one chunk in LDS: 4 B blocks x 16 rows x 128 B, rows
 // 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
 constexpr int kCodePitch = 144;
@@ -133,11 +135,11 @@ static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float 
 }
 
 // ------------------------------------------------------------------ work list
-// Items in union order: expert uniq[u] with c rows gets ceil(c / 16) items of
+// Items in union order: expert uniq[u] with c rows gets ceil(c / IR) items of
 // consecutive rows.  One workgroup of 256 threads, one thread per union slot
 // (E <= 256); an exclusive scan of the item counts places each expert's items.
 __device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int32_t *uniq,
-                                                const int32_t *off, int E, int32_t *items,
+                                                const int32_t *off, int E, int IR, int32_t *items,
                                                 int32_t *n_items) {
     __shared__ int wsum[256 / kWave];
     const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
@@ -147,7 +149,7 @@ __device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int
         e = uniq[u];
         cnt = off[e + 1] - off[e];
     }
-    const int ni = (cnt + kMfmaItemRows - 1) / kMfmaItemRows;
+    const int ni = (cnt + IR - 1) / IR;
     int inc = ni;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -161,8 +163,8 @@ __device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int
     for (int i = 0; i < ni; i++) {
         int32_t *it = items + 4 * (base + i);
         it[0] = e;
-        it[1] = off[e] + kMfmaItemRows * i;
-        it[2] = min(kMfmaItemRows, cnt - kMfmaItemRows * i);
+        it[1] = off[e] + IR * i;
+        it[2] = min(IR, cnt - IR * i);
         it[3] = 0;
     }
     if (u == blockDim.x - 1) n_items[0] = base + ni;
@@ -174,6 +176,7 @@ __device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int
 struct ItemsJob {
     const int32_t *n_uniq, *uniq, *off;
     int E;
+    int item_rows;  // IR: rows per item
     int32_t *items, *n_items;
     int with_union;  // build the union first (uni), in this workgroup
     UnionArgs uni;
@@ -182,11 +185,11 @@ struct ItemsJob {
 // The work list from the union's per-expert counts and offsets in LDS (union_block's
 // layout): the same items, in the same (increasing expert) order, as mfma_items_body.
 __device__ __forceinline__ void mfma_items_from_counts(const int32_t *cnt, const int32_t *offs, int E,
-                                                       int32_t *items, int32_t *n_items) {
+                                                       int IR, int32_t *items, int32_t *n_items) {
     __shared__ int wsum[256 / kWave];
     const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
     const int c = u < E ? cnt[u] : 0;
-    const int ni = (c + kMfmaItemRows - 1) / kMfmaItemRows;
+    const int ni = (c + IR - 1) / IR;
     int inc = ni;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -200,8 +203,8 @@ __device__ __forceinline__ void mfma_items_from_counts(const int32_t *cnt, const
     for (int i = 0; i < ni; i++) {
         int32_t *it = items + 4 * (base + i);
         it[0] = u;
-        it[1] = offs[u] + kMfmaItemRows * i;
-        it[2] = min(kMfmaItemRows, c - kMfmaItemRows * i);
+        it[1] = offs[u] + IR * i;
+        it[2] = min(IR, c - IR * i);
         it[3] = 0;
     }
     if (u == blockDim.x - 1) n_items[0] = base + ni;
@@ -221,9 +224,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepJob j0, PrepJob j1, Items
             __syncthreads();
             const int E = it.uni.E, W = (it.uni.T + 31) / 32, W8 = (W + 7) / 8;
             const int32_t *cnt = reinterpret_cast<const int32_t *>(prep_lds + (size_t)E * W + (size_t)E * W8);
-            mfma_items_from_counts(cnt, cnt + E, E, it.items, it.n_items);
+            mfma_items_from_counts(cnt, cnt + E, E, it.item_rows, it.items, it.n_items);
         } else {
-            mfma_items_body(it.n_uniq, it.uniq, it.off, it.E, it.items, it.n_items);
+            mfma_items_body(it.n_uniq, it.uniq, it.off, it.E, it.item_rows, it.items, it.n_items);
         }
     }
 }
@@ -263,7 +266,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Persistent grouped GEMM.  A workgroup of eight waves runs per CU and loops over work
-// items (16-row item, output block) wi = blockIdx.x + k * gridDim.x.  Waves 0-3
+// items (32-row item, output block) wi = blockIdx.x + k * gridDim.x.  Waves 0-3
 // compute, waves 4-7 load.  For each 4-group K chunk the loaders place, in one of two
 // LDS buffers, the chunk's weight codes (regrouped so that a compute lane's operand
 // words are one 8-byte read), its group scales and its activation tile; the compute
@@ -278,18 +281,28 @@ constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);
 constexpr int kLoadThreads = kWave * kLoadWaves;                // 256: one per weight row of a chunk
 constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
 constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
-constexpr int kBufAct = kTileBytes;                            // [16 rows][528 B]
-constexpr int kBufNs = kMfmaItemRows * 4;                      // [16 rows] fp32 chunk steps
-constexpr int kBufBytes = kBufCodes + kBufScales + kBufAct + kBufNs;
 constexpr int kMaxWorkPerWg = 64;
 
+// An LDS chunk buffer for items of IRB 16-row blocks: codes, scales, the activation
+// tile [16 IRB rows][528 B] and the rows' fp32 chunk steps.
+template <int IRB>
+struct MfmaBuf {
+    static constexpr int kRows = 16 * IRB;
+    static constexpr int kAct = kRows * kRowPitch;
+    static constexpr int kNs = kRows * 4;
+    static constexpr int kBytes = kBufCodes + kBufScales + kAct + kNs;
+    static constexpr int kActLoads = kRows * kChunkBytes / 16 / kLoadThreads;  // 16-byte loads per thread
+    static_assert(kActLoads == 2 * IRB, "two 16-byte loads per row block and thread");
+};
+
+template <int IR>
 struct WorkDesc {
     int e;      // expert, -1: shared
     int nb0;    // first output of the block
     int nch;    // K chunks (0: the block lies past this unit's outputs)
     int R;      // rows
     int row0;   // first row: union row (routed) or token (shared)
-    int srow[kMfmaItemRows];  // activation source row of each row (rows past R repeat R-1)
+    int srow[IR];  // activation source row of each row (rows past R repeat R-1)
 };
 
 
@@ -301,19 +314,23 @@ __device__ __forceinline__ int load_row_output(int r, int nb0, bool &second) {
     return GU ? nb0 + 32 * wv + (bb % 2) * 16 + jj : nb0 + 64 * wv + 16 * bb + jj;
 }
 
-constexpr int kActLoads = kMfmaItemRows * kChunkBytes / 16 / kLoadThreads;  // 16-byte loads per thread
-
+template <int NA>
 struct ChunkRegs {
     u32x4_t q[8];
     float s[4];
-    uint4 a[kActLoads];
+    uint4 a[NA];
     float n;
 };
 
-template <bool GU>
+// IRB: 16-row blocks per work item (items hold at most 16 IRB rows; with IRB = 2 an
+// item of at most 16 rows computes one block)
+template <bool GU, int IRB>
 __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
+    using Buf = MfmaBuf<IRB>;
+    constexpr int IR = Buf::kRows, kBufBytes = Buf::kBytes, kBufAct = Buf::kAct;
+    constexpr int kActLoads = Buf::kActLoads, kRowBlocks = IRB;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    WorkDesc *work = reinterpret_cast<WorkDesc *>(lds + 2 * kBufBytes);
+    WorkDesc<IR> *work = reinterpret_cast<WorkDesc<IR> *>(lds + 2 * kBufBytes);
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -321,14 +338,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 
     // ---- this workgroup's work items, described in LDS
     const int n_routed = a.with_routed ? a.n_items[0] : 0;
-    const int n_sh = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
+    const int n_sh = a.with_shared ? (a.T + IR - 1) / IR : 0;
     const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
     const int nb = (nmax + kBlk - 1) / kBlk;
     const int total = (n_routed + n_sh) * nb;
     const int G = gridDim.x, g = blockIdx.x;
     const int nwi = g < total ? min((total - g + G - 1) / G, kMaxWorkPerWg) : 0;
-    for (int idx = tid; idx < nwi * kMfmaItemRows; idx += kMfmaThreads) {
-        const int k = idx / kMfmaItemRows, r = idx % kMfmaItemRows;
+    for (int idx = tid; idx < nwi * IR; idx += kMfmaThreads) {
+        const int k = idx / IR, r = idx % IR;
         const int wi = g + k * G, y = wi / nb, b = wi % nb;
         int e, row0, R;
         if (y < n_routed) {
@@ -337,8 +354,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             R = a.items[4 * y + 2];
         } else {
             e = -1;
-            row0 = (y - n_routed) * kMfmaItemRows;
-            R = min(kMfmaItemRows, a.T - row0);
+            row0 = (y - n_routed) * IR;
+            R = min(IR, a.T - row0);
         }
         const int N = GU ? (e >= 0 ? a.F : a.Fs) : a.H;
         const int K = GU ? a.H : (e >= 0 ? a.F : a.Fs);
@@ -368,7 +385,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         const uint8_t *qb0 = nullptr, *qb1 = nullptr, *abase = nullptr;
         const float *sb0 = nullptr, *sb1 = nullptr, *nbase = nullptr;  // nbase: chunk steps
         uint32_t qo[8], so[4], no = 0;
-        const uint8_t *arow = nullptr;  // 64-bit: union rows x fragment bytes can pass 2^32
+        const uint8_t *arow[kRowBlocks] = {};  // 64-bit: union rows x fragment bytes can pass 2^32
+        bool two = false;                       // the item has a second row block
         uint32_t qlast = 0;
         int NG = 1;
         auto sc_col = [&](int i) __attribute__((always_inline)) {
@@ -376,7 +394,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             return (q % 32) + 32 * (i & 1) + 64 * ((q / 32) + 2 * (i >> 1));
         };
         auto rows_of = [&](int k) __attribute__((always_inline)) {
-            const WorkDesc &d = work[k];
+            const WorkDesc<IR> &d = work[k];
             const int e = __builtin_amdgcn_readfirstlane(d.e);
             const int nb0 = __builtin_amdgcn_readfirstlane(d.nb0);
             int K, N;
@@ -424,11 +442,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 const int n = min(load_row_output<GU>(sc_col(i), nb0, second), N - 1);
                 so[i] = (uint32_t)n * (uint32_t)NG;
             }
-            arow = abase + (size_t)d.srow[t / 16] * NGp * kGroupBytes + 16 * (t % 16);
-            no = (uint32_t)d.srow[t % kMfmaItemRows] * (uint32_t)(NGp / kCG);  // (only lanes t < 16 store it)
+#pragma unroll
+            for (int rb = 0; rb < kRowBlocks; rb++)
+                arow[rb] = abase + (size_t)d.srow[16 * rb + t / 16] * NGp * kGroupBytes + 16 * (t % 16);
+            two = IRB > 1 && __builtin_amdgcn_readfirstlane(d.R) > 16;
+            no = (uint32_t)d.srow[t % IR] * (uint32_t)(NGp / kCG);  // (only lanes t < IR store it)
             pk = k;
         };
-        auto load = [&](ChunkRegs &v) __attribute__((always_inline)) {
+        auto load = [&](ChunkRegs<kActLoads> &v) __attribute__((always_inline)) {
             const int k = lk, c = lc;  // always a chunk that exists
             if (k != pk) rows_of(k);
             const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
@@ -437,9 +458,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const uint32_t sg = (uint32_t)min(kCG * c + t % 4, NG - 1);
 #pragma unroll
             for (int i = 0; i < 4; i++) v.s[i] = ((i & 1) ? sb1 : sb0)[so[i] + sg];
-            const uint8_t *ac = arow + (uint32_t)(c * kChunkBytes);
+            // the second row block's rows only if the item has them (else the registers
+            // keep older values, which no compute wave reads)
 #pragma unroll
-            for (int i = 0; i < kActLoads; i++) v.a[i] = *reinterpret_cast<const uint4 *>(ac + 256 * i);
+            for (int i = 0; i < kActLoads; i++)
+                if (i < 2 || two)
+                    v.a[i] = *reinterpret_cast<const uint4 *>(arow[i / 2] + (uint32_t)(c * kChunkBytes + 256 * (i % 2)));
             v.n = nbase[no + c];
             // advance; past the last chunk the head stays there (that chunk is loaded again)
             int nk = lk, nc = lc + 1;
@@ -453,7 +477,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 lc = nc;
             }
         };
-        auto store = [&](const ChunkRegs &v, int buf) __attribute__((always_inline)) {
+        auto store = [&](const ChunkRegs<kActLoads> &v, int buf) __attribute__((always_inline)) {
             uint8_t *B = lds + (size_t)buf * kBufBytes;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
@@ -462,14 +486,17 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * sc_col(i) + t % 4] = v.s[i];
-            const int ar = t / 16;
 #pragma unroll
-            for (int i = 0; i < kActLoads; i++)
-                *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * i)) = v.a[i];
-            if (t < kMfmaItemRows)  // a lane's four rows' steps are one read
+            for (int i = 0; i < kActLoads; i++) {
+                const int ar = 16 * (i / 2) + t / 16;
+                *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * (i % 2))) = v.a[i];
+            }
+            if (t < IR)  // a lane's four rows' steps are one read
                 reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct)[t] = v.n;
         };
-        ChunkRegs r0, r1, r2;
+        ChunkRegs<kActLoads> r0, r1, r2;
+#pragma unroll
+        for (int i = 0; i < kActLoads; i++) r0.a[i] = r1.a[i] = r2.a[i] = make_uint4(0, 0, 0, 0);
         if (S > 0) {
             load(r0);
             load(r1);
@@ -497,68 +524,65 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         // ================= compute waves
         const int j = lane % 16, p = lane / 16;
         const int cs = wv;
-        f32x4_t acc[4];
-        int ck = 0, cc = 0;  // the chunk being computed
+        f32x4_t acc[kRowBlocks][4];  // [row block][output block]
+        int ck = 0, cc = 0;          // the chunk being computed
         while (ck < nwi && work[ck].nch == 0) ck++;
         // outputs of work item k
         auto epilogue = [&](int k) __attribute__((always_inline)) {
-            const WorkDesc &d = work[k];
+            const WorkDesc<IR> &d = work[k];
             const int e = d.e, R = d.R, row0 = d.row0;
             const int N = GU ? (e >= 0 ? a.F : a.Fs) : a.H;
             float *out = GU ? (e >= 0 ? a.h_routed : a.h_shared) : (e >= 0 ? a.y_routed : a.y_shared);
             out += (size_t)row0 * N;
-            const f32x4_t *tot = acc;
-            // D layout: register v of lane (j, p) is row 4p + v, column j
+            // D layout: register v of lane (j, p) is row 4p + v of the row block, column j
 #pragma unroll
-            for (int b = 0; b < (GU ? 2 : 4); b++) {
-                const int n = GU ? d.nb0 + 32 * cs + b * 16 + j : d.nb0 + 64 * cs + 16 * b + j;
-                if (n >= N) continue;
+            for (int rb = 0; rb < kRowBlocks; rb++) {
+                if (16 * rb >= R) break;
 #pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const int r = 4 * p + v;
-                    if (r >= R) continue;
-                    float val;
-                    if (GU) {
-                        const float gg = tot[b][v], uu = tot[b + 2][v];
-                        val = gg / (1.0f + expf(-gg)) * uu;
-                    } else {
-                        val = tot[b][v];
+                for (int b = 0; b < (GU ? 2 : 4); b++) {
+                    const int n = GU ? d.nb0 + 32 * cs + b * 16 + j : d.nb0 + 64 * cs + 16 * b + j;
+                    if (n >= N) continue;
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        const int r = 16 * rb + 4 * p + v;
+                        if (r >= R) continue;
+                        float val;
+                        if (GU) {
+                            const float gg = acc[rb][b][v], uu = acc[rb][b + 2][v];
+                            val = gg / (1.0f + expf(-gg)) * uu;
+                        } else {
+                            val = acc[rb][b][v];
+                        }
+                        out[(size_t)r * N + n] = val;
                     }
-                    out[(size_t)r * N + n] = val;
                 }
             }
         };
-        lds_barrier();
-        for (int s = 0; s < S; s++) {
-            const uint8_t *B = lds + (size_t)(s & 1) * kBufBytes;
-            const WorkDesc &d = work[ck];
-            const int K = GU ? a.H : (d.e >= 0 ? a.F : a.Fs);
-            const int NG = K / 64;
-            const int ng = min(kCG, NG - kCG * cc);
-            if (cc == 0) {
-#pragma unroll
-                for (int b = 0; b < 4; b++) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
+        // One chunk of RB row blocks: the chunk's group scales of this lane's four
+        // columns and the steps of its rows; then the groups, with the next group's code
+        // words and A fragments read before this group's products.  Per group: issue its
+        // 8 RB MFMAs, then (while they run) read and convert the next group's operands,
+        // then scale-accumulate this group's results.  Scheduling barriers keep that
+        // order, so the conversion overlaps the matrix pipe.  The code conversion is
+        // shared by the row blocks.
+        auto run_chunk = [&](const uint8_t *B, int ng, auto rbc) __attribute__((always_inline)) {
+            constexpr int RB = decltype(rbc)::value;
             const uint8_t *cw = B + cs * 64 * kCodePitch;
             const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
             const uint8_t *tile = B + kBufCodes + kBufScales;
             const float *stp = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
-            // the chunk's group scales of this lane's four columns and the steps of its
-            // four rows; then the groups, with the next group's code words and A fragments
-            // read before this group's products
-            f32x4_t sc4[4], csum[4];
+            f32x4_t sc4[4], csum[RB][4], st4[RB];
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
-                csum[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < 4; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
+#pragma unroll
+            for (int rb = 0; rb < RB; rb++) {
+                st4[rb] = *reinterpret_cast<const f32x4_t *>(stp + 16 * rb + 4 * p);
+#pragma unroll
+                for (int b = 0; b < 4; b++) csum[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-            const f32x4_t st4 = *reinterpret_cast<const f32x4_t *>(stp + 4 * p);
-            // Per group: issue its 8 MFMAs, then (while they run) read and convert the next
-            // group's operands, then scale-accumulate this group's results.  Scheduling
-            // barriers keep that order, so the conversion overlaps the matrix pipe.
             struct Opnd {
-                i32x4_t bo[4];  // [block] 16 q bytes
-                i32x4_t a[2];   // hi, lo
+                i32x4_t bo[4];      // [block] 16 q bytes
+                i32x4_t a[RB][2];   // [row block][hi, lo]
             };
             auto read_group = [&](int gi) __attribute__((always_inline)) {
                 Opnd o;
@@ -566,9 +590,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int b = 0; b < 4; b++)
                     w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
-                const uint8_t *ar = tile + j * kRowPitch + gi * kGroupBytes + 16 * p;
-                o.a[0] = *reinterpret_cast<const i32x4_t *>(ar);
-                o.a[1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
+#pragma unroll
+                for (int rb = 0; rb < RB; rb++) {
+                    const uint8_t *ar = tile + (16 * rb + j) * kRowPitch + gi * kGroupBytes + 16 * p;
+                    o.a[rb][0] = *reinterpret_cast<const i32x4_t *>(ar);
+                    o.a[rb][1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
+                }
 #pragma unroll
                 for (int b = 0; b < 4; b++) o.bo[b] = code_bytes(w[b]);
                 return o;
@@ -578,27 +605,57 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int gi = 0; gi < kCG; gi++) {
                 if (gi >= ng) break;
-                i32x4_t gh[4], gl[4];
+                i32x4_t gh[RB][4], gl[RB][4];
 #pragma unroll
-                for (int b = 0; b < 4; b++) gh[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[0], cur.bo[b], zero, 0, 0, 0);
+                for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
-                for (int b = 0; b < 4; b++) gl[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[1], cur.bo[b], zero, 0, 0, 0);
+                    for (int b = 0; b < 4; b++)
+                        gh[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][0], cur.bo[b], zero, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < 4; b++)
+                        gl[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][1], cur.bo[b], zero, 0, 0, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 Opnd nxt;
                 if (gi + 1 < kCG) nxt = read_group(min(gi + 1, ng - 1));
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int b = 0; b < 4; b++)
+                for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-                    for (int v = 0; v < 4; v++)
-                        csum[b][v] = fmaf(sc4[b][gi], (float)(gh[b][v] * 256 + gl[b][v]), csum[b][v]);
+                    for (int b = 0; b < 4; b++)
+#pragma unroll
+                        for (int v = 0; v < 4; v++)
+                            csum[rb][b][v] = fmaf(sc4[b][gi], (float)(gh[rb][b][v] * 256 + gl[rb][b][v]), csum[rb][b][v]);
                 if (gi + 1 < kCG) cur = nxt;
             }
             // the chunk's sums times the row steps (over 16: the codes entered as 16 q)
 #pragma unroll
-            for (int b = 0; b < 4; b++)
+            for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-                for (int v = 0; v < 4; v++) acc[b][v] = fmaf(csum[b][v], st4[v] * 0.0625f, acc[b][v]);
+                for (int b = 0; b < 4; b++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        acc[rb][b][v] = fmaf(csum[rb][b][v], st4[rb][v] * 0.0625f, acc[rb][b][v]);
+        };
+        lds_barrier();
+        for (int s = 0; s < S; s++) {
+            const uint8_t *B = lds + (size_t)(s & 1) * kBufBytes;
+            const WorkDesc<IR> &d = work[ck];
+            const int K = GU ? a.H : (d.e >= 0 ? a.F : a.Fs);
+            const int NG = K / 64;
+            const int ng = min(kCG, NG - kCG * cc);
+            if (cc == 0) {
+#pragma unroll
+                for (int rb = 0; rb < kRowBlocks; rb++)
+#pragma unroll
+                    for (int b = 0; b < 4; b++) acc[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            if constexpr (IRB == 2) {
+                if (d.R > 16) run_chunk(B, ng, std::integral_constant<int, 2>());
+                else run_chunk(B, ng, std::integral_constant<int, 1>());
+            } else {
+                run_chunk(B, ng, std::integral_constant<int, 1>());
+            }
             if (++cc >= d.nch) {
                 epilogue(ck);
                 cc = 0;
@@ -624,8 +681,8 @@ static int mfma_cus() {
     return cus;
 }
 
-template <bool GU>
-static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
+template <bool GU, int IRB>
+static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
     const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
     const int nb = (nmax + (GU ? 127 : 255)) / (GU ? 128 : 256);
     const long total_max = (long)((a.with_routed ? a.max_items : 0) + shared_items) * nb;
@@ -633,13 +690,20 @@ static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *n
     // one workgroup per CU, more if a workgroup's table would overflow
     long G = mfma_cus();
     if ((total_max + G - 1) / G > kMaxWorkPerWg) G = (total_max + kMaxWorkPerWg - 1) / kMaxWorkPerWg;
-    const size_t lds = 2 * (size_t)kBufBytes + kMaxWorkPerWg * sizeof(WorkDesc);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU>),
+    const size_t lds = 2 * (size_t)MfmaBuf<IRB>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipGetLastError();
     ProfScope prof(name, st);
-    q4_mfma_kernel<GU><<<(int)G, kMfmaThreads, lds, st>>>(a);
+    q4_mfma_kernel<GU, IRB><<<(int)G, kMfmaThreads, lds, st>>>(a);
     return hipGetLastError();
+}
+
+// the work items' row count (16 or 32) selects the kernel
+template <bool GU>
+static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
+    return a.item_rows > 16 ? launch_gemm_rb<GU, 2>(a, shared_items, name, st)
+                            : launch_gemm_rb<GU, 1>(a, shared_items, name, st);
 }
 
 // x prepared once with the work list; gate/up for every item; the routed and shared
@@ -652,13 +716,14 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     it.uniq = a.uniq;
     it.off = a.off;
     it.E = a.E;
+    it.item_rows = a.item_rows;
     it.items = a.with_routed ? a.items : nullptr;
     it.n_items = a.n_items;
     it.with_union = a.union_in_prep;
     it.uni = a.uni;
     e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
-    const int shared_items = a.with_shared ? (a.T + kMfmaItemRows - 1) / kMfmaItemRows : 0;
+    const int shared_items = a.with_shared ? (a.T + a.item_rows - 1) / a.item_rows : 0;
     if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
     // h rows in fragment order: the routed rows (as many as the largest union can
     // have) and the shared rows

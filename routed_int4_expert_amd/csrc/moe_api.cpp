@@ -266,6 +266,7 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     m.E = E;
     m.max_units = f.max_units;
     m.max_rows = f.T * k;
+    m.item_rows = mfma_item_rows(m.max_rows, E);
     m.max_items = p.max_items;
     m.with_routed = f.with_routed;
     m.with_shared = f.with_shared;

@@ -141,18 +141,22 @@ struct MfmaArgs {
     float *hr_step, *hs_step;
     float *y_routed, *y_shared;      // [rows][H], [T][H]
     int T, H, F, Fs, E, max_units, max_rows, max_items;
+    int item_rows;  // rows per work item: 16 or kMfmaItemRows
     int with_routed, with_shared;
     int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
     UnionArgs uni;
 };
 
-// Matrix-core work items: at most this many rows of one expert (one 16-row MFMA block).
-constexpr int kMfmaItemRows = 16;
+// Matrix-core work items: at most this many rows of one expert (two 16-row MFMA
+// blocks; an item of at most 16 rows computes one).  Batches with few rows per expert
+// cut items at 16 rows (mfma_item_rows).
+constexpr int kMfmaItemRows = 32;
+inline int mfma_item_rows(int rows, int E) { return rows >= 8 * E ? kMfmaItemRows : 16; }
 // Fragment rows hold a whole number of 4-group K chunks.
 __host__ __device__ inline int mfma_groups_padded(int K) { return (K / 64 + 3) / 4 * 4; }
-// Upper bound of the work items of a batch: sum over experts of ceil(rows / kMfmaItemRows).
+// Upper bound of the work items of a batch: sum over experts of ceil(rows / 16).
 inline int mfma_max_items(int max_units, int max_rows) {
-    return max_units + (max_rows + kMfmaItemRows - 1) / kMfmaItemRows;
+    return max_units + (max_rows + 15) / 16;
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
