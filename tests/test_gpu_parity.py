@@ -95,6 +95,40 @@ def test_small_shapes_full_parity(sh):
         f"k={sh.top_k} T={sh.tokens} top_p={sh.top_p}")
     d = S.make_layer(sh, seed=0)
     x = S.make_batch(sh, d, seed=0)
+    full_parity(sh, d, x)
+
+
+def test_item_row_boundaries():
+    """Experts routed exactly 66, 17, 16 and 33 rows and a 66-token shared expert.
+
+    With at least 8 rows per expert the matrix-core path cuts 32-row work items: 66 rows
+    are items of 32, 32 and 2, 33 rows 32 and 1, 17 rows one item of two row blocks and
+    16 rows one of one block.  Expert 0 carries a large bias (always picked); the second
+    pick of each token is forced by its router logits (+3 for the target, -3 elsewhere,
+    built on orthonormal router rows).
+    """
+    sh = S.custom("itemrows", hidden=256, n_experts=8, ffn=128, shared_ffn=64, top_k=2,
+                  tokens=66, routed_scale=1.5)
+    d = S.make_layer(sh, seed=0)
+    E, H, T = sh.n_experts, sh.hidden, sh.tokens
+    q, r = np.linalg.qr(S.normal_f64(0, "itemrows/router", (H, E)))
+    wr = (q * np.sign(np.diag(r))[None, :]).T.astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[0] = 4.0
+    target = np.array([1] * 17 + [2] * 16 + [3] * 33)
+    L = np.full((T, E), -3.0)
+    L[np.arange(T), target] = 3.0
+    z = S.normal_f64(0, "itemrows/z", (T, H))
+    w64 = wr.astype(np.float64)
+    x = (L @ w64 + z - (z @ w64.T) @ w64).astype(np.float32)
+    d.update(router_w=wr, router_bias=bias)
+    ids, _ = R.route(R.Layer(d), x)[:2]
+    counts = np.bincount(np.asarray(ids).ravel(), minlength=E)
+    assert list(counts[:4]) == [66, 17, 16, 33] and counts[4:].sum() == 0, counts
+    full_parity(sh, d, x)
+
+
+def full_parity(sh, d, x):
     layer = M.Layer.from_host(d, DEV)
     xd = torch.from_numpy(x).to(DEV)
     ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
