@@ -135,22 +135,17 @@ static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float 
 }
 
 // ------------------------------------------------------------------ work list
-// Items in union order: expert uniq[u] with c rows gets ceil(c / IR) items of
-// consecutive rows.  One workgroup of 256 threads, one thread per union slot
-// (E <= 256); an exclusive scan of the item counts places each expert's items.
-__device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int32_t *uniq,
-                                                const int32_t *off, int E, int IR, int32_t *items,
-                                                int32_t *n_items) {
+// Work items: expert e with c rows gets ceil(c / IR) items of consecutive rows.  Items
+// of more than 16 rows (two MFMA row blocks, about 1.5 times the work of one) come
+// first, then those of at most 16; each class in union order.  The kernel deals its
+// (item, output block) pairs to the workgroups in turn, so the longer pairs go out
+// first and the shorter ones even out the end.  One workgroup of 256 threads, one
+// thread per union slot (E <= 256); exclusive scans of the two item counts place each
+// expert's items.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *total) {
     __shared__ int wsum[256 / kWave];
-    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
-    const int nu = n_uniq[0];
-    int e = -1, cnt = 0;
-    if (u < nu && u < E) {
-        e = uniq[u];
-        cnt = off[e + 1] - off[e];
-    }
-    const int ni = (cnt + IR - 1) / IR;
-    int inc = ni;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    int inc = v;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
         const int o = __shfl_up(inc, d, kWave);
@@ -158,16 +153,43 @@ __device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int
     }
     if (lane == kWave - 1) wsum[wv] = inc;
     __syncthreads();
-    int base = inc - ni;
-    for (int v = 0; v < wv; v++) base += wsum[v];
+    int base = inc - v;
+    for (int w = 0; w < wv; w++) base += wsum[w];
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();  // wsum is reused by the next scan
+    return base;
+}
+
+__device__ __forceinline__ void place_items(int e, int c, int row_base, int IR, int32_t *items,
+                                            int32_t *n_items) {
+    const int ni = (c + IR - 1) / IR;
+    const int nbig = ni == 0 ? 0 : (ni - 1) + (c - IR * (ni - 1) > 16 ? 1 : 0);
+    int big_total, small_total;
+    const int big_base = block_exclusive_scan(nbig, &big_total);
+    const int small_base = block_exclusive_scan(ni - nbig, &small_total);
     for (int i = 0; i < ni; i++) {
-        int32_t *it = items + 4 * (base + i);
+        const int pos = i < nbig ? big_base + i : big_total + small_base + (i - nbig);
+        int32_t *it = items + 4 * pos;
         it[0] = e;
-        it[1] = off[e] + IR * i;
-        it[2] = min(IR, cnt - IR * i);
+        it[1] = row_base + IR * i;
+        it[2] = min(IR, c - IR * i);
         it[3] = 0;
     }
-    if (u == blockDim.x - 1) n_items[0] = base + ni;
+    if (threadIdx.x == 0) n_items[0] = big_total + small_total;
+}
+
+__device__ __forceinline__ void mfma_items_body(const int32_t *n_uniq, const int32_t *uniq,
+                                                const int32_t *off, int E, int IR, int32_t *items,
+                                                int32_t *n_items) {
+    const int u = threadIdx.x;
+    const int nu = n_uniq[0];
+    int e = -1, cnt = 0, r0 = 0;
+    if (u < nu && u < E) {
+        e = uniq[u];
+        cnt = off[e + 1] - off[e];
+        r0 = off[e];
+    }
+    place_items(e, cnt, r0, IR, items, n_items);
 }
 
 // Up to two fragment preparations and, optionally, the work list, in one launch:
@@ -183,31 +205,11 @@ struct ItemsJob {
 };
 
 // The work list from the union's per-expert counts and offsets in LDS (union_block's
-// layout): the same items, in the same (increasing expert) order, as mfma_items_body.
+// layout): the same items, in the same order, as mfma_items_body.
 __device__ __forceinline__ void mfma_items_from_counts(const int32_t *cnt, const int32_t *offs, int E,
                                                        int IR, int32_t *items, int32_t *n_items) {
-    __shared__ int wsum[256 / kWave];
-    const int u = threadIdx.x, lane = u % kWave, wv = u / kWave;
-    const int c = u < E ? cnt[u] : 0;
-    const int ni = (c + IR - 1) / IR;
-    int inc = ni;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(inc, d, kWave);
-        if (lane >= d) inc += o;
-    }
-    if (lane == kWave - 1) wsum[wv] = inc;
-    __syncthreads();
-    int base = inc - ni;
-    for (int v = 0; v < wv; v++) base += wsum[v];
-    for (int i = 0; i < ni; i++) {
-        int32_t *it = items + 4 * (base + i);
-        it[0] = u;
-        it[1] = offs[u] + IR * i;
-        it[2] = min(IR, c - IR * i);
-        it[3] = 0;
-    }
-    if (u == blockDim.x - 1) n_items[0] = base + ni;
+    const int u = threadIdx.x;
+    place_items(u, u < E ? cnt[u] : 0, u < E ? offs[u] : 0, IR, items, n_items);
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepJob j0, PrepJob j1, ItemsJob it) {
@@ -348,14 +350,15 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         const int k = idx / IR, r = idx % IR;
         const int wi = g + k * G, y = wi / nb, b = wi % nb;
         int e, row0, R;
-        if (y < n_routed) {
-            e = a.items[4 * y];
-            row0 = a.items[4 * y + 1];
-            R = a.items[4 * y + 2];
-        } else {
+        if (y < n_sh) {  // the shared expert's items first (full-size but the last)
             e = -1;
-            row0 = (y - n_routed) * IR;
+            row0 = y * IR;
             R = min(IR, a.T - row0);
+        } else {
+            const int32_t *it = a.items + 4 * (y - n_sh);
+            e = it[0];
+            row0 = it[1];
+            R = it[2];
         }
         const int N = GU ? (e >= 0 ? a.F : a.Fs) : a.H;
         const int K = GU ? a.H : (e >= 0 ? a.F : a.Fs);
