@@ -25,15 +25,14 @@
 // Work item = up to 32 rows of one expert (two 16-row MFMA blocks) x a block of
 // outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
 // outputs (down).  Experts with more rows, and the shared expert, span several
-// items.  The kernel is persistent (one workgroup of 8 waves per CU, looping over
+// items.  The kernel is persistent (one workgroup of 12 waves per CU, looping over
 // (item, output block) pairs) and splits loading from computing: 4 loader waves keep
-// three 4-group K chunks in flight in registers and place each one in one of two LDS
+// two 4-group K chunks in flight in registers and place each one in one of two LDS
 // buffers (codes regrouped for the operand reads, scales, the activation tile and the
-// rows' chunk steps); 4 compute waves, one per column set, run the MFMAs on the
-// other buffer, issuing a group's MFMAs before converting the next group's codes so
-// that the conversion overlaps the matrix pipe; the converted codes serve both row
-// blocks of an item.  One barrier per chunk.  Every output has one owner: the result
-// is deterministic.
+// rows' chunk steps); 8 compute waves, two per column set, run the MFMAs on the
+// other buffer, issuing a group's MFMAs before converting the next group's codes; the
+// converted codes serve both row blocks of an item.  One barrier per chunk.  Every
+// output has one owner: the result is deterministic.
 
 #include <math.h>
 
@@ -267,20 +266,21 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Persistent grouped GEMM.  A workgroup of eight waves runs per CU and loops over work
-// items (32-row item, output block) wi = blockIdx.x + k * gridDim.x.  Waves 0-3
-// compute, waves 4-7 load.  For each 4-group K chunk the loaders place, in one of two
-// LDS buffers, the chunk's weight codes (regrouped so that a compute lane's operand
-// words are one 8-byte read), its group scales and its activation tile; the compute
-// waves work on the other buffer.  Compute wave w takes the outputs of column set w.
-// The loaders keep the next three chunks in flight in a ring of register sets, across
-// work-item boundaries (under full load a chunk's loads take about two chunk times to
-// return); one barrier per chunk.
+// Persistent grouped GEMM.  A workgroup of twelve waves runs per CU and loops over work
+// items (item, output block) wi = blockIdx.x + k * gridDim.x.  Waves 0-7 compute,
+// waves 8-11 load.  For each 4-group K chunk the loaders place, in one of two LDS
+// buffers, the chunk's weight codes (regrouped so that a compute lane's operand words
+// are one 8-byte read), its group scales and its activation tile; the compute waves
+// work on the other buffer.  Compute waves 2c and 2c + 1 take the outputs of column
+// set c.  The loaders keep the next two chunks in flight in a pair of register sets,
+// across work-item boundaries; one barrier per chunk.
 constexpr int kColSets = 4;
-constexpr int kCompWaves = kColSets;
 constexpr int kLoadWaves = 4;
-constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);
 constexpr int kLoadThreads = kWave * kLoadWaves;                // 256: one per weight row of a chunk
+constexpr int kCW = 2;                                          // compute waves per column set
+constexpr int kCompWaves = kColSets * kCW;
+constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);  // 768
+constexpr int kNBL = 4 / kCW;                                   // 16-column blocks per compute wave
 constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
 constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
 constexpr int kMaxWorkPerWg = 64;
@@ -325,9 +325,15 @@ struct ChunkRegs {
 };
 
 // IRB: 16-row blocks per work item (items hold at most 16 IRB rows; with IRB = 2 an
-// item of at most 16 rows computes one block)
+// item of at most 16 rows computes one block).  Twelve waves: two compute waves per
+// column set, each taking two of the set's four 16-column blocks (gate/up: a gate block
+// and its up block), and four loaders, three waves per SIMD.  A wave's own MFMAs and
+// VALU instructions do not overlap; with two compute waves per SIMD one wave's VALU
+// work runs while the other's MFMAs execute.  The register budget of three waves per
+// SIMD leaves the loaders two chunks in flight.
 template <bool GU, int IRB>
 __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
+    constexpr int kThreads = kMfmaThreads, NBL = kNBL;
     using Buf = MfmaBuf<IRB>;
     constexpr int IR = Buf::kRows, kBufBytes = Buf::kBytes, kBufAct = Buf::kAct;
     constexpr int kActLoads = Buf::kActLoads, kRowBlocks = IRB;
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
     const int total = (n_routed + n_sh) * nb;
     const int G = gridDim.x, g = blockIdx.x;
     const int nwi = g < total ? min((total - g + G - 1) / G, kMaxWorkPerWg) : 0;
-    for (int idx = tid; idx < nwi * IR; idx += kMfmaThreads) {
+    for (int idx = tid; idx < nwi * IR; idx += kThreads) {
         const int k = idx / IR, r = idx % IR;
         const int wi = g + k * G, y = wi / nb, b = wi % nb;
         int e, row0, R;
@@ -497,37 +503,30 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             if (t < IR)  // a lane's four rows' steps are one read
                 reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct)[t] = v.n;
         };
-        ChunkRegs<kActLoads> r0, r1, r2;
+        ChunkRegs<kActLoads> r0, r1;
 #pragma unroll
-        for (int i = 0; i < kActLoads; i++) r0.a[i] = r1.a[i] = r2.a[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < kActLoads; i++) r0.a[i] = r1.a[i] = make_uint4(0, 0, 0, 0);
         if (S > 0) {
             load(r0);
             load(r1);
-            load(r2);
             store(r0, 0);
         }
         lds_barrier();
-        // chunk m sits in register set m % 3 and LDS buffer m % 2; at step s the set of
-        // chunk s (already stored) takes chunk s + 3, and chunk s + 1 is stored
+        // chunk m sits in register set m % 2 and LDS buffer m % 2; at step s the set of
+        // chunk s (already stored) takes chunk s + 2, and chunk s + 1 is stored
         int s = 0;
-        for (; s + 6 <= S; s += 6) {
+        for (; s + 2 <= S; s += 2) {
             load(r0); store(r1, 1); lds_barrier();
-            load(r1); store(r2, 0); lds_barrier();
-            load(r2); store(r0, 1); lds_barrier();
-            load(r0); store(r1, 0); lds_barrier();
-            load(r1); store(r2, 1); lds_barrier();
-            load(r2); store(r0, 0); lds_barrier();
+            load(r1); store(r0, 0); lds_barrier();
         }
         if (s < S) { load(r0); store(r1, 1); lds_barrier(); }
-        if (s + 1 < S) { load(r1); store(r2, 0); lds_barrier(); }
-        if (s + 2 < S) { load(r2); store(r0, 1); lds_barrier(); }
-        if (s + 3 < S) { load(r0); store(r1, 0); lds_barrier(); }
-        if (s + 4 < S) { load(r1); store(r2, 1); lds_barrier(); }
     } else {
         // ================= compute waves
         const int j = lane % 16, p = lane / 16;
-        const int cs = wv;
-        f32x4_t acc[kRowBlocks][4];  // [row block][output block]
+        const int cs = wv / kCW, half = wv % kCW;
+        // the 16-column block of the set that local block lb is
+        auto gblk = [&](int lb) __attribute__((always_inline)) { return half + 2 * lb; };
+        f32x4_t acc[kRowBlocks][NBL];  // [row block][local output block]
         int ck = 0, cc = 0;          // the chunk being computed
         while (ck < nwi && work[ck].nch == 0) ck++;
         // outputs of work item k
@@ -542,8 +541,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             for (int rb = 0; rb < kRowBlocks; rb++) {
                 if (16 * rb >= R) break;
 #pragma unroll
-                for (int b = 0; b < (GU ? 2 : 4); b++) {
-                    const int n = GU ? d.nb0 + 32 * cs + b * 16 + j : d.nb0 + 64 * cs + 16 * b + j;
+                for (int b = 0; b < (GU ? NBL / 2 : NBL); b++) {
+                    // gate/up: local block b is a gate block, b + NBL/2 its up block
+                    const int n = GU ? d.nb0 + 32 * cs + gblk(b) * 16 + j : d.nb0 + 64 * cs + 16 * gblk(b) + j;
                     if (n >= N) continue;
 #pragma unroll
                     for (int v = 0; v < 4; v++) {
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                         if (r >= R) continue;
                         float val;
                         if (GU) {
-                            const float gg = acc[rb][b][v], uu = acc[rb][b + 2][v];
+                            const float gg = acc[rb][b][v], uu = acc[rb][b + NBL / 2][v];
                             val = gg / (1.0f + expf(-gg)) * uu;
                         } else {
                             val = acc[rb][b][v];
@@ -574,25 +574,25 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
             const uint8_t *tile = B + kBufCodes + kBufScales;
             const float *stp = reinterpret_cast<const float *>(B + kBufCodes + kBufScales + kBufAct);
-            f32x4_t sc4[4], csum[RB][4], st4[RB];
+            f32x4_t sc4[NBL], csum[RB][NBL], st4[RB];
 #pragma unroll
-            for (int b = 0; b < 4; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * b + j));
+            for (int b = 0; b < NBL; b++) sc4[b] = *reinterpret_cast<const f32x4_t *>(scl + 4 * (cs * 64 + 16 * gblk(b) + j));
 #pragma unroll
             for (int rb = 0; rb < RB; rb++) {
                 st4[rb] = *reinterpret_cast<const f32x4_t *>(stp + 16 * rb + 4 * p);
 #pragma unroll
-                for (int b = 0; b < 4; b++) csum[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int b = 0; b < NBL; b++) csum[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
             struct Opnd {
-                i32x4_t bo[4];      // [block] 16 q bytes
+                i32x4_t bo[NBL];    // [local block] 16 q bytes
                 i32x4_t a[RB][2];   // [row block][hi, lo]
             };
             auto read_group = [&](int gi) __attribute__((always_inline)) {
                 Opnd o;
-                uint2 w[4];
+                uint2 w[NBL];
 #pragma unroll
-                for (int b = 0; b < 4; b++)
-                    w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * b + j) * kCodePitch + 32 * gi + 8 * p);
+                for (int b = 0; b < NBL; b++)
+                    w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * gblk(b) + j) * kCodePitch + 32 * gi + 8 * p);
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
                     const uint8_t *ar = tile + (16 * rb + j) * kRowPitch + gi * kGroupBytes + 16 * p;
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                     o.a[rb][1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
                 }
 #pragma unroll
-                for (int b = 0; b < 4; b++) o.bo[b] = code_bytes(w[b]);
+                for (int b = 0; b < NBL; b++) o.bo[b] = code_bytes(w[b]);
                 return o;
             };
             const i32x4_t zero = {0, 0, 0, 0};
@@ -608,14 +608,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int gi = 0; gi < kCG; gi++) {
                 if (gi >= ng) break;
-                i32x4_t gh[RB][4], gl[RB][4];
+                i32x4_t gh[RB][NBL], gl[RB][NBL];
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
-                    for (int b = 0; b < 4; b++)
+                    for (int b = 0; b < NBL; b++)
                         gh[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][0], cur.bo[b], zero, 0, 0, 0);
 #pragma unroll
-                    for (int b = 0; b < 4; b++)
+                    for (int b = 0; b < NBL; b++)
                         gl[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][1], cur.bo[b], zero, 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-                    for (int b = 0; b < 4; b++)
+                    for (int b = 0; b < NBL; b++)
 #pragma unroll
                         for (int v = 0; v < 4; v++)
                             csum[rb][b][v] = fmaf(sc4[b][gi], (float)(gh[rb][b][v] * 256 + gl[rb][b][v]), csum[rb][b][v]);
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-                for (int b = 0; b < 4; b++)
+                for (int b = 0; b < NBL; b++)
 #pragma unroll
                     for (int v = 0; v < 4; v++)
                         acc[rb][b][v] = fmaf(csum[rb][b][v], st4[rb][v] * 0.0625f, acc[rb][b][v]);
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; rb++)
 #pragma unroll
-                    for (int b = 0; b < 4; b++) acc[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    for (int b = 0; b < NBL; b++) acc[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
             if constexpr (IRB == 2) {
                 if (d.R > 16) run_chunk(B, ng, std::integral_constant<int, 2>());
