@@ -127,9 +127,10 @@ int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32
  * SwiGLU FFN of expert e(r) on token row_tok[r]:
  *   y_rows[r] = Wd_e (silu(Wg_e x) * (Wu_e x)),   fp32 accumulation, unweighted.
  * The int4 codes enter the products exactly; the activations (x, and the SwiGLU
- * output before the down projection) with 16 significant bits: for T <= 4 as 16-bit
- * fixed point per 32 consecutive values (one rounding of at most max|x| / 65278 per
- * value, exact int32 dot products), for larger T as bf16 hi + lo pairs.
+ * output before the down projection) as 16-bit fixed point with a power-of-two step
+ * per block of consecutive values (32 for T <= 4, 256 for larger T): one rounding of
+ * less than max|x| / 32639 per value, none for values with at most 15 significant
+ * bits relative to the block's largest; the dot products are exact int32 sums.
  * Inputs n_uniq/uniq/off/row_tok as produced by moe_union (device).
  * Output: y_rows [T*k][H] fp32; rows past off[E] are left untouched. */
 int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
@@ -176,6 +177,21 @@ typedef struct {
 
 int moe_prof_begin(void);
 int moe_prof_end(moe_prof_stat *out, int32_t max_entries, int32_t *n_entries);
+
+/* ---- test hook -----------------------------------------------------------
+ * Not part of the layer's computation: for tests that check the expert products
+ * bit for bit.  Selects what the gate/up step of every later moe_expert_ffn and
+ * moe_layer_forward call in this process writes as the down projection's input:
+ * MOE_GU_SWIGLU (the default) silu(Wg x) * (Wu x) as in step 4 ([R] §1.3), MOE_GU_GATE
+ * the gate pre-activation Wg x, MOE_GU_UP the up pre-activation Wu x.  With integer
+ * activations and power-of-two group scales every product and partial sum is exact,
+ * so Wd (Wg x) matches an exact reference bitwise where SiLU's exp would not.
+ * Returns MOE_OK, or MOE_EINVAL for another mode (the mode is then unchanged).
+ * Process-wide; calls in flight on other threads see either mode. */
+#define MOE_GU_SWIGLU 0
+#define MOE_GU_GATE 1
+#define MOE_GU_UP 2
+int moe_test_set_gate_up_output(int32_t mode);
 
 #ifdef __cplusplus
 }

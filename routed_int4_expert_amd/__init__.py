@@ -22,7 +22,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
-           "moe_prof_end")
+           "moe_prof_end", "moe_test_set_gate_up_output")
+MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,8 @@ def lib():
     L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_test_set_gate_up_output.restype = ctypes.c_int
+    L.moe_test_set_gate_up_output.argtypes = [i32]
     _lib = L
     return L
 
@@ -248,3 +251,9 @@ def moe_prof_end() -> dict:
     n = ctypes.c_int32(0)
     _check(lib().moe_prof_end(buf, 64, ctypes.byref(n)), "moe_prof_end")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].ms)) for i in range(min(n.value, 64))}
+
+
+def moe_test_set_gate_up_output(mode: int):
+    """Test hook: what the gate/up step writes as h (MOE_GU_SWIGLU, MOE_GU_GATE or
+    MOE_GU_UP) for every later call in this process."""
+    _check(lib().moe_test_set_gate_up_output(mode), "moe_test_set_gate_up_output")

@@ -14,13 +14,15 @@
 // code q into u = q + 8 in [0, 15]; masking a 32-bit word of 8 codes with 0x0F0F0F0F
 // (and the word shifted right by 4) gives the even (odd) elements as four unsigned
 // bytes, three bit operations for eight codes.  Activations are staged per 32-element
-// chunk in 16-bit fixed point: x16 = rint(x * 32639 / max|x|), split into two signed
-// bytes x16 = 256 hi + lo; v_dot4_i32_i8 accumulates u * hi and u * lo exactly in
-// int32, and per chunk
+// chunk in 16-bit fixed point: x16 = rint(x * 2^n) with the power-of-two step 2^-n
+// that maps max|x| to at most 32639 (x16_shift), split into two signed bytes
+// x16 = 256 hi + lo; v_dot4_i32_i8 accumulates u * hi and u * lo exactly in int32,
+// and per chunk
 //   sum(q x16) = 256 sum(u hi) + sum(u lo) - 8 sum(x16)
 // (the unsigned-offset identity of "colibri 开发演进实录" §2.2, K1), times the chunk's
-// step max|x| / 32639 and the fp32 gs64 scale (two chunks per 64-group).  The only
-// rounding before the fp32 accumulation is x16: at most max|x| / 65278 per element.
+// step and the fp32 gs64 scale (two chunks per 64-group).  The only rounding before
+// the fp32 accumulation is x16: less than max|x| / 32639 per element, none for values
+// with at most 15 significant bits relative to the chunk's largest.
 //
 // The gate/up kernel finishes with the fused SiLU(g) * u epilogue and writes
 // h [rows][F]; the down kernel writes the unweighted y [rows][H].  Each output
@@ -34,7 +36,7 @@ namespace moe {
 
 // LDS row layout: per 32-element chunk 20 dwords -- for each 8-element group d four
 // dwords of signed bytes (hi of elements 8d+0,2,4,6; hi of 8d+1,3,5,7; lo of the
-// even ones; lo of the odd ones), the chunk's step max|x|/32639 (fp32) at dword 16
+// even ones; lo of the odd ones), the chunk's step 2^-n (fp32) at dword 16
 // and 8 sum(x16) (int32) at dword 17, then padding: the 16-byte reads of 8
 // consecutive lanes (80 bytes apart) hit distinct banks.
 constexpr int kChunkPitch = 20;
@@ -225,13 +227,13 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         mb = max(mb, dpp_u32<0xB1>(mb));
         mb = max(mb, dpp_u32<0x4E>(mb));
         const bool finite = mb < 0x7F800000u;
-        const float mx = __uint_as_float(mb);
-        const float inv = (finite && mb != 0u) ? kX16Max / mx : 0.0f;
+        const bool live = finite && mb != 0u;
+        const int n = live ? x16_shift(mb) : 0;
         int x16[8], hi[8], lo[8];
         int ps = 0;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            x16[e] = (int)fminf(fmaxf(rintf(xe[e] * inv), -kX16Max), kX16Max);
+            x16[e] = live ? (int)fminf(fmaxf(rintf(ldexpf(xe[e], n)), -kX16Max), kX16Max) : 0;
             hi[e] = (x16[e] + 128) >> 8;
             lo[e] = x16[e] - (hi[e] << 8);
             ps += x16[e];
@@ -247,7 +249,7 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         ps += (int)dpp_u32<0x4E>((uint32_t)ps);
         if (g % 4 == 0) {
             // step of x16 (a NaN step carries a non-finite input into every product)
-            chunk[16] = finite ? __float_as_uint(mx / kX16Max) : 0x7FC00000u;
+            chunk[16] = finite ? (live ? __float_as_uint(ldexpf(1.0f, -n)) : 0u) : 0x7FC00000u;
             chunk[17] = (uint32_t)(8 * ps);
         }
     }
@@ -473,8 +475,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
                             if (r >= R) continue;
                             float v;
                             if (GU) {
-                                const float g = acc[f][0][r], u = acc[f][S::NM - 1][r];
-                                v = g / (1.0f + expf(-g)) * u;
+                                v = gate_up_out(a.gu_out, acc[f][0][r], acc[f][S::NM - 1][r]);
                             } else {
                                 v = acc[f][0][r];
                             }

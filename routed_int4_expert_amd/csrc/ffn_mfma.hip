@@ -11,7 +11,8 @@
 //    are w AND 0xF0F0F0F0, the even ones (w << 4) AND 0xF0F0F0F0, so the codes
 //    enter the matrix core exactly ("colibrì 深度拆解" §5.2 packing).
 //  - A (activations): prepared once per row and 256-element K chunk as 16-bit
-//    fixed point, x16 = rint(x * 32639 / max|x|), split into signed bytes
+//    fixed point, x16 = rint(x * 2^n) with the power-of-two step 2^-n that maps
+//    max|x| to at most 32639 (x16_shift), split into signed bytes
 //    x16 = 256 hi + lo (the unsigned-offset and split identities of
 //    "colibri 开发演进实录" §2.2, K1, with the offset removed by the sign-carrying
 //    codes), in the codes' element order (per word: 0,2,4,6 then 1,3,5,7),
@@ -19,8 +20,8 @@
 //    exact int32 sum.
 //  - per 64-group ("colibri 开发演进实录" §2.1 gs64) 256 hi + lo is converted to
 //    fp32 and scaled by the group scale into the chunk's sum, which the row's
-//    chunk step (max|x| / 32639, over 16 for the codes' factor) scales into the
-//    fp32 running sum.  The one rounding of x is x16 itself.
+//    chunk step (over 16 for the codes' factor) scales into the fp32 running sum.
+//    The one rounding of x is x16 itself.
 //
 // Work item = up to 32 rows of one expert (two 16-row MFMA blocks) x a block of
 // outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
@@ -48,7 +49,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kHighNibbles = 0xF0F0F0F0u;  // 16 q per byte
-constexpr float kX16Max = 32639.0f;             // 127 * 256 + 127: hi and lo stay signed bytes
 constexpr int kGroupBytes = 128;                // one row's 64-group: 4 x 16 B hi, then 4 x 16 B lo
 constexpr int kCG = 4;                          // groups per K chunk
 constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 512 B
@@ -58,7 +58,7 @@ constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct L
 constexpr int kCodePitch = 144;
 
 // ------------------------------------------------------------------ prep
-// Rows of K fp32 values -> per 256-element chunk c: step[row][c] = max|x| / 32639
+// Rows of K fp32 values -> per 256-element chunk c: step[row][c] = 2^-x16_shift(max|x|)
 // (NaN if the chunk holds a non-finite value, 0 if it is all zero) and, per 64-group
 // G, 128 bytes: for word w (elements 64G + 8w .. +7) the hi bytes of its even
 // elements (0,2,4,6) and of its odd ones at 8w, the lo bytes likewise at 64 + 8w.
@@ -101,12 +101,12 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, m, kWave));
     const bool finite = mb < 0x7F800000u;
-    const float mx = __uint_as_float(mb);
-    const float r = finite && mb ? kX16Max / mx : 0.0f;
+    const bool nz = finite && mb != 0u;
+    const int sh = nz ? x16_shift(mb) : 0;
     int hi[8], lo[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) {
-        const int x16 = (int)rintf(e[s] * r);
+        const int x16 = nz ? (int)rintf(ldexpf(e[s], sh)) : 0;
         hi[s] = (x16 + 128) >> 8;
         lo[s] = x16 - 256 * hi[s];
     }
@@ -118,7 +118,7 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
         *reinterpret_cast<uint2 *>(grp + 64 + 8 * wg) =
             make_uint2(pack_bytes(lo[0], lo[2], lo[4], lo[6]), pack_bytes(lo[1], lo[3], lo[5], lo[7]));
     }
-    if (in_rows && w == 0) j.step[(size_t)row * NC + c] = finite ? mx / kX16Max : __builtin_nanf("");
+    if (in_rows && w == 0) j.step[(size_t)row * NC + c] = finite ? (nz ? ldexpf(1.0f, -sh) : 0.0f) : __builtin_nanf("");
 }
 
 static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step) {
@@ -551,8 +551,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                         if (r >= R) continue;
                         float val;
                         if (GU) {
-                            const float gg = acc[rb][b][v], uu = acc[rb][b + NBL / 2][v];
-                            val = gg / (1.0f + expf(-gg)) * uu;
+                            val = gate_up_out(a.gu_out, acc[rb][b][v], acc[rb][b + NBL / 2][v]);
                         } else {
                             val = acc[rb][b][v];
                         }

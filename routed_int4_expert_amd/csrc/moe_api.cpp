@@ -100,6 +100,10 @@ static int check_device() {
 
 static int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
 
+// what the gate/up step writes (moe_test_set_gate_up_output); read when a call builds
+// its kernel arguments
+static std::atomic<int> g_gu_out{kGuSwiglu};
+
 // -------------------------------------------------------------- workspace plan
 static size_t router_part_bytes(const moe_layer &L, int T) {
     // largest S(T') * T' over T' <= T, so the plan grows monotonically with T
@@ -236,6 +240,7 @@ static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_
 
 static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *ws) {
     MfmaArgs m;
+    m.gu_out = f.gu_out;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
     m.x_step = at<float>(ws, p.x_step);
@@ -286,6 +291,7 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
                         const int32_t *n_uniq, const int32_t *uniq, const int32_t *off,
                         const int32_t *row_tok, float *y_routed, void *ws) {
     FfnArgs a;
+    a.gu_out = g_gu_out.load();
     a.x = x;
     a.n_uniq = n_uniq;
     a.uniq = uniq;
@@ -461,6 +467,12 @@ int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t 
     a.H = H;
     a.eps = eps;
     return launched(launch_residual_rmsnorm(a, (hipStream_t)stream));
+}
+
+int moe_test_set_gate_up_output(int32_t mode) {
+    if (mode != MOE_GU_SWIGLU && mode != MOE_GU_GATE && mode != MOE_GU_UP) return MOE_EINVAL;
+    g_gu_out.store(mode);
+    return MOE_OK;
 }
 
 const char *moe_strerror(int code) {

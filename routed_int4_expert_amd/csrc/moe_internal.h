@@ -15,6 +15,33 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// What the gate/up step writes as h: SiLU(g) * u (the layer), or, for the test hook
+// moe_test_set_gate_up_output, the gate or the up pre-activation.
+constexpr int kGuSwiglu = MOE_GU_SWIGLU, kGuGate = MOE_GU_GATE, kGuUp = MOE_GU_UP;
+__device__ __forceinline__ float gate_up_out(int mode, float g, float u) {
+    return mode == kGuSwiglu ? g / (1.0f + expf(-g)) * u : (mode == kGuGate ? g : u);
+}
+
+// ---------------------------------------------------------------- 16-bit activations
+// Both expert-FFN paths take activations as 16-bit fixed point per block: x16 =
+// rint(x * 2^n) with n the largest integer for which max|x| * 2^n <= 32639 = 127 * 256
+// + 127 (so hi = (x16 + 128) >> 8 and lo = x16 - 256 hi are signed bytes), and step
+// 2^-n.  A power-of-two step scales exactly: values with at most 15 significant bits
+// relative to the block's largest are represented exactly.  mb: the bit pattern of
+// max|x| (finite, nonzero).  Subnormal maxima are first scaled by 2^64 (exactly); n is
+// at most 149, so the step 2^-n stays representable.
+__device__ __forceinline__ int x16_shift(uint32_t mb) {
+    int bias = 0;
+    if (mb < 0x00800000u) {
+        mb = __float_as_uint(__uint_as_float(mb) * 18446744073709551616.0f);
+        bias = 64;
+    }
+    const int ef = (int)(mb >> 23);
+    // 1.f * 2^14 <= 32639 iff the mantissa is at most 16255 / 16384 (8,322,560 / 2^23)
+    const int k = (mb & 0x7FFFFFu) <= 8322560u ? 14 : 13;
+    return min(k + 127 - ef + bias, 149);
+}
+
 // ---------------------------------------------------------------- router tiling
 // Router logits are a [T][E] x [E][H]^T product in fp64, tiled 64 tokens x 64
 // experts per workgroup with a split over H so small batches still cover the chip.
@@ -103,6 +130,7 @@ struct FfnArgs {
     float *y_shared;                 // [T][H]
     int T, H, F, Fs, max_units;
     int with_routed, with_shared;
+    int gu_out;  // what the gate/up step writes as h: kGuSwiglu, kGuGate or kGuUp
     // Selection and union inside the gate/up launch (one token): every routed
     // workgroup selects and builds the union in LDS from the router logits; the
     // first routed workgroup also writes them out through sel (ids, w, keff) and uni
@@ -130,7 +158,7 @@ constexpr int kGemvMaxTokens = 4;
 struct MfmaArgs {
     const float *x;                  // [T][H]
     uint8_t *x_frag;                 // [T][NGp(H)][128]
-    float *x_step;                   // [T][NGp(H) / 4]  max|x| / 32639 per chunk
+    float *x_step;                   // [T][NGp(H) / 4]  power-of-two step per chunk
     const int32_t *n_uniq, *uniq, *off, *row_tok;
     int32_t *items;                  // [max_items][4]: expert, first row, rows, 0
     int32_t *n_items;
@@ -142,6 +170,7 @@ struct MfmaArgs {
     float *y_routed, *y_shared;      // [rows][H], [T][H]
     int T, H, F, Fs, E, max_units, max_rows, max_items;
     int item_rows;  // rows per work item: 16 or kMfmaItemRows
+    int gu_out;     // as FfnArgs::gu_out
     int with_routed, with_shared;
     int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
     UnionArgs uni;

@@ -150,3 +150,12 @@ def test_valid_call_without_gpu_reports_device_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; fake pointers must not reach a launch")
     assert call_forward(_layer()) == M.MOE_EDEVICE
+
+
+def test_gate_up_output_hook_validates():
+    """The test hook accepts its three modes and rejects others (no device needed)."""
+    lib = M.lib()
+    assert lib.moe_test_set_gate_up_output(3) == M.MOE_EINVAL
+    assert lib.moe_test_set_gate_up_output(-1) == M.MOE_EINVAL
+    for mode in (M.MOE_GU_GATE, M.MOE_GU_UP, M.MOE_GU_SWIGLU):
+        assert lib.moe_test_set_gate_up_output(mode) == M.MOE_OK

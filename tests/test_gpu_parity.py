@@ -128,6 +128,51 @@ def test_item_row_boundaries():
     full_parity(sh, d, x)
 
 
+@pytest.mark.parametrize("T", [3, 24, 40], ids=["gemv", "mfma16", "mfma32"])
+@pytest.mark.parametrize("mode", ["gate", "up"])
+def test_exact_expert_products(T, mode):
+    """Exactness special case: activations in {-1, 0, 1} and every gs64 scale 2^-6.
+
+    Each pre-activation is 2^-6 times an integer of at most 12 bits, so the 16-bit
+    activation blocks represent x and the pre-activations exactly and every product
+    and partial sum is exact in int32 and fp32.  With the gate/up step writing the
+    gate (or up) pre-activation P instead of SiLU(g) * u, the expert rows
+    y = Wd P must equal the exact value bit for bit: T = 3 runs the GEMV kernels,
+    T = 24 the matrix-core kernels with 16-row items, T = 40 with 32-row items.
+    """
+    sh = S.custom(f"exact{T}", hidden=256, n_experts=8, ffn=128, shared_ffn=64, top_k=2,
+                  tokens=T)
+    d = S.make_layer(sh, seed=0)
+    for key in ("gate_s", "up_s", "down_s", "sh_gate_s", "sh_up_s", "sh_down_s"):
+        d[key] = np.full_like(d[key], 2.0 ** -6)
+    x = np.rint(S.uniform_f32(0, f"exact{T}/x", (T, sh.hidden), -1.49, 1.49)).astype(np.float32)
+    assert set(np.unique(x)) <= {-1.0, 0.0, 1.0}
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    M.moe_test_set_gate_up_output(M.MOE_GU_GATE if mode == "gate" else M.MOE_GU_UP)
+    try:
+        y = M.moe_expert_ffn(layer, xd, un)
+        torch.cuda.synchronize()
+    finally:
+        M.moe_test_set_gate_up_output(M.MOE_GU_SWIGLU)
+    rows = int(ru["off"][-1])
+    x64 = x.astype(np.float64)
+    ref = np.empty((rows, sh.hidden), np.float64)
+    for e in range(sh.n_experts):
+        r0, r1 = int(ru["off"][e]), int(ru["off"][e + 1])
+        if r1 == r0:
+            continue
+        q, sc = (d["gate_q"][e], d["gate_s"][e]) if mode == "gate" else (d["up_q"][e], d["up_s"][e])
+        pre = x64[ru["row_tok"][r0:r1]] @ R.dequantize_gs64(q, sc).T
+        ref[r0:r1] = pre @ R.dequantize_gs64(d["down_q"][e], d["down_s"][e]).T
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref), "reference not exact in fp32"
+    got = y.cpu().numpy()[:rows]
+    np.testing.assert_array_equal(got, ref.astype(np.float32))
+    say(f"exact {mode} T={T}: {rows} rows bit-identical")
+
+
 def full_parity(sh, d, x):
     layer = M.Layer.from_host(d, DEV)
     xd = torch.from_numpy(x).to(DEV)
