@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-BF16_PEAK_FLOPS = 2.5e15   # dense bf16 MFMA
+I8_PEAK_OPS = 5.0e15       # dense int8 MFMA (the matrix-core path's arithmetic)
 
 
 def log(msg):
@@ -280,9 +280,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # the expert FFNs' arithmetic: int8 x int8 dot products into int32 (decode GEMV,
-        # T <= 4) or bf16 matrix-core products into fp32 (T > 4); fp32 accumulation
-        "dtype": "i8" if T <= 4 else "bf16",
+        # the expert FFNs' arithmetic: int8 x int8 products into int32 (v_dot4 in the
+        # decode GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
+        "dtype": "i8",
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: {WORKLOADS[wl]}",
@@ -305,7 +305,7 @@ def main():
             "traffic": counted_traffic(wl, gu_name),
             "bytes_per_launch": float(gu_bytes),
             "avg_launch_us": float(gu_avg_ms * 1e3),
-            "mfma_util_vs_bf16_dense": float(gu_flops / (gu_avg_ms * 1e-3) / BF16_PEAK_FLOPS),
+            "mfma_util_vs_i8_dense": float(gu_flops / (gu_avg_ms * 1e-3) / I8_PEAK_OPS),
         },
         "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
     }
