@@ -86,6 +86,17 @@ SMALL = [
     # fewer than k, and the shared expert is narrower than the routed ones
     S.custom("midtok", hidden=320, n_experts=48, ffn=128, shared_ffn=64, top_k=6, tokens=40,
              top_p=0.85, routed_scale=1.5, bias_amp=0.2),
+    # the compiled limits: the largest batch (4096 tokens, 32-row items, a 1024-thread union
+    # over 32K picks), the largest hidden size and the largest FFN widths, each on the GEMV
+    # path (T <= 4; four staged rows of K = 16384 fill the 160 KB of LDS) and the
+    # matrix-core path
+    S.custom("maxtok", hidden=128, n_experts=64, ffn=64, shared_ffn=64, top_k=8, tokens=4096,
+             top_p=0.9, bias_amp=0.1),
+    S.custom("maxdim", hidden=16384, n_experts=8, ffn=128, shared_ffn=64, top_k=2, tokens=5),
+    S.custom("maxdim_gemv", hidden=16384, n_experts=8, ffn=128, shared_ffn=64, top_k=2, tokens=3),
+    S.custom("maxffn", hidden=128, n_experts=8, ffn=16384, shared_ffn=16384, top_k=2, tokens=6),
+    S.custom("maxffn_gemv", hidden=128, n_experts=8, ffn=16384, shared_ffn=16384, top_k=2,
+             tokens=4),
 ]
 
 
