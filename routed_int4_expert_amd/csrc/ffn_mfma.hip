@@ -23,9 +23,9 @@
 //    chunk step (over 16 for the codes' factor) scales into the fp32 running sum.
 //    The one rounding of x is x16 itself.
 //
-// Work item = up to 32 rows of one expert (two 16-row MFMA blocks) x a block of
-// outputs: 4 column sets x 32 outputs (gate and up for the same columns) or 4 x 64
-// outputs (down).  Experts with more rows, and the shared expert, span several
+// Work item = up to 16 or, for batches with many rows per expert, 32 rows of one
+// expert (one or two 16-row MFMA blocks) x a block of outputs: 4 column sets x 32
+// outputs (gate and up for the same columns) or 4 x 64 outputs (down).  Experts with more rows, and the shared expert, span several
 // items.  The kernel is persistent (one workgroup of 12 waves per CU, looping over
 // (item, output block) pairs) and splits loading from computing: 4 loader waves keep
 // two 4-group K chunks in flight in registers and place each one in one of two LDS
