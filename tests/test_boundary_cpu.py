@@ -159,3 +159,18 @@ def test_gate_up_output_hook_validates():
     assert lib.moe_test_set_gate_up_output(-1) == M.MOE_EINVAL
     for mode in (M.MOE_GU_GATE, M.MOE_GU_UP, M.MOE_GU_SWIGLU):
         assert lib.moe_test_set_gate_up_output(mode) == M.MOE_OK
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every call raises: there is no other path."""
+    import subprocess
+    import sys
+    code = ("import routed_int4_expert_amd as M\n"
+            "M.LIB_PATH = '/nonexistent/libmoe_gfx950.so'\n"
+            "try:\n"
+            "    M.strerror(0)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised', 'missing' in str(e))\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "raised True"
