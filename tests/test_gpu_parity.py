@@ -86,6 +86,19 @@ SMALL = [
     # fewer than k, and the shared expert is narrower than the routed ones
     S.custom("midtok", hidden=320, n_experts=48, ffn=128, shared_ffn=64, top_k=6, tokens=40,
              top_p=0.85, routed_scale=1.5, bias_amp=0.2),
+    # degenerate routing: top-1; k = E (every expert selected, a dense sigma mixture);
+    # a top-p so small that every token keeps only its first pick (keff = 1), each on
+    # the GEMV and the matrix-core path
+    S.custom("top1", hidden=256, n_experts=16, ffn=128, shared_ffn=64, top_k=1, tokens=9,
+             routed_scale=2.0),
+    S.custom("top1_gemv", hidden=256, n_experts=16, ffn=128, shared_ffn=64, top_k=1, tokens=2),
+    S.custom("dense", hidden=128, n_experts=8, ffn=64, shared_ffn=64, top_k=8, tokens=6,
+             norm_topk=0),
+    S.custom("dense_gemv", hidden=128, n_experts=8, ffn=64, shared_ffn=0, top_k=8, tokens=1),
+    S.custom("toppmin", hidden=256, n_experts=32, ffn=128, shared_ffn=128, top_k=8, tokens=20,
+             top_p=0.01, routed_scale=2.5),
+    S.custom("toppmin_one", hidden=256, n_experts=32, ffn=128, shared_ffn=128, top_k=8, tokens=1,
+             top_p=0.01, routed_scale=2.5),
     # the compiled limits: the largest batch (4096 tokens, 32-row items, a 1024-thread union
     # over 32K picks), the largest hidden size and the largest FFN widths, each on the GEMV
     # path (T <= 4; four staged rows of K = 16384 fill the 160 KB of LDS) and the
