@@ -174,3 +174,14 @@ def test_missing_library_fails_loudly():
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip() == "raised True"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits non-zero with a message, before
+    touching a device."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert res.returncode != 0
+    assert "one GPU" in (res.stdout + res.stderr)
