@@ -256,6 +256,85 @@ def test_topp_limits():
     assert np.all(k0 == 1)
 
 
+# --------------------------------------------------------------------------- ties
+# Exact ties, worked by hand from the reading of "MoE 路由与专家流式加载" §1.2 (k rounds
+# of argmax over choice, excluding taken experts, a strictly greater score replacing
+# the best so far, so equal scores go to the lower id; top-p sorts the k gates
+# descending with equal gates in slot order).  Each case is built so that ties to the
+# higher id, a top-p sort that orders equal gates by id, or a strict cut (cum > p*tot)
+# gives a different answer.
+def _sel_layer(E, k, bias=None, top_p=0.0, norm=1, scale=1.0):
+    d = dict(hidden=64, n_experts=E, ffn=64, shared_ffn=0, top_k=k, top_p=top_p,
+             norm_topk=norm, routed_scale=scale,
+             router_w=np.zeros((E, 64), np.float32),
+             router_bias=None if bias is None else np.asarray(bias, np.float32))
+    return R.Layer(d)
+
+
+def test_topk_ties_go_to_lowest_id():
+    # expert 3 leads; experts 1, 4, 6, 8 tie for the remaining three slots
+    lg = np.full((1, 10), -1.0)
+    lg[0, 3] = 3.0
+    lg[0, [1, 4, 6, 8]] = 2.0
+    ids, w, keff = R.select(_sel_layer(10, 4), lg)
+    assert ids[0].tolist() == [3, 1, 4, 6] and keff[0] == 4
+    s3, s2 = 1 / (1 + math.exp(-3.0)), 1 / (1 + math.exp(-2.0))
+    tot = ((s3 + s2) + s2) + s2  # slot order
+    np.testing.assert_array_equal(w[0], np.float32([s3 / tot, s2 / tot, s2 / tot, s2 / tot]))
+
+
+def test_topk_ties_with_equal_bias():
+    # equal logits and equal biases give equal choices; a larger bias ranks first
+    lg = np.zeros((1, 12))
+    lg[0, [2, 5, 9, 11]] = 0.5
+    bias = np.zeros(12)
+    bias[[2, 5, 9, 11]] = 0.25
+    bias[7] = 1.0
+    ids, _, _ = R.select(_sel_layer(12, 3, bias=bias), lg)
+    assert ids[0].tolist() == [7, 2, 5]
+
+
+def test_topk_all_keys_equal():
+    # no bias and equal logits: every choice is equal, so the picks are experts 0..k-1 in
+    # id order, each with weight routed_scale / k under norm_topk
+    lg = np.zeros((2, 256))
+    ids, w, keff = R.select(_sel_layer(256, 8, scale=2.5), lg)
+    assert ids.tolist() == [list(range(8))] * 2 and keff.tolist() == [8, 8]
+    assert np.all(w == np.float32(2.5 / 8))
+    ids, _, _ = R.select(_sel_layer(6, 6), np.zeros((1, 6)))
+    assert ids[0].tolist() == [0, 1, 2, 3, 4, 5]
+
+
+def test_topp_equal_gates_keep_slot_order():
+    # experts 5 and 2 have the same gate; 5 is picked first (larger bias).  total = 2 sig,
+    # p * total = sig exactly, and the running sum reaches it after the first gate in the
+    # sort, which is slot 0 (expert 5): keff = 1, expert 5 kept with weight 1 * scale
+    lg = np.full((1, 6), -5.0)
+    lg[0, [2, 5]] = 1.0
+    bias = np.zeros(6)
+    bias[5], bias[2] = 0.3, 0.2
+    ids, w, keff = R.select(_sel_layer(6, 2, bias=bias, top_p=0.5, scale=2.0), lg)
+    assert ids[0].tolist() == [5, -1] and keff[0] == 1
+    assert w[0].tolist() == [2.0, 0.0]
+
+
+def test_topp_cut_inside_equal_gates():
+    # expert 9 (logit 3, bias 0.5) first, then experts 7, 4, 1 with equal gates (logit 1)
+    # in that slot order (biases 0.3 > 0.2 > 0.1).  p sits between sig9 + sig and sig9 + 2 sig of
+    # the total, so two of the three equal gates are kept: the first two slots (7, 4)
+    s9, s1 = 1 / (1 + math.exp(-3.0)), 1 / (1 + math.exp(-1.0))
+    tot = s9 + 3 * s1
+    p = (s9 + 1.5 * s1) / tot
+    lg = np.full((1, 12), -4.0)
+    lg[0, 9] = 3.0
+    lg[0, [1, 4, 7]] = 1.0
+    bias = np.zeros(12)
+    bias[9], bias[7], bias[4], bias[1] = 0.5, 0.3, 0.2, 0.1
+    ids, w, keff = R.select(_sel_layer(12, 4, bias=bias, top_p=p, norm=0), lg)
+    assert ids[0].tolist() == [9, 7, 4, -1] and keff[0] == 3
+    np.testing.assert_array_equal(w[0], np.float32([s9, s1, s1, 0.0]))
+
+
 # --------------------------------------------------------------------------- union
 def _union_bruteforce(E, ids, keff):
     T, k = ids.shape
@@ -420,3 +499,21 @@ def test_bf16_rounding_mode():
     assert back[0] == 1.0 and back[1] == 1.0 and back[2] == np.float32(1.0 + 2 ** -6)
     assert back[3] == -2.5
     assert abs(back[4] - 1e-3) <= 1e-3 * 2 ** -8
+
+
+# --------------------------------------------------------------------------- workload inputs
+@pytest.mark.parametrize("pool", [0, 1])
+def test_prefill_inputs_union_near_200(pool):
+    """The 512-token prefill batch is built with a fixed popularity spread (alpha); under
+    the oracle's routing its batch union is close to the 200 of 256 experts the workload
+    asks for, with a skewed rows-per-expert histogram."""
+    sh = S.SHAPES["glm_prefill"]
+    rw, rb = S.router(sh, 0, 0)
+    d = S.layer_params(sh)
+    d.update(router_w=rw, router_bias=rb)
+    x, _ = S.gumbel_skew_batch(sh, sh.tokens, rw, rb, 0, pool)
+    ids, _, keff = R.route(R.Layer(d), x)
+    u = R.union(sh.n_experts, ids, keff)
+    counts = np.diff(u["off"])
+    assert 190 <= u["n_uniq"] <= 210, u["n_uniq"]
+    assert counts.max() >= 88 and np.median(counts[counts > 0]) <= 16
