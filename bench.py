@@ -280,9 +280,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # the expert FFNs' arithmetic: int8 x int8 products into int32 (v_dot4 in the
-        # decode GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
-        "dtype": "i8",
+        # the expert FFNs' arithmetic: int4 codes times 16-bit fixed-point activations
+        # (carried as two int8 limbs) with exact int32 group sums (v_dot4 in the decode
+        # GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
+        "dtype": "i4xfx16-i32-f32acc",
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: {WORKLOADS[wl]}",

@@ -113,7 +113,11 @@ int moe_route(const moe_layer *L, const float *x, int32_t T, int32_t *ids, float
 /* Step 3 ([R] §1.3, batch-union): deduplicates the kept experts of the whole batch
  * so each is read once, and builds the token permutation.
  *   ids [T][k], keff [T] as produced by moe_route (ids outside [0, E) and slots
- *   at or past keff are ignored).
+ *   at or past keff are ignored).  The kept ids of one token must be distinct, as
+ *   moe_route produces them: a token that lists an expert twice gets one row for
+ *   both picks (count, off and row_tok then differ from counting the pick twice,
+ *   and both picks' pick_row name that row); nothing is read or written out of
+ *   bounds either way.
  * Outputs: n_uniq [1]; uniq [E] the distinct experts ascending, -1 after n_uniq;
  *          off [E+1] exclusive prefix sum of per-expert row counts;
  *          row_tok [T*k] token of each row, rows ordered by (expert, token)
@@ -165,7 +169,9 @@ const char *moe_strerror(int code);
  * every kernel the calls above launch is bracketed by two HIP events recorded
  * on the call's own stream.  moe_prof_end() waits for those events, returns
  * per-kernel totals (summed over launches, in milliseconds) and stops the
- * timing.  Process-wide; not for concurrent use from several threads.
+ * timing.  The recording belongs to the calling host thread: calls made on other
+ * threads are neither timed nor affected.  Measurement only: it never changes what a
+ * call computes.
  * moe_prof_end writes at most max_entries entries and the number of distinct
  * kernels to *n_entries.  Both return MOE_OK, or MOE_EDEVICE if an event call
  * failed, MOE_EINVAL for bad arguments. */
@@ -178,20 +184,23 @@ typedef struct {
 int moe_prof_begin(void);
 int moe_prof_end(moe_prof_stat *out, int32_t max_entries, int32_t *n_entries);
 
-/* ---- test hook -----------------------------------------------------------
- * Not part of the layer's computation: for tests that check the expert products
- * bit for bit.  Selects what the gate/up step of every later moe_expert_ffn and
- * moe_layer_forward call in this process writes as the down projection's input:
- * MOE_GU_SWIGLU (the default) silu(Wg x) * (Wu x) as in step 4 ([R] §1.3), MOE_GU_GATE
- * the gate pre-activation Wg x, MOE_GU_UP the up pre-activation Wu x.  With integer
- * activations and power-of-two group scales every product and partial sum is exact,
- * so Wd (Wg x) matches an exact reference bitwise where SiLU's exp would not.
- * Returns MOE_OK, or MOE_EINVAL for another mode (the mode is then unchanged).
- * Process-wide; calls in flight on other threads see either mode. */
+/* ---- test entry point --------------------------------------------------
+ * Not part of the layer's computation: for tests that check the expert products bit
+ * for bit.  The same as moe_expert_ffn (same arguments, validation, errors and
+ * outputs) except for what the gate/up step hands to the down projection, chosen per
+ * call by gate_up_output: MOE_GU_SWIGLU silu(Wg x) * (Wu x) as in step 4 ([R] §1.3),
+ * MOE_GU_GATE the gate pre-activation Wg x, MOE_GU_UP the up pre-activation Wu x.  With
+ * integer activations and power-of-two group scales every product and partial sum is
+ * exact, so Wd (Wg x) matches an exact reference bitwise where SiLU's exp would not.
+ * Another gate_up_output value gives MOE_EINVAL.  Nothing is kept between calls: no
+ * other call's result depends on this one. */
 #define MOE_GU_SWIGLU 0
 #define MOE_GU_GATE 1
 #define MOE_GU_UP 2
-int moe_test_set_gate_up_output(int32_t mode);
+int moe_expert_ffn_probe(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                         const int32_t *uniq, const int32_t *off, const int32_t *row_tok,
+                         int32_t gate_up_output, float *y_rows, void *ws, size_t ws_bytes,
+                         void *stream);
 
 #ifdef __cplusplus
 }

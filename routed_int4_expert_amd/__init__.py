@@ -22,7 +22,7 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
-           "moe_prof_end", "moe_test_set_gate_up_output")
+           "moe_prof_end", "moe_expert_ffn_probe")
 MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
 
@@ -88,8 +88,8 @@ def lib():
     L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
-    L.moe_test_set_gate_up_output.restype = ctypes.c_int
-    L.moe_test_set_gate_up_output.argtypes = [i32]
+    L.moe_expert_ffn_probe.restype = ctypes.c_int
+    L.moe_expert_ffn_probe.argtypes = [P, vp, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -253,7 +253,17 @@ def moe_prof_end() -> dict:
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].ms)) for i in range(min(n.value, 64))}
 
 
-def moe_test_set_gate_up_output(mode: int):
-    """Test hook: what the gate/up step writes as h (MOE_GU_SWIGLU, MOE_GU_GATE or
-    MOE_GU_UP) for every later call in this process."""
-    _check(lib().moe_test_set_gate_up_output(mode), "moe_test_set_gate_up_output")
+def moe_expert_ffn_probe(layer: Layer, x, un: dict, gate_up_output: int, y_rows=None, ws=None,
+                         stream=None):
+    """Test entry point: moe_expert_ffn with the gate/up step handing the down projection
+    SiLU(g) * u (MOE_GU_SWIGLU), the gate pre-activation (MOE_GU_GATE) or the up
+    pre-activation (MOE_GU_UP), chosen for this call only."""
+    import torch
+    T, k, H = x.shape[0], layer.top_k, layer.hidden
+    y_rows = torch.zeros((max(T * k, 1), H), dtype=torch.float32, device=x.device) if y_rows is None else y_rows
+    ws = layer.workspace(T, x.device) if ws is None else ws
+    _check(lib().moe_expert_ffn_probe(layer.ref(), _ptr(x), T, _ptr(un["n_uniq"]), _ptr(un["uniq"]),
+                                      _ptr(un["off"]), _ptr(un["row_tok"]), int(gate_up_output),
+                                      _ptr(y_rows), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_expert_ffn_probe")
+    return y_rows

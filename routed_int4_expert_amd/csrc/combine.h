@@ -1,8 +1,7 @@
 // combine.h -- step 5 of the MoE layer ("MoE 路由与专家流式加载" §1 and §1.4): the
 // gate-weighted sum of a token's expert outputs plus the always-on shared expert,
-// for four consecutive outputs.  Used by the combine kernel and by the down launch
-// that fuses it, so both add in the same order: slot order in fp32 (fmaf), then
-// the shared expert's output with weight 1.  The bf16 output is the
+// for four consecutive outputs, as the combine kernel computes it: slot order in fp32
+// (fmaf), then the shared expert's output with weight 1.  The bf16 output is the
 // round-to-nearest-even of that fp32.
 #pragma once
 

@@ -100,10 +100,6 @@ static int check_device() {
 
 static int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
 
-// what the gate/up step writes (moe_test_set_gate_up_output); read when a call builds
-// its kernel arguments
-static std::atomic<int> g_gu_out{kGuSwiglu};
-
 // -------------------------------------------------------------- workspace plan
 static size_t router_part_bytes(const moe_layer &L, int T) {
     // largest S(T') * T' over T' <= T, so the plan grows monotonically with T
@@ -289,9 +285,10 @@ static hipError_t run_ffn(const FfnArgs &f, const Plan &p, int E, int k, void *w
 
 static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T,
                         const int32_t *n_uniq, const int32_t *uniq, const int32_t *off,
-                        const int32_t *row_tok, float *y_routed, void *ws) {
+                        const int32_t *row_tok, float *y_routed, void *ws,
+                        int gu_out = kGuSwiglu) {
     FfnArgs a;
-    a.gu_out = g_gu_out.load();
+    a.gu_out = gu_out;
     a.x = x;
     a.n_uniq = n_uniq;
     a.uniq = uniq;
@@ -359,11 +356,12 @@ int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32
                               (hipStream_t)stream));
 }
 
-int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
-                   const int32_t *uniq, const int32_t *off, const int32_t *row_tok, float *y_rows,
-                   void *ws, size_t ws_bytes, void *stream) {
+static int expert_ffn_call(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                           const int32_t *uniq, const int32_t *off, const int32_t *row_tok,
+                           int gu_out, float *y_rows, void *ws, size_t ws_bytes, void *stream) {
     int rc;
     if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (gu_out != kGuSwiglu && gu_out != kGuGate && gu_out != kGuUp) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if ((rc = check_experts(L, true, false))) return rc;
     if (!x || !n_uniq || !uniq || !off || !row_tok || !y_rows) return MOE_EINVAL;
@@ -371,9 +369,24 @@ int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t 
     if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
     if ((rc = check_device())) return rc;
     const Plan p = make_plan(*L, T);
-    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_rows, ws);
+    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_rows, ws, gu_out);
     a.with_shared = 0;
     return launched(run_ffn(a, p, L->n_experts, L->top_k, ws, (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                   const int32_t *uniq, const int32_t *off, const int32_t *row_tok, float *y_rows,
+                   void *ws, size_t ws_bytes, void *stream) {
+    return expert_ffn_call(L, x, T, n_uniq, uniq, off, row_tok, kGuSwiglu, y_rows, ws, ws_bytes,
+                           stream);
+}
+
+int moe_expert_ffn_probe(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,
+                         const int32_t *uniq, const int32_t *off, const int32_t *row_tok,
+                         int32_t gate_up_output, float *y_rows, void *ws, size_t ws_bytes,
+                         void *stream) {
+    return expert_ffn_call(L, x, T, n_uniq, uniq, off, row_tok, gate_up_output, y_rows, ws,
+                           ws_bytes, stream);
 }
 
 int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
@@ -467,12 +480,6 @@ int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t 
     a.H = H;
     a.eps = eps;
     return launched(launch_residual_rmsnorm(a, (hipStream_t)stream));
-}
-
-int moe_test_set_gate_up_output(int32_t mode) {
-    if (mode != MOE_GU_SWIGLU && mode != MOE_GU_GATE && mode != MOE_GU_UP) return MOE_EINVAL;
-    g_gu_out.store(mode);
-    return MOE_OK;
 }
 
 const char *moe_strerror(int code) {

@@ -15,8 +15,8 @@ namespace moe {
 
 constexpr int kWave = 64;
 
-// What the gate/up step writes as h: SiLU(g) * u (the layer), or, for the test hook
-// moe_test_set_gate_up_output, the gate or the up pre-activation.
+// What the gate/up step writes as h: SiLU(g) * u (the layer), or, for the test entry
+// point moe_expert_ffn_probe, the gate or the up pre-activation.
 constexpr int kGuSwiglu = MOE_GU_SWIGLU, kGuGate = MOE_GU_GATE, kGuUp = MOE_GU_UP;
 __device__ __forceinline__ float gate_up_out(int mode, float g, float u) {
     return mode == kGuSwiglu ? g / (1.0f + expf(-g)) * u : (mode == kGuGate ? g : u);

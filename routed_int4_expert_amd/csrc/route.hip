@@ -10,11 +10,16 @@
 // workspace and are added, in slice order, by the selection kernel, so the result
 // does not depend on scheduling.
 //
-// Selection: one wave per token.  Each lane holds up to four experts' sigmoid
-// and biased choice score in fp64; the k picks are k wave-wide argmax
-// reductions (butterfly over the 64 lanes, ties to the lower expert id).  The
-// top-p cut, renormalisation and scaling work on at most 16 picks held
-// identically in every lane.
+// Selection: one wave per token (select_token in select_union.h).  Each lane holds
+// up to four experts' sigmoid gate and biased choice score in fp64, the choice as a
+// monotone 64-bit key.  The k-th largest key is found by a bitwise threshold search
+// (one ballot count per candidate bit, starting below the bits all live keys share).
+// If exactly k keys reach it, those are the picks; otherwise every key above it is
+// picked and the keys equal to it fill the remaining slots in increasing expert id
+// (the result of k rounds of argmax with ties to the lower id).  The picks are then
+// ranked (choice descending, lower id first) by DPP rotations within one row of 16
+// lanes and moved to their slots with ds_permute.  Top-p, renormalisation and
+// scaling work on the at most 16 picks in lanes 0..k-1.
 #include <math.h>
 
 #include "router_gemv.h"

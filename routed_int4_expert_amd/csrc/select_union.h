@@ -156,7 +156,9 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
     kor = wave_or_u64(kor);
     const unsigned long long diff = kand ^ kor;
     const int top = diff ? 63 - __clzll((long long)diff) : -1;  // highest differing bit
-    unsigned long long thr = top >= 63 ? 0ull : kor & ~((2ull << top) - 1ull);
+    // All live keys equal (diff == 0, e.g. a zero token without bias): thr is that key
+    // and there is nothing to search; the equal-key branch below takes the k lowest ids.
+    unsigned long long thr = diff == 0 ? kor : (top >= 63 ? 0ull : kor & ~((2ull << top) - 1ull));
     bool exact = false;
     for (int bit = top; bit >= 0; bit--) {
         const unsigned long long cand = thr | (1ull << bit);
@@ -189,12 +191,14 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
             eq_before += __popcll(eqm);
         }
     }
-    // compact the k picks into LDS (expert order): lane j < k then holds pick j
+    // compact the k picks into LDS (expert order): lane j < k then holds pick j.  Exactly
+    // k experts are selected above; the bound keeps every store inside the k-entry scratch
+    // whatever the keys are.
     int base = 0;
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const unsigned long long sm = __ballot(sel[i]);
-        if (sel[i]) {
+        if (sel[i] && base + __popcll(sm & below) < a.k) {
             const int pos = base + __popcll(sm & below);
             ps->key[pos] = key[i];
             ps->sig[pos] = sig[i];

@@ -69,9 +69,8 @@ int main(int argc, char **argv) {
     EXPECT(moe_expert_ffn(&L, x, 4, i32, i32, i32, NULL, FAKE(0x70000), FAKE(0x40000), ws, NULL) == MOE_EINVAL);
     EXPECT(moe_residual_rmsnorm(FAKE(0x20000), NULL, 4, 100, 1e-6f, FAKE(0x30000), NULL, NULL) == MOE_EINVAL);
 
-    EXPECT(moe_test_set_gate_up_output(3) == MOE_EINVAL);
-    EXPECT(moe_test_set_gate_up_output(MOE_GU_GATE) == MOE_OK);
-    EXPECT(moe_test_set_gate_up_output(MOE_GU_SWIGLU) == MOE_OK);
+    EXPECT(moe_expert_ffn_probe(&L, x, 4, i32, i32, i32, i32, 3, FAKE(0x70000), FAKE(0x40000), ws, NULL) == MOE_EINVAL);
+    EXPECT(moe_expert_ffn_probe(&L, x, 4, i32, i32, i32, NULL, MOE_GU_GATE, FAKE(0x70000), FAKE(0x40000), ws, NULL) == MOE_EINVAL);
     for (int c = -5; c <= 0; c++) EXPECT(strcmp(moe_strerror(c), "unknown error code") != 0);
     EXPECT(strcmp(moe_strerror(99), "unknown error code") == 0);
 

@@ -152,13 +152,20 @@ def test_valid_call_without_gpu_reports_device_error():
     assert call_forward(_layer()) == M.MOE_EDEVICE
 
 
-def test_gate_up_output_hook_validates():
-    """The test hook accepts its three modes and rejects others (no device needed)."""
+def test_expert_ffn_probe_validates():
+    """The probe entry point rejects a gate/up output mode other than its three, before
+    anything else, and otherwise validates like moe_expert_ffn (no device needed)."""
     lib = M.lib()
-    assert lib.moe_test_set_gate_up_output(3) == M.MOE_EINVAL
-    assert lib.moe_test_set_gate_up_output(-1) == M.MOE_EINVAL
-    for mode in (M.MOE_GU_GATE, M.MOE_GU_UP, M.MOE_GU_SWIGLU):
-        assert lib.moe_test_set_gate_up_output(mode) == M.MOE_OK
+    c = _layer()
+    i32 = ctypes.c_void_p(0x50000)
+    wsb = ws_bytes(c, 4)
+    args = lambda mode, x=0x20000: (ctypes.byref(c), ctypes.c_void_p(x), 4, i32, i32, i32, i32, mode,
+                                    ctypes.c_void_p(0x70000), ctypes.c_void_p(0x40000), wsb, None)
+    for mode in (3, -1, 99):
+        assert lib.moe_expert_ffn_probe(*args(mode)) == M.MOE_EINVAL
+    for mode in (M.MOE_GU_SWIGLU, M.MOE_GU_GATE, M.MOE_GU_UP):
+        assert lib.moe_expert_ffn_probe(*args(mode, x=0x20004)) == M.MOE_EALIGN
+        assert lib.moe_expert_ffn_probe(*args(mode, x=0)) == M.MOE_EINVAL
 
 
 def test_missing_library_fails_loudly():

@@ -122,6 +122,70 @@ def test_small_shapes_full_parity(sh):
     full_parity(sh, d, x)
 
 
+def tie_case(kind, T):
+    """A layer and batch whose choice scores tie exactly (identical router rows, equal
+    biases), so the selection's equal-key branch decides the picks and their order.
+
+    tie_topk: six experts with bias +20 lead; five experts with one shared router row
+      and bias +10 tie for the last two of 8 slots (the two lowest ids, 9 and 12, win).
+      Every third token is zero: then the six leaders tie as well.
+    tie_zero: no bias; every third token is zero, so all 256 choices are equal (picks:
+      experts 0..7 in id order).
+    tie_topp: top-2 with top-p 0.5; experts 200 and 7 share a router row, bias 5.3 and
+      5.2, so their gates are equal and top-p keeps exactly one: slot 0 (expert 200).
+    tie_topp4: top-4 with top-p 0.6; experts 1, 4, 7 share a router row with biases
+      7.1 < 7.2 < 7.3 (slot order 7, 4, 1), behind expert 250 (bias 8); where the cut
+      falls inside the equal gates, slot order decides which survive.
+    """
+    E, H = 256, 256
+    k = {"tie_topk": 8, "tie_zero": 8, "tie_topp": 2, "tie_topp4": 4}[kind]
+    top_p = {"tie_topp": 0.5, "tie_topp4": 0.6}.get(kind, 0.0)
+    sh = S.custom(f"{kind}{T}", hidden=H, n_experts=E, ffn=64, shared_ffn=64, top_k=k,
+                  tokens=T, top_p=top_p, routed_scale=2.5, router_std=1 / 16.0)
+    d = S.make_layer(sh, seed=0)
+    wr, b = d["router_w"].copy(), d["router_bias"].copy()
+    if kind == "tie_topk":
+        b[[250, 3, 77, 128, 200, 31]] = 20.0
+        tied = [190, 12, 64, 140, 9]
+        wr[tied] = wr[tied[0]]
+        b[tied] = 10.0
+    elif kind == "tie_topp":
+        wr[7] = wr[200]
+        b[200], b[7] = 5.3, 5.2
+    elif kind == "tie_topp4":
+        wr[[1, 4]] = wr[7]
+        b[250], b[7], b[4], b[1] = 8.0, 7.3, 7.2, 7.1
+    d["router_w"] = wr
+    d["router_bias"] = None if kind == "tie_zero" else b
+    x = S.make_batch(sh, d, seed=0)
+    x[::3] = 0.0
+    return sh, d, x
+
+
+TIE_T = [1, 5, 9, 40, 300]
+
+
+@pytest.mark.parametrize("T", TIE_T, ids=[f"T{t}" for t in TIE_T])
+@pytest.mark.parametrize("kind", ["tie_topk", "tie_zero", "tie_topp", "tie_topp4"])
+def test_exact_ties(kind, T):
+    """Exact ties on every selection path: T = 1 (selection inside the gate/up launch),
+    T = 5 (router gates and keys, select+union in one workgroup), T = 9 (summed router
+    slices, select+union), T = 40 (selection kernel, union in the preparation launch),
+    T = 300 (selection kernel, union kernel).  ids, keff and w must equal the oracle."""
+    sh, d, x = tie_case(kind, T)
+    say(f"ties {kind} T={T}")
+    rids, _, rkeff = R.route(R.Layer(d), x)
+    if kind == "tie_topk":
+        if T > 1:
+            assert rids[1].tolist()[-2:] == [9, 12]
+        assert rids[0].tolist() == [3, 31, 77, 128, 200, 250, 9, 12]  # zero token
+    if kind == "tie_zero":
+        assert rids[0].tolist() == list(range(8))
+    if kind == "tie_topp":
+        assert np.all(rids[:, 0] == 200) and np.all(rkeff == 1)
+    full_parity(sh, d, x)
+
+
 def test_item_row_boundaries():
     """Experts routed exactly 66, 17, 16 and 33 rows and a 66-token shared expert.
 
@@ -175,12 +239,8 @@ def test_exact_expert_products(T, mode):
     xd = torch.from_numpy(x).to(DEV)
     ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
     un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
-    M.moe_test_set_gate_up_output(M.MOE_GU_GATE if mode == "gate" else M.MOE_GU_UP)
-    try:
-        y = M.moe_expert_ffn(layer, xd, un)
-        torch.cuda.synchronize()
-    finally:
-        M.moe_test_set_gate_up_output(M.MOE_GU_SWIGLU)
+    y = M.moe_expert_ffn_probe(layer, xd, un, M.MOE_GU_GATE if mode == "gate" else M.MOE_GU_UP)
+    torch.cuda.synchronize()
     rows = int(ru["off"][-1])
     x64 = x.astype(np.float64)
     ref = np.empty((rows, sh.hidden), np.float64)
