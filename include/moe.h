@@ -151,6 +151,23 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out,
                       int32_t out_dtype, const moe_route_out *dbg, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward with its scratch
+ * in a file-scope device array of MOE_STATIC_SCRATCH_BYTES instead of a caller
+ * workspace.  Same arguments (minus ws and ws_bytes), validation, outputs and errors;
+ * a layer and batch whose workspace (moe_workspace_bytes(L, T)) exceeds the array give
+ * MOE_EWORKSPACE and launch nothing (64 MiB: the GLM-shaped layer up to 128 tokens).
+ * The call allocates nothing: the array is part of the library's device code, held on
+ * every GPU the library runs on until the process ends; its address is looked up once
+ * per device on the first call there (with that device current).  Every call on one
+ * GPU shares that GPU's array, and its contents on entry are ignored (as a workspace's
+ * are), so nothing in it needs clearing; calls that overlap in time on one GPU (other
+ * streams or host threads without ordering) race on it and must be serialised by the
+ * caller.  Devices numbered 64 and above give MOE_EDEVICE. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_static(const moe_layer *L, const float *x, int32_t T, void *out,
+                             int32_t out_dtype, const moe_route_out *dbg, void *stream);
+
 /* Glue between stacked MoE layers -- not a step of the layer itself.  For each of
  * the T rows of H fp32 values: h_out = h + delta (delta NULL: h_out = h), then
  * x_out = h_out / sqrt(mean(h_out^2) + eps) (RMSNorm with unit gain), fp32 with

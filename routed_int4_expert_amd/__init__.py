@@ -22,7 +22,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
-           "moe_prof_end", "moe_expert_ffn_probe")
+           "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static")
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
 
@@ -88,6 +89,8 @@ def lib():
     L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_layer_forward_static.restype = ctypes.c_int
+    L.moe_layer_forward_static.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOutC), vp]
     L.moe_expert_ffn_probe.restype = ctypes.c_int
     L.moe_expert_ffn_probe.argtypes = [P, vp, i32, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     _lib = L
@@ -227,6 +230,24 @@ def moe_layer_forward(layer: Layer, x, out=None, out_dtype: int = MOE_F32, dbg: 
     _check(lib().moe_layer_forward(layer.ref(), _ptr(x), T, _ptr(out), out_dtype,
                                    ctypes.byref(rc) if rc is not None else None, _ptr(ws),
                                    ws.numel(), _stream(stream)), "moe_layer_forward")
+    return out
+
+
+def moe_layer_forward_static(layer: Layer, x, out=None, out_dtype: int = MOE_F32,
+                             dbg: dict | None = None, stream=None):
+    """moe_layer_forward without a workspace: the library's own device scratch array
+    (MOE_STATIC_SCRATCH_BYTES per GPU) serves as scratch; nothing is allocated."""
+    import torch
+    T, H = x.shape[0], layer.hidden
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32,
+                          device=x.device)
+    rc = None
+    if dbg:
+        rc = RouteOutC(**{k: (v.data_ptr() if v is not None else None) for k, v in dbg.items()})
+    _check(lib().moe_layer_forward_static(layer.ref(), _ptr(x), T, _ptr(out), out_dtype,
+                                          ctypes.byref(rc) if rc is not None else None,
+                                          _stream(stream)), "moe_layer_forward_static")
     return out
 
 

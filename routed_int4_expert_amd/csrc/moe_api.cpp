@@ -318,6 +318,85 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     return a;
 }
 
+
+// moe_layer_forward's host-only argument checks (no HIP call): MOE_OK or the error code.
+int layer_forward_validate(const moe_layer *L, const float *x, int32_t T, const void *out,
+                           int32_t out_dtype) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if ((rc = check_router(L)) || (rc = check_experts(L, true, true))) return rc;
+    if (!x || !out) return MOE_EINVAL;
+    if (!aligned16(x) || ((uintptr_t)out & 7u)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+int device_ok() { return check_device(); }
+
+// The launch sequence of the layer on a validated call (T > 0, ws large enough for T).
+int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
+                      const moe_route_out *dbg, void *ws, hipStream_t st) {
+    const Plan p = make_plan(*L, T);
+    moe_route_out d;
+    memset(&d, 0, sizeof(d));
+    if (dbg) d = *dbg;
+    int32_t *ids = d.ids ? d.ids : at<int32_t>(ws, p.ids);
+    float *w = d.w ? d.w : at<float>(ws, p.w);
+    int32_t *keff = d.keff ? d.keff : at<int32_t>(ws, p.keff);
+    int32_t *n_uniq = d.n_uniq ? d.n_uniq : at<int32_t>(ws, p.n_uniq);
+    int32_t *uniq = d.uniq ? d.uniq : at<int32_t>(ws, p.uniq);
+    int32_t *off = d.off ? d.off : at<int32_t>(ws, p.off);
+    int32_t *row_tok = d.row_tok ? d.row_tok : at<int32_t>(ws, p.row_tok);
+    int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
+
+    hipError_t e;
+    // one token: selection and union run inside the gate/up launch
+    const bool sel_in_ffn = T == 1;
+    float *y_routed = at<float>(ws, p.y_routed);
+    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
+    if (sel_in_ffn) {
+        e = run_logits(*L, p, x, T, ws, st);
+    } else if (T <= kSelectUnionTokens) {
+        // small batch: selection and union in one workgroup
+        e = run_logits(*L, p, x, T, ws, st);
+        if (e == hipSuccess)
+            e = launch_select_union(select_args(*L, p, T, ids, w, keff, ws),
+                                    union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
+    } else {
+        e = run_route(*L, p, x, T, ids, w, keff, ws, st);
+        // the union inside the first matrix-core preparation launch when it fits there
+        if (union_in_prep_fits(L->n_experts, T, L->top_k)) {
+            a.union_in_prep = 1;
+            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
+        } else if (e == hipSuccess) {
+            e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
+        }
+    }
+    CombineArgs c;
+    c.w = w;
+    c.keff = keff;
+    c.pick_row = pick_row;
+    c.y_routed = y_routed;
+    c.y_shared = L->shared_ffn > 0 ? at<float>(ws, p.y_shared) : nullptr;
+    c.out = out;
+    c.T = T;
+    c.H = L->hidden;
+    c.k = L->top_k;
+    c.out_bf16 = out_dtype == MOE_BF16;
+    if (e == hipSuccess) {
+        if (sel_in_ffn) {
+            a.fuse_select = 1;
+            a.sel = select_args(*L, p, T, ids, w, keff, ws);
+            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
+        }
+        e = run_ffn(a, p, L->n_experts, L->top_k, ws, st);
+    }
+    if (e == hipSuccess) e = launch_combine(c, st);
+    return launched(e);
+}
+
+
 }  // namespace moe
 
 using namespace moe;
@@ -392,72 +471,11 @@ int moe_expert_ffn_probe(const moe_layer *L, const float *x, int32_t T, const in
 int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
                       const moe_route_out *dbg, void *ws, size_t ws_bytes, void *stream) {
     int rc;
-    if ((rc = check_dims(L)) || (rc = check_T(T))) return rc;
-    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_EINVAL;
+    if ((rc = layer_forward_validate(L, x, T, out, out_dtype))) return rc;
     if (T == 0) return MOE_OK;
-    if ((rc = check_router(L)) || (rc = check_experts(L, true, true))) return rc;
-    if (!x || !out) return MOE_EINVAL;
-    if (!aligned16(x) || ((uintptr_t)out & 7u)) return MOE_EALIGN;
     if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
     if ((rc = check_device())) return rc;
-    const Plan p = make_plan(*L, T);
-    hipStream_t st = (hipStream_t)stream;
-    moe_route_out d;
-    memset(&d, 0, sizeof(d));
-    if (dbg) d = *dbg;
-    int32_t *ids = d.ids ? d.ids : at<int32_t>(ws, p.ids);
-    float *w = d.w ? d.w : at<float>(ws, p.w);
-    int32_t *keff = d.keff ? d.keff : at<int32_t>(ws, p.keff);
-    int32_t *n_uniq = d.n_uniq ? d.n_uniq : at<int32_t>(ws, p.n_uniq);
-    int32_t *uniq = d.uniq ? d.uniq : at<int32_t>(ws, p.uniq);
-    int32_t *off = d.off ? d.off : at<int32_t>(ws, p.off);
-    int32_t *row_tok = d.row_tok ? d.row_tok : at<int32_t>(ws, p.row_tok);
-    int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
-
-    hipError_t e;
-    // one token: selection and union run inside the gate/up launch
-    const bool sel_in_ffn = T == 1;
-    float *y_routed = at<float>(ws, p.y_routed);
-    FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
-    if (sel_in_ffn) {
-        e = run_logits(*L, p, x, T, ws, st);
-    } else if (T <= kSelectUnionTokens) {
-        // small batch: selection and union in one workgroup
-        e = run_logits(*L, p, x, T, ws, st);
-        if (e == hipSuccess)
-            e = launch_select_union(select_args(*L, p, T, ids, w, keff, ws),
-                                    union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row), st);
-    } else {
-        e = run_route(*L, p, x, T, ids, w, keff, ws, st);
-        // the union inside the first matrix-core preparation launch when it fits there
-        if (union_in_prep_fits(L->n_experts, T, L->top_k)) {
-            a.union_in_prep = 1;
-            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
-        } else if (e == hipSuccess) {
-            e = run_union(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row, st);
-        }
-    }
-    CombineArgs c;
-    c.w = w;
-    c.keff = keff;
-    c.pick_row = pick_row;
-    c.y_routed = y_routed;
-    c.y_shared = L->shared_ffn > 0 ? at<float>(ws, p.y_shared) : nullptr;
-    c.out = out;
-    c.T = T;
-    c.H = L->hidden;
-    c.k = L->top_k;
-    c.out_bf16 = out_dtype == MOE_BF16;
-    if (e == hipSuccess) {
-        if (sel_in_ffn) {
-            a.fuse_select = 1;
-            a.sel = select_args(*L, p, T, ids, w, keff, ws);
-            a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
-        }
-        e = run_ffn(a, p, L->n_experts, L->top_k, ws, st);
-    }
-    if (e == hipSuccess) e = launch_combine(c, st);
-    return launched(e);
+    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream);
 }
 
 int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t H, float eps,

@@ -194,6 +194,15 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st);
 bool union_in_prep_fits(int E, int T, int k);
 
 
+// moe_layer_forward in two parts: host-only argument checks (no HIP call) and, for a
+// validated call with T > 0 and a large enough workspace on a checked device, the
+// launch sequence.  device_ok: the lazy once-per-device gfx950 check.
+int layer_forward_validate(const moe_layer *L, const float *x, int32_t T, const void *out,
+                           int32_t out_dtype);
+int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
+                      const moe_route_out *dbg, void *ws, hipStream_t st);
+int device_ok();
+
 // Bracketing HIP events around one kernel launch while moe_prof_begin() is active.
 struct ProfScope {
     ProfScope(const char *name, hipStream_t st);

@@ -1,7 +1,7 @@
 /* Drives the host side of the C ABI (include/moe.h) for a library built with
  * AddressSanitizer and UndefinedBehaviorSanitizer on its host code
- * (tests/test_sanitizers.py): workspace plans, every validation error, the test hook
- * and error strings.  No call reaches a kernel launch: each fails validation first,
+ * (tests/test_sanitizers.py): workspace plans, every validation error, the test entry
+ * point, the static-scratch forward's size limit and error strings.  No call reaches a kernel launch: each fails validation first,
  * except one well-formed call made only when argv[1] is "nogpu", where it must report
  * MOE_EDEVICE.  Pointers are fake, aligned addresses that validation never
  * dereferences.  Exits 0 when every call returns what it should. */
@@ -71,10 +71,23 @@ int main(int argc, char **argv) {
 
     EXPECT(moe_expert_ffn_probe(&L, x, 4, i32, i32, i32, i32, 3, FAKE(0x70000), FAKE(0x40000), ws, NULL) == MOE_EINVAL);
     EXPECT(moe_expert_ffn_probe(&L, x, 4, i32, i32, i32, NULL, MOE_GU_GATE, FAKE(0x70000), FAKE(0x40000), ws, NULL) == MOE_EINVAL);
+    /* the static-scratch forward: validation as moe_layer_forward, then the size limit */
+    EXPECT(moe_layer_forward_static(&L, NULL, 4, out, MOE_F32, NULL, NULL) == MOE_EINVAL);
+    EXPECT(moe_layer_forward_static(&L, x, 4, out, 7, NULL, NULL) == MOE_EINVAL);
+    EXPECT(moe_layer_forward_static(&L, FAKE(0x20004), 4, out, MOE_F32, NULL, NULL) == MOE_EALIGN);
+    EXPECT(moe_layer_forward_static(NULL, x, 4, out, MOE_F32, NULL, NULL) == MOE_EINVAL);
+    EXPECT(moe_layer_forward_static(&L, x, 0, out, MOE_F32, NULL, NULL) == MOE_OK);
+    EXPECT(moe_layer_forward_static(&L, x, MOE_MAX_TOKENS + 1, out, MOE_F32, NULL, NULL) == MOE_EUNSUPPORTED);
+    B = L; B.hidden = 1024; B.ffn = 512; B.shared_ffn = 512; B.n_experts = 32; B.top_k = 8;
+    EXPECT(moe_workspace_bytes(&B, MOE_MAX_TOKENS) > (size_t)MOE_STATIC_SCRATCH_BYTES);
+    EXPECT(moe_layer_forward_static(&B, x, MOE_MAX_TOKENS, out, MOE_F32, NULL, NULL) == MOE_EWORKSPACE);
     for (int c = -5; c <= 0; c++) EXPECT(strcmp(moe_strerror(c), "unknown error code") != 0);
     EXPECT(strcmp(moe_strerror(99), "unknown error code") == 0);
 
-    if (argc > 1 && strcmp(argv[1], "nogpu") == 0) EXPECT(forward(&L, 4, ws, x, out) == MOE_EDEVICE);
+    if (argc > 1 && strcmp(argv[1], "nogpu") == 0) {
+        EXPECT(forward(&L, 4, ws, x, out) == MOE_EDEVICE);
+        EXPECT(moe_layer_forward_static(&L, x, 4, out, MOE_F32, NULL, NULL) == MOE_EDEVICE);
+    }
     if (fails) return 1;
     printf("abi sanitizer run ok\n");
     return 0;
