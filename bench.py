@@ -3,15 +3,20 @@
 
 A step is one whole layer forward (router, selection, union, int4-gs64 expert
 FFNs, combine + shared expert) on one batch of synthetic tokens that are
-already resident in HBM.  The default workload is the GLM-5.2-shaped decode
-layer: H=6144, 256 routed experts (F=2048) + 1 shared expert (Fs=2048), top-8,
-norm_topk, routed scale 2.5, one token per step, bf16 output.  Each step uses
-another token of a 64-token pool and another of ``--layers`` resident copies
-of the layer (distinct HBM, experts permuted per copy), so neither the routed
-experts nor the shared expert and router can be served from the 256 MB
-last-level cache.
+already resident in HBM.  The headline workload (``value``) is the
+GLM-5.2-shaped decode layer: H=6144, 256 routed experts (F=2048) + 1 shared
+expert (Fs=2048), top-8, norm_topk, routed scale 2.5, one token per step, bf16
+output.  Each step uses another token of a 64-token pool and another of several
+resident copies of the layer (distinct HBM, experts permuted per copy), so
+neither the routed experts nor the shared expert and router can be served from
+the 256 MB last-level cache.
 
-Prints one JSON line; progress goes to stderr.
+By default every workload is measured in the same run and reported under
+``workloads`` in the one JSON line (small-expert decode, 512-token prefill,
+the 16-layer stack and the compute-bound grouped-GEMM microbenchmark), each with
+its step time (eager, per-step median/p10/p90, graph replay, cache-hot where it
+applies), the roofline of its dominant kernel and MFMA utilisation.
+``--workload NAME`` measures one workload only.  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ import ctypes
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -30,7 +36,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-I8_PEAK_OPS = 5.0e15       # dense int8 MFMA (the matrix-core path's arithmetic)
+BF16_PEAK_FLOPS = 2.5e15   # dense bf16 MFMA (the peak the utilisation target names)
+I8_PEAK_OPS = 5.0e15       # dense int8 MFMA (the arithmetic the matrix-core path runs)
+
+WORKLOADS = {
+    "glm_decode": "MoE layer H=6144, 256 routed experts F=2048 + 1 shared Fs=2048, int4-gs64, "
+                  "top-8 noaux_tc, norm_topk, routed_scale 2.5, 1 token/step, bf16 out",
+    "small_decode": "MoE layer H=2048, 256 routed experts F=512 + 1 shared Fs=512, int4-gs64, top-8, "
+                    "norm_topk, 64 tokens/step, fp32 out",
+    "glm_prefill": "the GLM-shaped layer, 512 tokens/step whose router logits are a popularity-skewed "
+                   "Gumbel sample (union ~200 experts), fp32 out",
+    "glm_stack16": "16 GLM-shaped layers resident (distinct HBM), 32 tokens/step, top-p 0.7, "
+                   "Zipf(1.1) bias, RMSNorm + residual between layers, fp32",
+    "glm_rows256": "grouped-GEMM microbenchmark: 16 GLM-shaped experts + shared, 512 tokens top-8 "
+                   "(~256 rows per expert), fp32 out",
+}
+DEFAULT_ORDER = ("glm_decode", "small_decode", "glm_prefill", "glm_stack16", "glm_rows256")
+# resident layer copies cycled per step (enough distinct HBM to defeat the last-level cache)
+COPIES = {"glm_decode": 8, "small_decode": 8, "glm_prefill": 2, "glm_stack16": 16, "glm_rows256": 2}
 
 
 def log(msg):
@@ -42,6 +65,33 @@ def q4_bytes(n, k):
     return n * k // 2 + n * (k // 64) * 4
 
 
+def host_cpu():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+_BANKS = {}
+
+
+def bank_for(sh):
+    """The host expert bank of a shape (cached: the GLM-shaped workloads share one)."""
+    from routed_int4_expert_amd import synth as S
+    key = (sh.bank or sh.name, sh.n_experts, sh.hidden, sh.ffn, sh.shared_ffn)
+    if key not in _BANKS:
+        t0 = time.time()
+        _BANKS[key] = S.Bank(sh, seed=0)
+        log(f"expert bank {key[0]} x{sh.n_experts} generated on the host in {time.time() - t0:.1f} s")
+    return _BANKS[key]
+
+
 def build_layers(sh, n_layers, dev, shared_router=False):
     """n_layers resident copies of the layer: distinct HBM, experts permuted per copy.
     With shared_router every copy uses copy 0's router (the prefill tokens are built
@@ -50,9 +100,7 @@ def build_layers(sh, n_layers, dev, shared_router=False):
     import routed_int4_expert_amd as M
     from routed_int4_expert_amd import synth as S
 
-    t0 = time.time()
-    bank = S.Bank(sh, seed=0)
-    log(f"expert bank generated on the host in {time.time() - t0:.1f} s")
+    bank = bank_for(sh)
     base = {k: torch.from_numpy(getattr(bank, k)).to(dev) for k in S.Bank.ROUTED + S.Bank.SHARED}
     layers, routers = [], []
     for l in range(n_layers):
@@ -67,55 +115,53 @@ def build_layers(sh, n_layers, dev, shared_router=False):
     del base
     torch.cuda.synchronize()
     gb = n_layers * (sh.n_experts + 1) * S.expert_bytes(sh) / 1e9
-    log(f"{n_layers} resident layer copies ready ({gb:.1f} GB of experts)")
+    log(f"{sh.name}: {n_layers} resident layer copies ready ({gb:.1f} GB of experts)")
     return bank, layers, routers
 
 
-def cpu_baseline(sh, bank, routers, xs_host, seconds, per_token_layers=1):
-    """The CPU oracle (plain C, fp64) on the same workload, one token at a time."""
+def cpu_baseline(sh, bank, routers, xs_host, seconds):
+    """The CPU oracle (plain C, fp64) on single-token forwards of the same layer copies:
+    with the host's OpenMP threads over FFN rows, then on one thread."""
     import oracle as R
     from routed_int4_expert_amd import synth as S
 
-    Ls = []
-    for l in range(per_token_layers):
-        d = S.make_layer(sh, seed=0, layer=l, bank=bank)
-        d["router_w"], d["router_bias"] = routers[l]
-        Ls.append(R.Layer(d))
-    # tokens of the pool in turn until the time budget is spent (timing excludes set-up)
-    n, t0 = 0, time.time()
-    while n == 0 or time.time() - t0 < seconds:
-        i = n % xs_host.shape[0]
-        for L in Ls:
-            R.layer_forward(L, xs_host[i:i + 1])
-        n += 1
-    dt = time.time() - t0
+    # layer copy 0 (its experts are the bank's own arrays: no host copy)
+    d = S.make_layer(sh, seed=0, layer=0, bank=bank)
+    d["router_w"], d["router_bias"] = routers[0]
+    Ls = [R.Layer(d)]
+
+    def run(budget):
+        n, t0 = 0, time.time()
+        while n == 0 or time.time() - t0 < budget:
+            i = n % xs_host.shape[0]
+            R.layer_forward(Ls[n % len(Ls)], xs_host[i:i + 1])
+            n += 1
+        return n, time.time() - t0
+
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    what = "single-token forwards" if per_token_layers == 1 else \
-        f"tokens each through {per_token_layers} layers (no glue)"
-    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{n} {what} of the same layer copies, {dt:.1f} s, fp64 C oracle "
-                       "with OpenMP over FFN rows")
-
-
-WORKLOADS = {
-    "glm_decode": "MoE layer H=6144, 256 routed experts F=2048 + 1 shared Fs=2048, int4-gs64, "
-                  "top-8 noaux_tc, norm_topk, routed_scale 2.5, 1 token/step, bf16 out",
-    "glm_prefill": "the same layer, 512 tokens/step whose router logits are a popularity-skewed "
-                   "Gumbel sample (union ~200 experts), fp32 out",
-    "small_decode": "MoE layer H=2048, 256 routed experts F=512 + 1 shared Fs=512, int4-gs64, top-8, "
-                    "norm_topk, 64 tokens/step, fp32 out",
-    "glm_stack16": "16 GLM-shaped layers resident (distinct HBM), 32 tokens/step, top-p 0.7, "
-                   "Zipf(1.1) bias, RMSNorm + residual between layers, fp32",
-}
+    n, dt = run(seconds)
+    rec = dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+               sample=f"{n} single-token forwards of the GLM-shaped decode layer (copy 0), {dt:.1f} s, "
+                      f"fp64 C oracle with OpenMP over FFN rows ({cores} threads)",
+               cpu_model=host_cpu(), host_cpus_visible=os.cpu_count())
+    try:  # one thread: the oracle's OpenMP runtime is the process's libgomp
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        n1, dt1 = run(seconds / 2)
+        gomp.omp_set_num_threads(cores)
+        rec["single_thread"] = dict(value=n1 / dt1, unit="tokens/s", cores=1,
+                                    sample=f"{n1} single-token forwards, {dt1:.1f} s, one thread")
+    except OSError:
+        pass
+    return rec
 
 
 def counted_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs (profiles/hbm_counters.json, calibrated against a copy of known size), or None
     when there is none for this workload or the kernel's source changed since."""
-    root = os.path.dirname(os.path.abspath(__file__))
     try:
-        with open(os.path.join(root, "profiles", "hbm_counters.json")) as f:
+        with open(os.path.join(ROOT, "profiles", "hbm_counters.json")) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
@@ -123,7 +169,7 @@ def counted_traffic(workload, kernel):
         if e.get("workload") != workload or e.get("kernel") != kernel:
             continue
         try:
-            with open(os.path.join(root, e["source"]), "rb") as f:
+            with open(os.path.join(ROOT, e["source"]), "rb") as f:
                 if hashlib.sha256(f.read()).hexdigest() != e["source_sha256"]:
                     return None
         except OSError:
@@ -132,15 +178,296 @@ def counted_traffic(workload, kernel):
     return None
 
 
+def read_probe(gib=4.0, reps=10):
+    """The practical HBM read ceiling: moe_probe_read over a `gib` GiB buffer, timed with
+    HIP events on the launch stream; the best of a few grid sizes."""
+    import torch
+    import routed_int4_expert_amd as M
+    nbytes = int(gib * (1 << 30))
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    best = None
+    for blocks in (2048, 4096, 8192):
+        def go():
+            rc = M.lib().moe_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 0x9E3779B9,
+                                        ctypes.c_void_p(sink.data_ptr()), blocks, sp)
+            if rc != M.MOE_OK:
+                raise M.MoeError(rc, "moe_probe_read")
+        go()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            go()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbps > best["read_gbps"]:
+            best = dict(read_gbps=gbps, bytes=nbytes, blocks=blocks, ms=ms)
+    del buf
+    torch.cuda.empty_cache()
+    best["frac_of_peak"] = best["read_gbps"] / HBM_PEAK_GBPS
+    return best
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a, dtype=np.float64), q))
+
+
+def run_workload(wl, args, dev):
+    """Measure one workload; returns its record (the fields of the JSON line)."""
+    import torch
+    import routed_int4_expert_amd as M
+    from routed_int4_expert_amd import synth as S
+
+    sh = S.SHAPES[wl]
+    T, H, F, Fs, E = sh.tokens, sh.hidden, sh.ffn, sh.shared_ffn, sh.n_experts
+    stack = wl == "glm_stack16"
+    nlay = COPIES[wl] if args.layers is None else (sh.layers if stack else args.layers)
+    bank, layers, routers = build_layers(sh, nlay, dev, shared_router=(wl == "glm_prefill"))
+    if wl == "glm_prefill":
+        npool = 2
+        xs_host = np.concatenate([S.gumbel_skew_batch(sh, T, routers[0][0], routers[0][1], 0, p)[0]
+                                  for p in range(npool)])
+    else:
+        npool = max(1, 64 // T)
+        xs_host = S.tokens(sh, npool * T, seed=0, pool=0)
+    xpool = torch.from_numpy(xs_host).to(dev)
+    out_bf16 = wl == "glm_decode"
+    out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
+    ws = layers[0].workspace(T, dev)
+    per_step = nlay if stack else 1
+    n_pct = max(args.steps, 30)
+    nrec = (args.warmup + args.steps + args.steps + n_pct + 2) * per_step
+    nu = torch.zeros((nrec,), dtype=torch.int32, device=dev)
+    offb = torch.zeros((nrec, E + 1), dtype=torch.int32, device=dev)
+    hbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
+    xbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    fwd = M.lib().moe_layer_forward
+    glue = M.lib().moe_residual_rmsnorm
+    xptr = [ctypes.c_void_p(xpool.data_ptr() + (i * T * H * 4)) for i in range(npool)]
+    dbgs = [M.RouteOutC(n_uniq=nu.data_ptr() + 4 * r, off=offb.data_ptr() + 4 * (E + 1) * r)
+            for r in range(nrec)]
+    refs = [lay.ref() for lay in layers]
+    outp, wsp, wsn = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    hp, xp = ctypes.c_void_p(hbuf.data_ptr()), ctypes.c_void_p(xbuf.data_ptr())
+    odt = M.MOE_BF16 if out_bf16 else M.MOE_F32
+
+    def check(rc, what):
+        if rc != M.MOE_OK:
+            raise M.MoeError(rc, what)
+
+    def step(i, rec, stream, copy=None, tok=None):
+        """Step i: layer copy i mod copies, token batch i mod pool (unless pinned)."""
+        c = i % len(refs) if copy is None else copy
+        b = i % npool if tok is None else tok
+        if not stack:
+            check(fwd(refs[c], xptr[b], T, outp, odt, ctypes.byref(dbgs[rec]), wsp, wsn, stream),
+                  "moe_layer_forward")
+            return
+        # the stack: h = tokens; per layer x = RMSNorm(h); out = MoE(x); h += out (next glue)
+        check(glue(xptr[b], None, T, H, ctypes.c_float(1e-6), hp, xp, stream), "glue")
+        for l in range(nlay):
+            if l > 0:
+                check(glue(hp, outp, T, H, ctypes.c_float(1e-6), hp, xp, stream), "glue")
+            check(fwd(refs[l], xp, T, outp, odt, ctypes.byref(dbgs[rec * nlay + l]), wsp, wsn,
+                      stream), "moe_layer_forward")
+
+    cur = torch.cuda.current_stream()
+    stream = ctypes.c_void_p(cur.cuda_stream)
+    rec = 0
+    for i in range(args.warmup):
+        step(i, rec, stream)
+        rec += 1
+    torch.cuda.synchronize()
+    log(f"{wl}: warmup {args.warmup} steps done")
+
+    # timed region: K steps bracketed by synchronisation and HIP events on the launch stream
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_ev.record()
+    rec0 = rec
+    for i in range(args.steps):
+        step(args.warmup + i, rec, stream)
+        rec += 1
+    e_ev.record()
+    torch.cuda.synchronize()
+    ms_step = s_ev.elapsed_time(e_ev) / args.steps
+    stat_sl = slice(rec0 * per_step, rec * per_step)
+    log(f"{wl}: timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+
+    # per-step HIP events (distribution)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_pct)]
+    for i in range(n_pct):
+        evs[i][0].record()
+        step(args.warmup + i, rec, stream)
+        evs[i][1].record()
+        rec += 1
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+
+    # per-kernel HIP events on the launch stream (the same steps again)
+    M.moe_prof_begin()
+    for i in range(args.steps):
+        step(args.warmup + i, rec, stream)
+        rec += 1
+    kern = M.moe_prof_end()
+    torch.cuda.synchronize()
+
+    # graph replay: G consecutive steps captured once, replayed
+    G = 8 if T * per_step <= 64 and not stack else 1
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            step(0, rec, ctypes.c_void_p(side.cuda_stream))
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(G):
+                step(i, rec, cs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // G)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * G)
+        del g
+    except Exception as exc:  # graph timing is reported when it works, never required
+        log(f"{wl}: graph replay not timed ({exc})")
+
+    # cache-hot: one layer copy and one batch every step (the weights stay in the caches
+    # as far as they fit)
+    hot_ms = None
+    if not stack:
+        for i in range(3):
+            step(0, rec, stream, copy=0, tok=0)
+        h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        h0.record()
+        for i in range(args.steps):
+            step(0, rec, stream, copy=0, tok=0)
+        h1.record()
+        torch.cuda.synchronize()
+        hot_ms = h0.elapsed_time(h1) / args.steps
+
+    n_uniq = nu[stat_sl].cpu().numpy().astype(np.float64)
+    rows = offb[stat_sl, E].cpu().numpy().astype(np.float64)
+    exp_b, sh_b = S.expert_bytes(sh), S.expert_bytes(sh, Fs)
+    # algorithmic bytes and flops per step: union experts + shared expert + router + x + out
+    step_bytes = per_step * (n_uniq.mean() * exp_b + sh_b + E * H * 4 + E * 4 + T * H * 4
+                             + T * H * (2 if out_bf16 else 4))
+    step_flops = per_step * (2.0 * 3 * H * F * rows.mean() + 2.0 * 3 * H * Fs * T + 2.0 * T * E * H)
+    ffn_flops = per_step * (2.0 * 3 * H * (F * rows.mean() + Fs * T))
+    gemv = T <= 4
+    kernels = {}
+    # gate/up: every unit's codes + scales, x read, h written; down: codes + scales, h read, y written
+    units = {
+        "gateup": dict(name="ffn_gateup" if gemv else "ffn_gateup_mfma",
+                       bytes=(n_uniq.mean() * 2 * q4_bytes(F, H) + 2 * q4_bytes(Fs, H) + T * H * 4
+                              + (rows.mean() * F + T * Fs) * 4),
+                       flops=2.0 * 2 * H * (F * rows.mean() + Fs * T)),
+        "down": dict(name="ffn_down" if gemv else "ffn_down_mfma",
+                     bytes=(n_uniq.mean() * q4_bytes(H, F) + q4_bytes(H, Fs)
+                            + (rows.mean() * F + T * Fs) * 4 + (rows.mean() + T) * H * 4),
+                     flops=2.0 * H * (F * rows.mean() + Fs * T)),
+    }
+    for role, u in units.items():
+        launches, ms = kern.get(u["name"], (0, float("nan")))
+        avg = ms / max(launches, 1)
+        ach = u["bytes"] / (avg * 1e-3) / 1e9
+        kernels[role] = {
+            "kernel": u["name"], "bound": "hbm", "achieved": float(ach), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": float(ach / HBM_PEAK_GBPS),
+            "traffic": counted_traffic(wl, u["name"]),
+            "bytes_per_launch": float(u["bytes"]), "avg_launch_us": float(avg * 1e3),
+            "useful_tflops": float(u["flops"] / (avg * 1e-3) / 1e12),
+            "mfma_util_vs_bf16_dense": float(u["flops"] / (avg * 1e-3) / BF16_PEAK_FLOPS),
+            "mfma_util_vs_i8_dense": float(u["flops"] / (avg * 1e-3) / I8_PEAK_OPS),
+        }
+    gu = kernels["gateup"]
+    rec_out = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        # the expert FFNs' arithmetic: int4 codes times 16-bit fixed-point activations
+        # (carried as two int8 limbs) with exact int32 group sums (v_dot4 in the decode
+        # GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
+        "dtype": "i4xfx16-i32-f32acc",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl}: {WORKLOADS[wl]}",
+            "tokens_per_step": T,
+            "layers_per_step": per_step,
+            "layer_copies_cycled": nlay,
+            "mean_union_experts": float(n_uniq.mean()),
+            "mean_routed_rows": float(rows.mean()),
+            "algorithmic_bytes_per_step": float(step_bytes),
+            "algorithmic_flops_per_step": float(step_flops),
+        },
+        "timing": {
+            "eager_ms_per_step": ms_step,
+            "median_ms": pct(per, 50), "p10_ms": pct(per, 10), "p90_ms": pct(per, 90),
+            "per_step_samples": n_pct,
+            "graph_replay_ms_per_step": graph_ms,
+            "graph_steps_per_replay": G,
+            "cache_hot_ms_per_step": hot_ms,
+        },
+        "step_roofline": {
+            "hbm_gbps": float(step_bytes / (ms_step * 1e-3) / 1e9),
+            "frac_of_hbm_peak": float(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS),
+            "useful_tflops": float(step_flops / (ms_step * 1e-3) / 1e12),
+            "ffn_mfma_util_vs_bf16_dense": float(ffn_flops / (ms_step * 1e-3) / BF16_PEAK_FLOPS),
+        },
+        "roofline": {
+            "kernel": f"{gu['kernel']} (gate+up of every union expert and the shared expert, "
+                      "SiLU*up epilogue)",
+            "bound": "hbm", "achieved": gu["achieved"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": gu["frac"], "traffic": gu["traffic"],
+            "bytes_per_launch": gu["bytes_per_launch"], "avg_launch_us": gu["avg_launch_us"],
+            "mfma_util_vs_bf16_dense": gu["mfma_util_vs_bf16_dense"],
+            "mfma_util_vs_i8_dense": gu["mfma_util_vs_i8_dense"],
+        },
+        "kernel_rooflines": kernels,
+        "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
+    }
+    extra = dict(bank=bank, routers=routers, xs_host=xs_host, sh=sh)
+    del layers, ws, xpool, out, hbuf, xbuf, nu, offb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec_out, extra
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="glm_decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--layers", type=int, default=8, help="resident layer copies cycled per step")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=None,
+                    help="resident layer copies cycled per step (default: per workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-long device buffer 13 times (calibrates the HBM "
                          "byte counters against a transfer of known size) and exit")
@@ -151,8 +478,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import routed_int4_expert_amd as M
-    from routed_int4_expert_amd import synth as S
 
     if args.copy_probe:
         n = args.copy_probe // 4
@@ -175,146 +500,29 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    wl = args.workload
-    sh = S.SHAPES[wl]
-    T, H, F, Fs, E, k = sh.tokens, sh.hidden, sh.ffn, sh.shared_ffn, sh.n_experts, sh.top_k
-    stack = wl == "glm_stack16"
-    nlay = sh.layers if stack else args.layers
-    bank, layers, routers = build_layers(sh, nlay, dev, shared_router=(wl == "glm_prefill"))
-    # token pool: decode shapes draw independent tokens; prefill batches are built for the router
-    if wl == "glm_prefill":
-        npool = 2
-        xs_host = np.concatenate([S.gumbel_skew_batch(sh, T, routers[0][0], routers[0][1], 0, p)[0]
-                                  for p in range(npool)])
-    else:
-        npool = max(1, 64 // T)
-        xs_host = S.tokens(sh, npool * T, seed=0, pool=0)
-    xpool = torch.from_numpy(xs_host).to(dev)
-    out_bf16 = wl == "glm_decode"
-    out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
-    ws = layers[0].workspace(T, dev)
-    per_step = nlay if stack else 1
-    nsteps = args.warmup + args.steps
-    ncall = (nsteps + args.steps) * per_step
-    nu = torch.zeros((ncall,), dtype=torch.int32, device=dev)
-    offb = torch.zeros((ncall, E + 1), dtype=torch.int32, device=dev)
-    hbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
-    xbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
-
-    # per-call C arguments prepared up front, so the host issues launches as fast as it can
-    fwd = M.lib().moe_layer_forward
-    glue = M.lib().moe_residual_rmsnorm
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    xptr = [ctypes.c_void_p(xpool.data_ptr() + (i * T * H * 4)) for i in range(npool)]
-    dbgs = [M.RouteOutC(n_uniq=nu.data_ptr() + 4 * r, off=offb.data_ptr() + 4 * (E + 1) * r)
-            for r in range(ncall)]
-    refs = [lay.ref() for lay in layers]
-    outp, wsp, wsn = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel()
-    hp, xp = ctypes.c_void_p(hbuf.data_ptr()), ctypes.c_void_p(xbuf.data_ptr())
-    odt = M.MOE_BF16 if out_bf16 else M.MOE_F32
-
-    def check(rc, what):
-        if rc != M.MOE_OK:
-            raise M.MoeError(rc, what)
-
-    def step(i, rec):
-        if not stack:
-            check(fwd(refs[i % len(refs)], xptr[i % npool], T, outp, odt, ctypes.byref(dbgs[rec]),
-                      wsp, wsn, stream), "moe_layer_forward")
-            return
-        # the stack: h = tokens; per layer x = RMSNorm(h); out = MoE(x); h += out (next glue)
-        check(glue(xptr[i % npool], None, T, H, ctypes.c_float(1e-6), hp, xp, stream), "glue")
-        for l in range(nlay):
-            if l > 0:
-                check(glue(hp, outp, T, H, ctypes.c_float(1e-6), hp, xp, stream), "glue")
-            check(fwd(refs[l], xp, T, outp, odt, ctypes.byref(dbgs[rec * nlay + l]), wsp, wsn,
-                      stream), "moe_layer_forward")
-
-    for i in range(args.warmup):
-        step(i, i)
-    torch.cuda.synchronize()
-    log(f"{wl}: warmup {args.warmup} steps done")
-
-    # timed region: K steps bracketed by synchronisation and HIP events on the launch stream
-    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s_ev.record()
-    for i in range(args.steps):
-        step(args.warmup + i, args.warmup + i)
-    e_ev.record()
-    torch.cuda.synchronize()
-    ms_step = s_ev.elapsed_time(e_ev) / args.steps
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
-
-    # the same steps again with per-kernel HIP events on the launch stream
-    M.moe_prof_begin()
-    for i in range(args.steps):
-        step(args.warmup + i, nsteps + i)
-    kern = M.moe_prof_end()
-    torch.cuda.synchronize()
-
-    sl = slice(args.warmup * per_step, nsteps * per_step)
-    n_uniq = nu[sl].cpu().numpy().astype(np.float64)
-    rows = offb[sl, E].cpu().numpy().astype(np.float64)
-    exp_b, sh_b = S.expert_bytes(sh), S.expert_bytes(sh, Fs)
-    # algorithmic bytes and flops per step: union experts + shared expert + router + x + out
-    step_bytes = per_step * (n_uniq.mean() * exp_b + sh_b + E * H * 4 + E * 4 + T * H * 4
-                             + T * H * (2 if out_bf16 else 4))
-    step_flops = per_step * (2.0 * 3 * H * F * rows.mean() + 2.0 * 3 * H * Fs * T + 2.0 * T * E * H)
-    # the dominant kernel: gate/up of every unit (codes + scales), x read, h written
-    gu_bytes = (n_uniq.mean() * 2 * q4_bytes(F, H) + 2 * q4_bytes(Fs, H) + T * H * 4
-                + (rows.mean() * F + T * Fs) * 4)
-    gu_flops = 2.0 * 2 * H * (F * rows.mean() + Fs * T)
-    gu_name = "ffn_gateup" if T <= 4 else "ffn_gateup_mfma"
-    gu_launches, gu_ms = kern.get(gu_name, (0, float("nan")))
-    gu_avg_ms = gu_ms / max(gu_launches, 1)
-    achieved = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
-    result = {
-        "metric": METRIC,
-        "value": T / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        # the expert FFNs' arithmetic: int4 codes times 16-bit fixed-point activations
-        # (carried as two int8 limbs) with exact int32 group sums (v_dot4 in the decode
-        # GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
-        "dtype": "i4xfx16-i32-f32acc",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{wl}: {WORKLOADS[wl]}",
-            "tokens_per_step": T,
-            "layer_copies_cycled": nlay,
-            "mean_union_experts": float(n_uniq.mean()),
-            "mean_routed_rows": float(rows.mean()),
-            "algorithmic_bytes_per_step": float(step_bytes),
-            "step_hbm_gbps": float(step_bytes / (ms_step * 1e-3) / 1e9),
-            "step_tflops": float(step_flops / (ms_step * 1e-3) / 1e12),
-        },
-        "roofline": {
-            "kernel": (f"{gu_name} (gate+up of every union expert and the shared expert, "
-                       "SiLU*up epilogue)"),
-            "bound": "hbm",
-            "achieved": float(achieved),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": float(achieved / HBM_PEAK_GBPS),
-            "traffic": counted_traffic(wl, gu_name),
-            "bytes_per_launch": float(gu_bytes),
-            "avg_launch_us": float(gu_avg_ms * 1e3),
-            "mfma_util_vs_i8_dense": float(gu_flops / (gu_avg_ms * 1e-3) / I8_PEAK_OPS),
-        },
-        "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
-    }
-    if not args.no_cpu_baseline:
-        log(f"CPU baseline: oracle for ~{args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(sh, bank, routers, xs_host, args.cpu_seconds,
-                                              per_token_layers=nlay if stack else 1)
-    print(json.dumps(result), flush=True)
+    order = DEFAULT_ORDER if args.workload == "all" else (args.workload,)
+    head, head_extra, subs = None, None, {}
+    for wl in order:
+        rec, extra = run_workload(wl, args, dev)
+        if head is None:
+            head, head_extra = rec, extra
+        else:
+            subs[wl] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "dtype", "config", "timing",
+                                            "step_roofline", "roofline", "kernel_rooflines",
+                                            "kernels_us_per_step")}
+            log(f"{wl}: {rec['value']:.0f} tokens/s, {rec['ms_per_step'] * 1e3:.1f} us/step, "
+                f"gate/up {rec['roofline']['frac']:.2f} of HBM peak")
+    if subs:
+        head["workloads"] = subs
+    if not args.no_probe:
+        log("streaming-read ceiling probe")
+        head["hbm_read_ceiling"] = read_probe()
+        head["roofline"]["frac_of_read_ceiling"] = head["roofline"]["achieved"] / head["hbm_read_ceiling"]["read_gbps"]
+    if not args.no_cpu_baseline and order[0] == "glm_decode":
+        log(f"CPU baseline: oracle for ~{args.cpu_seconds:.0f} s (+ one thread)")
+        head["cpu_baseline"] = cpu_baseline(head_extra["sh"], head_extra["bank"], head_extra["routers"],
+                                            head_extra["xs_host"], args.cpu_seconds)
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

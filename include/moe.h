@@ -199,6 +199,15 @@ typedef struct {
 } moe_prof_stat;
 
 int moe_prof_begin(void);
+
+/* Streaming-read probe (measurement only, not a step of the layer): one kernel that
+ * reads the `bytes` of device buffer `buf` once (16-byte aligned, bytes a multiple of
+ * 16) with `blocks` workgroups of 256 threads, and stores the XOR of all its words to
+ * sink[0] only if that XOR equals `key` (so nothing is normally written).  Its time
+ * gives the part's practical HBM read ceiling.  MOE_EINVAL for bad arguments,
+ * MOE_EDEVICE without a gfx950 device or on a launch failure. */
+int moe_probe_read(const void *buf, size_t bytes, uint32_t key, uint32_t *sink, int32_t blocks,
+                   void *stream);
 int moe_prof_end(moe_prof_stat *out, int32_t max_entries, int32_t *n_entries);
 
 /* ---- test entry point --------------------------------------------------

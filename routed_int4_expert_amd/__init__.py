@@ -22,7 +22,7 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
-           "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static")
+           "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static", "moe_probe_read")
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
@@ -89,6 +89,8 @@ def lib():
     L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_probe_read.restype = ctypes.c_int
+    L.moe_probe_read.argtypes = [vp, sz, ctypes.c_uint32, vp, i32, vp]
     L.moe_layer_forward_static.restype = ctypes.c_int
     L.moe_layer_forward_static.argtypes = [P, vp, i32, vp, i32, ctypes.POINTER(RouteOutC), vp]
     L.moe_expert_ffn_probe.restype = ctypes.c_int

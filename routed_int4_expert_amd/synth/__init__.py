@@ -16,6 +16,8 @@ experts with one shared expert, ~19 MB of int4 payload per 6144x2048 expert):
                       logits ~N(0,1), bias ~U(-0.5, 0.5).
 * ``glm_stack16``     16 GLM-shaped layers, 32 tokens, top-p 0.7, Zipf(1.1)
                       expert popularity in the router bias, RMSNorm + residual glue.
+* ``glm_rows256``     16 GLM-shaped experts, 512 tokens top-8 (~256 rows per expert):
+                      the grouped GEMM's compute-bound regime (a microbenchmark).
 """
 from __future__ import annotations
 
@@ -171,6 +173,10 @@ SHAPES = {
     "glm_stack16": Shape("glm_stack16", 6144, 256, 2048, 2048, 8, 0.7, 1, 2.5, 32,
                          router_std=1.0 / math.sqrt(6144), bias_kind="zipf", bank="glm",
                          layers=16, extra={"zipf_s": 1.1, "zipf_amp": 0.5}),
+    # grouped-GEMM microbenchmark in the compute-bound regime: GLM-shaped experts, 16 of
+    # them, 512 tokens top-8, so each expert has about 256 rows and the shared expert 512
+    "glm_rows256": Shape("glm_rows256", 6144, 16, 2048, 2048, 8, 0.0, 1, 2.5, 512,
+                         router_std=1.0 / math.sqrt(6144), bias_amp=0.05, bank="glm"),
 }
 
 
