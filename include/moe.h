@@ -78,6 +78,15 @@ typedef struct {
     const float *router_bias; /* [E] fp32 selection bias; NULL = all zero */
     moe_q4 gate, up, down;    /* routed experts, stacked by expert id */
     moe_q4 sh_gate, sh_up, sh_down; /* shared expert [Fs][H] / [H][Fs]; ignored if Fs == 0 */
+    /* Group-limited routing.  The pages' engine runs one group ([R] §1.2: n_group == 1,
+     * asserted); with n_group > 1 (DeepSeek-V3's noaux_tc) the experts form n_group equal
+     * groups of consecutive ids, each scored by the sum of its two largest choice scores,
+     * and only the topk_group best groups (equal scores: lower group id) take part in the
+     * top-k.  n_group 0 or 1: no groups.  Otherwise E % n_group == 0, at least two experts
+     * per group, n_group <= 64, 1 <= topk_group <= n_group and topk_group * E / n_group >= k
+     * (MOE_EINVAL otherwise). */
+    int32_t n_group;
+    int32_t topk_group;
 } moe_layer;
 
 /* Optional routing outputs of moe_layer_forward.  Any member may be NULL. */
@@ -167,6 +176,24 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out,
 #define MOE_STATIC_SCRATCH_BYTES (64u << 20)
 int moe_layer_forward_static(const moe_layer *L, const float *x, int32_t T, void *out,
                              int32_t out_dtype, const moe_route_out *dbg, void *stream);
+
+/* First-dense layers ([R] §1.5): the model's first layers are a plain MLP (dense_mlp),
+ * not MoE.  For every token t:
+ *   out[t] = Wd (silu(Wg x_t) * (Wu x_t)),
+ * the same int4-gs64 SwiGLU and arithmetic as an expert in moe_expert_ffn (16-bit
+ * fixed-point activation blocks, exact int32 dot products, fp32 accumulation).  x [T][H]
+ * fp32; out [T][H] fp32 (MOE_F32) or bf16 round-to-nearest-even of the fp32 result
+ * (MOE_BF16).  Conventions, validation and errors as moe_layer_forward; the workspace
+ * comes from moe_dense_workspace_bytes (0 for an invalid D). */
+typedef struct {
+    int32_t hidden;       /* H, multiple of 64, up to MOE_MAX_DIM */
+    int32_t ffn;          /* F, multiple of 64, up to MOE_MAX_DIM */
+    moe_q4 gate, up, down; /* [F][H], [F][H], [H][F] */
+} moe_dense;
+
+size_t moe_dense_workspace_bytes(const moe_dense *D, int32_t max_tokens);
+int moe_dense_forward(const moe_dense *D, const float *x, int32_t T, void *out, int32_t out_dtype,
+                      void *ws, size_t ws_bytes, void *stream);
 
 /* Glue between stacked MoE layers -- not a step of the layer itself.  For each of
  * the T rows of H fp32 values: h_out = h + delta (delta NULL: h_out = h), then

@@ -39,6 +39,7 @@ class RefLayer(ctypes.Structure):
         ("sh_gate_q", ctypes.c_void_p), ("sh_gate_s", ctypes.c_void_p),
         ("sh_up_q", ctypes.c_void_p), ("sh_up_s", ctypes.c_void_p),
         ("sh_down_q", ctypes.c_void_p), ("sh_down_s", ctypes.c_void_p),
+        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
     ]
 
 
@@ -64,6 +65,7 @@ def _load():
         "moe_ref_expert_ffn": (ctypes.c_int, [L, vp, i32, vp, vp, vp]),
         "moe_ref_layer_forward": (ctypes.c_int, [L, vp, i32, vp, i32, vp]),
         "moe_ref_rmsnorm": (ctypes.c_int, [vp, i32, i32, ctypes.c_double, vp]),
+        "moe_ref_dense_mlp": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -100,10 +102,12 @@ class Layer:
         self.shared_ffn, self.top_k = int(d["shared_ffn"]), int(d["top_k"])
         self.top_p, self.norm_topk = float(d["top_p"]), int(d["norm_topk"])
         self.routed_scale = float(d["routed_scale"])
+        self.n_group, self.topk_group = int(d.get("n_group", 0)), int(d.get("topk_group", 0))
         s = RefLayer()
         s.hidden, s.n_experts, s.ffn = self.hidden, self.n_experts, self.ffn
         s.shared_ffn, s.top_k, s.top_p = self.shared_ffn, self.top_k, self.top_p
         s.norm_topk, s.routed_scale = self.norm_topk, self.routed_scale
+        s.n_group, s.topk_group = self.n_group, self.topk_group
         for k in self.FIELDS:
             setattr(s, k, _p(self.d[k]) if self.d[k] is not None and self.d[k].size else None)
         self.struct = s
@@ -215,6 +219,17 @@ def layer_forward(L: Layer, x: np.ndarray, toks=None) -> np.ndarray:
         out = np.empty((tk.size, L.hidden), np.float64)
         _check(_load().moe_ref_layer_forward(L.ref(), _p(x), T, _p(tk), tk.size, _p(out)),
                "layer_forward")
+    return out
+
+
+def dense_mlp(gq, gs, uq, us, dq, ds, x: np.ndarray) -> np.ndarray:
+    """The first-dense-layer SwiGLU MLP on every token, fp64 [T][H]."""
+    arrs = [np.ascontiguousarray(a) for a in (gq, gs, uq, us, dq, ds)]
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    F, H = arrs[0].shape[0], arrs[0].shape[1] * 2
+    T = x.shape[0]
+    out = np.empty((T, H), np.float64)
+    _check(_load().moe_ref_dense_mlp(*[_p(a) for a in arrs], H, F, _p(x), T, _p(out)), "dense_mlp")
     return out
 
 

@@ -105,6 +105,13 @@ static int ref_layer_ok(const moe_ref_layer *L) {
     if (L->shared_ffn < 0 || L->shared_ffn % 64 != 0) return 0;
     if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > 64) return 0;
     if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return 0;
+    if (L->n_group < 0) return 0;
+    if (L->n_group > 256) return 0;
+    if (L->n_group > 1) { /* equal groups of at least two experts, enough experts kept */
+        if (L->n_experts % L->n_group != 0 || L->n_experts / L->n_group < 2) return 0;
+        if (L->topk_group < 1 || L->topk_group > L->n_group) return 0;
+        if ((int64_t)L->topk_group * (L->n_experts / L->n_group) < L->top_k) return 0;
+    }
     if (!L->router_w) return 0;
     return 1;
 }
@@ -143,6 +150,42 @@ static void ref_select_one(const moe_ref_layer *L, const double *logit,
         sig[e] = ref_sigmoid(logit[e]);
         double b = L->router_bias ? (double)L->router_bias[e] : 0.0;
         choice[e] = sig[e] + b;
+    }
+    /* Group-limited routing (n_group > 1).  The pages' engine has n_group == 1 and
+     * asserts it ([R] §1.2); for more groups this follows DeepSeek-V3's noaux_tc, the
+     * routing the page is modelled on: experts form n_group equal groups of consecutive
+     * ids; a group's score is the sum of its two largest choice scores (a repeated
+     * maximum counts twice); the topk_group groups with the largest scores are kept
+     * (iterative argmax, equal scores to the lower group id); experts of the other
+     * groups take no part in the top-k below. */
+    if (L->n_group > 1) {
+        const int32_t G = L->n_group, gsz = E / G;
+        double gscore[256];
+        char gkeep[256];
+        for (int32_t g = 0; g < G; g++) {
+            double m1 = -INFINITY, m2 = -INFINITY;
+            for (int32_t j = 0; j < gsz; j++) {
+                double c = choice[g * gsz + j];
+                if (c > m1) {
+                    m2 = m1;
+                    m1 = c;
+                } else if (c > m2) {
+                    m2 = c;
+                }
+            }
+            gscore[g] = m1 + m2;
+            gkeep[g] = 0;
+        }
+        for (int32_t r = 0; r < L->topk_group; r++) {
+            int32_t best = -1;
+            for (int32_t g = 0; g < G; g++) {
+                if (gkeep[g]) continue;
+                if (best < 0 || gscore[g] > gscore[best]) best = g;
+            }
+            gkeep[best] = 1;
+        }
+        for (int32_t e = 0; e < E; e++)
+            if (!gkeep[e / gsz]) taken[e] = 1; /* never a candidate */
     }
     /* Iterative argmax; a strictly greater score replaces the best so far, so
      * equal scores go to the lowest expert id. */
@@ -400,6 +443,19 @@ int moe_ref_layer_forward(const moe_ref_layer *L, const float *x, int32_t T,
     free(logit);
     free(y);
     return rc;
+}
+
+/* [R] §1.5: the first layers are a plain MLP (dense_mlp), the same SwiGLU as an
+ * expert applied to every token. */
+int moe_ref_dense_mlp(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
+                      const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+                      const float *x, int32_t T, double *out) {
+    if (T < 0 || (T > 0 && (!x || !out))) return REF_EINVAL;
+    for (int32_t t = 0; t < T; t++) {
+        int rc = moe_ref_swiglu(gq, gs, uq, us, dq, ds, H, F, x + (int64_t)t * H, out + (int64_t)t * H);
+        if (rc) return rc;
+    }
+    return 0;
 }
 
 int moe_ref_rmsnorm(const float *h, int32_t T, int32_t H, double eps, float *y) {

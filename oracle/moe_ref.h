@@ -48,6 +48,8 @@ typedef struct {
     const uint8_t *sh_gate_q; const float *sh_gate_s;  /* [Fs][H/2], [Fs][H/64] */
     const uint8_t *sh_up_q;   const float *sh_up_s;
     const uint8_t *sh_down_q; const float *sh_down_s;  /* [H][Fs/2], [H][Fs/64] */
+    int32_t n_group;      /* expert groups for group-limited routing; 0 or 1 = none */
+    int32_t topk_group;   /* groups kept when n_group > 1 */
 } moe_ref_layer;
 
 /* ---- int4 codec ([Q] §5.2) ------------------------------------------------ */
@@ -93,6 +95,13 @@ int moe_ref_expert_ffn(const moe_ref_layer *L, const float *x, int32_t T,
  * [n_toks][H] in list order; otherwise out is [T][H]. */
 int moe_ref_layer_forward(const moe_ref_layer *L, const float *x, int32_t T,
                           const int32_t *toks, int32_t n_toks, double *out);
+
+/* ---- first-dense layers ([R] §1.5) ---------------------------------------- */
+/* out[t] = Wd (silu(Wg x_t) .* (Wu x_t)) for every token: the plain SwiGLU MLP of the
+ * first layers; Wg/Wu [F][H], Wd [H][F] int4-gs64; out [T][H] fp64. */
+int moe_ref_dense_mlp(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
+                      const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+                      const float *x, int32_t T, double *out);
 
 /* RMSNorm (gamma = 1): y = h / sqrt(mean(h^2) + eps), fp64 internally, fp32 out. */
 int moe_ref_rmsnorm(const float *h, int32_t T, int32_t H, double eps, float *y);

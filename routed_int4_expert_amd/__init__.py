@@ -22,7 +22,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
-           "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static", "moe_probe_read")
+           "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static", "moe_probe_read",
+           "moe_dense_workspace_bytes", "moe_dense_forward")
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
@@ -45,7 +46,13 @@ class LayerC(ctypes.Structure):
         ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
         ("gate", Q4), ("up", Q4), ("down", Q4),
         ("sh_gate", Q4), ("sh_up", Q4), ("sh_down", Q4),
+        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
     ]
+
+
+class DenseC(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("gate", Q4), ("up", Q4), ("down", Q4)]
 
 
 class ProfStatC(ctypes.Structure):
@@ -89,6 +96,10 @@ def lib():
     L.moe_prof_end.argtypes = [ctypes.POINTER(ProfStatC), i32, ctypes.POINTER(i32)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_dense_workspace_bytes.restype = sz
+    L.moe_dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseC), i32]
+    L.moe_dense_forward.restype = ctypes.c_int
+    L.moe_dense_forward.argtypes = [ctypes.POINTER(DenseC), vp, i32, vp, i32, vp, sz, vp]
     L.moe_probe_read.restype = ctypes.c_int
     L.moe_probe_read.argtypes = [vp, sz, ctypes.c_uint32, vp, i32, vp]
     L.moe_layer_forward_static.restype = ctypes.c_int
@@ -132,12 +143,14 @@ class Layer:
 
     def __init__(self, params: dict, tensors: dict):
         self.params = {k: params[k] for k in PARAMS}
+        self.params.update(n_group=int(params.get("n_group", 0)), topk_group=int(params.get("topk_group", 0)))
         self.t = dict(tensors)
         c = LayerC()
         c.hidden, c.n_experts = int(params["hidden"]), int(params["n_experts"])
         c.ffn, c.shared_ffn, c.top_k = int(params["ffn"]), int(params["shared_ffn"]), int(params["top_k"])
         c.top_p, c.norm_topk = float(params["top_p"]), int(params["norm_topk"])
         c.routed_scale = float(params["routed_scale"])
+        c.n_group, c.topk_group = self.params["n_group"], self.params["topk_group"]
         g = self.t.get
         c.router_w = _ptr(g("router_w"))
         c.router_bias = _ptr(g("router_bias"))
@@ -250,6 +263,50 @@ def moe_layer_forward_static(layer: Layer, x, out=None, out_dtype: int = MOE_F32
     _check(lib().moe_layer_forward_static(layer.ref(), _ptr(x), T, _ptr(out), out_dtype,
                                           ctypes.byref(rc) if rc is not None else None,
                                           _stream(stream)), "moe_layer_forward_static")
+    return out
+
+
+class Dense:
+    """A first-dense layer's device tensors (int4-gs64 gate/up [F][H], down [H][F]) and its C
+    description."""
+
+    def __init__(self, tensors: dict):
+        self.t = dict(tensors)
+        c = DenseC()
+        F, h2 = self.t["gate_q"].shape
+        c.hidden, c.ffn = int(h2) * 2, int(F)
+        for name in ("gate", "up", "down"):
+            setattr(c, name, Q4(_ptr(self.t[name + "_q"]), _ptr(self.t[name + "_s"])))
+        self.c = c
+        self.hidden, self.ffn = c.hidden, c.ffn
+
+    @classmethod
+    def from_host(cls, d: dict, device="cuda"):
+        import torch
+        return cls({k: torch.from_numpy(np.ascontiguousarray(d[k])).to(device)
+                    for k in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")})
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def workspace(self, T: int, device="cuda"):
+        import torch
+        n = lib().moe_dense_workspace_bytes(self.ref(), int(T))
+        if n == 0:
+            raise MoeError(MOE_EINVAL, "moe_dense_workspace_bytes")
+        return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def moe_dense_forward(dense: Dense, x, out=None, out_dtype: int = MOE_F32, ws=None, stream=None):
+    """First-dense-layer SwiGLU MLP on every token: out [T][H] fp32 or bf16."""
+    import torch
+    T, H = x.shape[0], dense.hidden
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32,
+                          device=x.device)
+    ws = dense.workspace(T, x.device) if ws is None else ws
+    _check(lib().moe_dense_forward(dense.ref(), _ptr(x), T, _ptr(out), out_dtype, _ptr(ws), ws.numel(),
+                                   _stream(stream)), "moe_dense_forward")
     return out
 
 

@@ -14,10 +14,26 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+// four outputs n .. n+3 of token t, as fp32 or as their bf16 round-to-nearest-even
+__device__ __forceinline__ void store4(const CombineArgs &a, int t, int n, float4 acc) {
+    if (a.out_bf16) {
+        uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (size_t)t * a.H + n;
+        const uint2 packed = make_uint2((uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16),
+                                        (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16));
+        *reinterpret_cast<uint2 *>(o) = packed;
+    } else {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + (size_t)t * a.H + n) = acc;
+    }
+}
+
 // outputs n .. n+3 of token t (n a multiple of 4, H a multiple of 64).  The slots'
 // rows and weights are read first, then all the rows' values, so the loads take two
 // round trips whatever k is; the sum runs in slot order.
 __device__ __forceinline__ void combine4(const CombineArgs &a, int t, int n) {
+    if (a.k == 0) {  // no routed experts: the always-on FFN's output alone
+        store4(a, t, n, *reinterpret_cast<const float4 *>(a.y_shared + (size_t)t * a.H + n));
+        return;
+    }
     const int ke = min(max(a.keff[t], 0), a.k);
     // loads are unconditional (clamped slot, row 0 for an empty slot), so they are all
     // in flight together; empty slots are masked out of the sum
@@ -53,14 +69,7 @@ __device__ __forceinline__ void combine4(const CombineArgs &a, int t, int n) {
         acc.z += ys.z;
         acc.w += ys.w;
     }
-    if (a.out_bf16) {
-        uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + (size_t)t * a.H + n;
-        const uint2 packed = make_uint2((uint32_t)bf16_rne(acc.x) | ((uint32_t)bf16_rne(acc.y) << 16),
-                                        (uint32_t)bf16_rne(acc.z) | ((uint32_t)bf16_rne(acc.w) << 16));
-        *reinterpret_cast<uint2 *>(o) = packed;
-    } else {
-        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + (size_t)t * a.H + n) = acc;
-    }
+    store4(a, t, n, acc);
 }
 
 }  // namespace moe

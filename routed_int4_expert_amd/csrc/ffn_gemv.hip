@@ -564,7 +564,8 @@ static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     }
     // resident workgroups per CU (4 waves each): registers allow 4, LDS may allow fewer
     int per_cu = 4;
-    while (per_cu > 1 && (size_t)per_cu * (lds + 2048) > 160 * 1024) per_cu--;  // + static LDS
+    const size_t lds_static = (GU && RM == 1) ? sizeof(PickScratch) + 256 : 256;
+    while (per_cu > 1 && (size_t)per_cu * (lds + lds_static) > 160 * 1024) per_cu--;
     const long cap = (long)device_cus() * per_cu;
     const int blocks1 = (N + S::BF - 1) / S::BF;  // workgroups per unit at one pass each
     int passes = 1, passes_sh = 1, nsh = 0, gx;

@@ -33,6 +33,12 @@ static int check_dims(const moe_layer *L) {
     if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return MOE_EINVAL;  // also rejects NaN
     if (!isfinite(L->routed_scale)) return MOE_EINVAL;
     if (L->n_experts > MOE_MAX_EXPERTS || L->top_k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+    if (L->n_group < 0) return MOE_EINVAL;
+    if (L->n_group > 1) {
+        if (L->n_group > 64 || L->n_experts % L->n_group || L->n_experts / L->n_group < 2) return MOE_EINVAL;
+        if (L->topk_group < 1 || L->topk_group > L->n_group) return MOE_EINVAL;
+        if ((long)L->topk_group * (L->n_experts / L->n_group) < L->top_k) return MOE_EINVAL;
+    }
     if (L->hidden > MOE_MAX_DIM || L->ffn > MOE_MAX_DIM || L->shared_ffn > MOE_MAX_DIM)
         return MOE_EUNSUPPORTED;
     return MOE_OK;
@@ -185,6 +191,8 @@ static SelectArgs select_args(const moe_layer &L, const Plan &p, int T, int32_t 
     sa.top_p = L.top_p;
     sa.routed_scale = L.routed_scale;
     sa.norm_topk = L.norm_topk ? 1 : 0;
+    sa.n_group = L.n_group > 1 ? L.n_group : 1;
+    sa.topk_group = L.n_group > 1 ? L.topk_group : 1;
     return sa;
 }
 
@@ -397,6 +405,61 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
 }
 
 
+
+// ---------------------------------------------------------------- first-dense layers
+// A dense layer runs the expert-FFN kernels with no routed unit and the MLP as the
+// always-on unit for every token (the shared-expert role).  Its plan holds that unit's
+// buffers only: h [T][F], y [T][H] (bf16 output: the fp32 rows before conversion; fp32
+// output goes straight to out) and, above the GEMV range, the activation fragments.
+static int check_dense(const moe_dense *D) {
+    if (!D) return MOE_EINVAL;
+    if (D->hidden <= 0 || D->hidden % 64 || D->ffn <= 0 || D->ffn % 64) return MOE_EINVAL;
+    if (D->hidden > MOE_MAX_DIM || D->ffn > MOE_MAX_DIM) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+static moe_layer dense_as_layer(const moe_dense &D) {
+    moe_layer L;
+    memset(&L, 0, sizeof(L));
+    L.hidden = D.hidden;
+    L.n_experts = 1;
+    L.ffn = 64;
+    L.shared_ffn = D.ffn;
+    L.top_k = 1;
+    L.routed_scale = 1.0f;
+    L.sh_gate = D.gate;
+    L.sh_up = D.up;
+    L.sh_down = D.down;
+    return L;
+}
+
+struct DensePlan {
+    size_t h, y, x_frag, x_step, hs_frag, hs_step, total;
+};
+
+static DensePlan make_dense_plan(const moe_dense &D, int T) {
+    DensePlan p;
+    memset(&p, 0, sizeof(p));
+    const size_t Tz = T > 0 ? (size_t)T : 1, H = D.hidden, F = D.ffn;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    p.h = take(Tz * F * 4);
+    p.y = take(Tz * H * 4);
+    if (Tz > (size_t)kGemvMaxTokens) {
+        const size_t gh = mfma_groups_padded((int)H), gf = mfma_groups_padded((int)F);
+        p.x_frag = take(Tz * gh * 128);
+        p.x_step = take(Tz * gh);
+        p.hs_frag = take(Tz * gf * 128);
+        p.hs_step = take(Tz * gf);
+    }
+    p.total = o;
+    return p;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -476,6 +539,89 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
     if ((rc = check_device())) return rc;
     return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream);
+}
+
+size_t moe_dense_workspace_bytes(const moe_dense *D, int32_t max_tokens) {
+    if (check_dense(D) != MOE_OK || max_tokens < 0 || max_tokens > MOE_MAX_TOKENS) return 0;
+    return make_dense_plan(*D, max_tokens).total;
+}
+
+int moe_dense_forward(const moe_dense *D, const float *x, int32_t T, void *out, int32_t out_dtype,
+                      void *ws, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_dense(D)) || (rc = check_T(T))) return rc;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if ((rc = check_q4(D->gate)) || (rc = check_q4(D->up)) || (rc = check_q4(D->down))) return rc;
+    if (!x || !out) return MOE_EINVAL;
+    if (!aligned16(x) || ((uintptr_t)out & 7u)) return MOE_EALIGN;
+    if (out_dtype == MOE_F32 && !aligned16(out)) return MOE_EALIGN;
+    const size_t need = moe_dense_workspace_bytes(D, T);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    if (!aligned16(ws)) return MOE_EALIGN;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const DensePlan p = make_dense_plan(*D, T);
+    const moe_layer L = dense_as_layer(*D);
+    FfnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.gu_out = kGuSwiglu;
+    a.x = x;
+    a.sh_gate = D->gate;
+    a.sh_up = D->up;
+    a.sh_down = D->down;
+    a.h_shared = at<float>(ws, p.h);
+    // fp32 output: the down projection writes out directly
+    a.y_shared = out_dtype == MOE_F32 ? static_cast<float *>(out) : at<float>(ws, p.y);
+    a.T = T;
+    a.H = D->hidden;
+    a.F = L.ffn;
+    a.Fs = D->ffn;
+    a.max_units = 0;
+    a.with_routed = 0;
+    a.with_shared = 1;
+    hipError_t e;
+    if (T <= kGemvMaxTokens) {
+        e = launch_ffn_gemv(a, st);
+    } else {
+        MfmaArgs m;
+        memset(&m, 0, sizeof(m));
+        m.gu_out = kGuSwiglu;
+        m.x = x;
+        m.x_frag = at<uint8_t>(ws, p.x_frag);
+        m.x_step = at<float>(ws, p.x_step);
+        m.sh_gate = D->gate;
+        m.sh_up = D->up;
+        m.sh_down = D->down;
+        m.h_shared = a.h_shared;
+        m.hs_frag = at<uint8_t>(ws, p.hs_frag);
+        m.hs_step = at<float>(ws, p.hs_step);
+        m.y_shared = a.y_shared;
+        m.T = T;
+        m.H = D->hidden;
+        m.F = L.ffn;
+        m.Fs = D->ffn;
+        m.E = 1;
+        m.max_units = 0;
+        m.max_rows = 0;
+        m.item_rows = mfma_item_rows(T, 1);
+        m.max_items = 0;
+        m.with_routed = 0;
+        m.with_shared = 1;
+        e = launch_ffn_mfma(m, st);
+    }
+    if (e == hipSuccess && out_dtype == MOE_BF16) {
+        CombineArgs c;
+        memset(&c, 0, sizeof(c));
+        c.y_shared = a.y_shared;
+        c.out = out;
+        c.T = T;
+        c.H = D->hidden;
+        c.k = 0;
+        c.out_bf16 = 1;
+        e = launch_combine(c, st);
+    }
+    return launched(e);
 }
 
 int moe_residual_rmsnorm(const float *h, const float *delta, int32_t T, int32_t H, float eps,

@@ -99,6 +99,7 @@ struct SelectArgs {
     int S, T, E, k;
     float top_p, routed_scale;
     int norm_topk;
+    int n_group, topk_group;  // group-limited routing when n_group > 1
 };
 
 struct UnionArgs {
@@ -116,7 +117,7 @@ struct CombineArgs {
     const float *y_routed;  // [rows][H]
     const float *y_shared;  // [T][H] or nullptr
     void *out;              // [T][H] fp32 or bf16
-    int T, H, k, out_bf16;
+    int T, H, k, out_bf16;  // k == 0: no routed terms (a dense layer's output conversion)
 };
 
 struct FfnArgs {

@@ -39,12 +39,20 @@ __device__ __forceinline__ void gate_and_key(double l, const float *bias, int e,
     key = mono_key(isnan(c) ? -INFINITY : c);
 }
 
-// Per-wave LDS scratch of select_token: the k picks, compacted (expert order).
+// Per-wave LDS scratch of select_token: the k picks, compacted (expert order), and the
+// token's choice scores for the group scores of group-limited routing.
 struct PickScratch {
     unsigned long long key[MOE_MAX_TOPK];
     double sig[MOE_MAX_TOPK];
     int id[MOE_MAX_TOPK];
+    double choice[MOE_MAX_EXPERTS];
 };
+
+// The choice score a monotone key came from (mono_key inverted).
+__device__ __forceinline__ double key_value(unsigned long long k) {
+    const unsigned long long b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __longlong_as_double((long long)b);
+}
 
 // AND and OR of a 64-bit value over a whole wave (all 64 lanes active), as
 // wave-uniform values: within each row of 16 lanes by DPP moves (swap neighbours,
@@ -140,15 +148,56 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         }
     }
 
+    // Group-limited routing (n_group > 1; DeepSeek-V3's noaux_tc, [R] §1.2 has one group):
+    // group g = experts [g*gs, (g+1)*gs); its score is the sum of its two largest choices;
+    // the topk_group best groups (equal scores: lower id) stay, the other experts' keys
+    // become 0, below every live key, so they are never picked.
+    if (a.n_group > 1) {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const int e = lane + kWave * i;
+            if (e < a.E) ps->choice[e] = key_value(key[i]);
+        }
+        wave_lds_sync();
+        const int gs = a.E / a.n_group;
+        double gscore = -INFINITY;
+        if (lane < a.n_group) {
+            double m1 = -INFINITY, m2 = -INFINITY;
+            for (int j = 0; j < gs; j++) {
+                const double c = ps->choice[lane * gs + j];
+                if (c > m1) {
+                    m2 = m1;
+                    m1 = c;
+                } else if (c > m2) {
+                    m2 = c;
+                }
+            }
+            gscore = m1 + m2;
+        }
+        int grank = 0;
+        for (int g = 0; g < a.n_group; g++) {
+            const double sg = readlane_f64(gscore, g);
+            grank += (sg > gscore || (sg == gscore && g < lane)) ? 1 : 0;
+        }
+        const unsigned long long gkeep = __ballot(lane < a.n_group && grank < a.topk_group);
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const int e = lane + kWave * i;
+            if (e < a.E && !((gkeep >> (e / gs)) & 1ull)) key[i] = 0ull;
+        }
+        wave_lds_sync();  // the choice scratch is read by every lane before it is reused
+    }
+
     // thr = the k-th largest key: the largest value with at least k keys >= it, built
     // bit by bit.  As soon as exactly k keys are >= a candidate, those k are the picks
     // (no key equal to the k-th is left out), which ends the search early.  Bits above
     // the highest one in which the live keys differ are the same in all of them, so
     // thr starts with them and the search starts below (there are at least k live keys).
+    // live keys: experts below E (and in a kept group); every live key is nonzero
     unsigned long long kand = ~0ull, kor = 0ull;
 #pragma unroll
     for (int i = 0; i < EPL; i++)
-        if (lane + kWave * i < a.E) {
+        if (key[i] != 0ull) {
             kand &= key[i];
             kor |= key[i];
         }
@@ -185,7 +234,7 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         int eq_before = 0;
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
-            const unsigned long long eqm = __ballot(key[i] == thr && (lane + kWave * i) < a.E);
+            const unsigned long long eqm = __ballot(key[i] == thr && key[i] != 0ull);
             const int r = eq_before + __popcll(eqm & below);
             sel[i] = key[i] > thr || (((eqm >> lane) & 1ull) && r < need);
             eq_before += __popcll(eqm);

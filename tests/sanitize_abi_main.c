@@ -53,6 +53,16 @@ int main(int argc, char **argv) {
     EXPECT(forward(&B, 4, ws, x, out) != MOE_OK);
     B = L; B.top_p = 1.5f;
     EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
+    B = L; B.n_group = 3;                      /* 16 experts do not split into 3 groups */
+    EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
+    B = L; B.n_group = 4; B.topk_group = 0;
+    EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
+    B = L; B.n_group = 8; B.topk_group = 1;    /* 2 experts kept < top-4 */
+    EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
+    B = L; B.n_group = 16; B.topk_group = 8;   /* groups of one expert */
+    EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
+    B = L; B.n_group = -1;
+    EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
     B = L; B.router_w = NULL;
     EXPECT(forward(&B, 4, ws, x, out) == MOE_EINVAL);
     EXPECT(forward(&L, 4, ws, NULL, out) == MOE_EINVAL);

@@ -80,6 +80,12 @@ def call_forward(c, T=4, x=0x20000, out=0x30000, dtype=0, ws=0x40000, wsb=None):
     (dict(gate=M.Q4(None, 0x10000)), M.MOE_EINVAL),
     (dict(down=M.Q4(0x10008, 0x10000)), M.MOE_EALIGN),
     (dict(sh_up=M.Q4(0x10000, None)), M.MOE_EINVAL),
+    (dict(n_group=3), M.MOE_EINVAL),                 # 16 experts in 3 groups
+    (dict(n_group=4, topk_group=0), M.MOE_EINVAL),
+    (dict(n_group=4, topk_group=5), M.MOE_EINVAL),
+    (dict(n_group=8, topk_group=1), M.MOE_EINVAL),   # 2 experts kept < top-4
+    (dict(n_group=16, topk_group=8), M.MOE_EINVAL),  # single-expert groups
+    (dict(n_group=-1), M.MOE_EINVAL),
 ])
 def test_forward_validation_codes(kw, code):
     assert call_forward(_layer(**kw)) == code
@@ -192,3 +198,40 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def _dense(**kw):
+    c = M.DenseC()
+    c.hidden, c.ffn = 256, 192
+    for n in ("gate", "up", "down"):
+        setattr(c, n, M.Q4(0x10000, 0x10000))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_dense_validation_codes():
+    """moe_dense_forward validates like moe_layer_forward (no device needed)."""
+    lib = M.lib()
+    ok = _dense()
+    nb = lambda c, T: lib.moe_dense_workspace_bytes(ctypes.byref(c), T)
+    assert nb(ok, 0) > 0 and nb(ok, 4) <= nb(ok, 5) <= nb(ok, 300)
+    assert nb(_dense(hidden=100), 4) == 0 and nb(ok, -1) == 0 and nb(ok, M.MOE_MAX_TOKENS + 1) == 0
+
+    def fwd(c, T=4, x=0x20000, out=0x30000, dtype=0, ws=0x40000, wsb=None):
+        wsb = (nb(c, T) or (1 << 30)) if wsb is None else wsb
+        return lib.moe_dense_forward(ctypes.byref(c), x, T, out, dtype, ws, wsb, None)
+
+    assert fwd(_dense(hidden=100)) == M.MOE_EINVAL
+    assert fwd(_dense(ffn=32)) == M.MOE_EINVAL
+    assert fwd(_dense(ffn=32768)) == M.MOE_EUNSUPPORTED
+    assert fwd(_dense(gate=M.Q4(None, 0x10000))) == M.MOE_EINVAL
+    assert fwd(_dense(down=M.Q4(0x10008, 0x10000))) == M.MOE_EALIGN
+    assert fwd(ok, x=None) == M.MOE_EINVAL
+    assert fwd(ok, x=0x20004) == M.MOE_EALIGN
+    assert fwd(ok, dtype=5) == M.MOE_EINVAL
+    assert fwd(ok, T=-1) == M.MOE_EINVAL
+    assert fwd(ok, T=M.MOE_MAX_TOKENS + 1) == M.MOE_EUNSUPPORTED
+    assert fwd(ok, wsb=16) == M.MOE_EWORKSPACE
+    assert fwd(ok, T=0) == M.MOE_OK
+    assert lib.moe_dense_forward(None, 0x20000, 4, 0x30000, 0, 0x40000, 1 << 30, None) == M.MOE_EINVAL

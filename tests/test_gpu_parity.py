@@ -190,6 +190,60 @@ def test_exact_ties(kind, T):
     full_parity(sh, d, x)
 
 
+GROUP_T = [1, 5, 9, 40, 300]
+
+
+@pytest.mark.parametrize("T", GROUP_T, ids=[f"T{t}" for t in GROUP_T])
+@pytest.mark.parametrize("cfg", [(256, 8, 8, 4, 0.0), (64, 6, 4, 2, 0.8), (32, 4, 16, 3, 0.0)],
+                         ids=["E256g8k4", "E64g4k2topp", "E32g16k3"])
+def test_group_limited_routing(cfg, T):
+    """Group-limited routing (n_group > 1) on every selection path against the oracle:
+    ids, keff, w, the union and the layer.  Groups of 32, 16 and 2 experts."""
+    E, k, n_group, topk_group, top_p = cfg
+    sh = S.custom(f"grp{E}_{T}", hidden=256, n_experts=E, ffn=64, shared_ffn=64, top_k=k,
+                  tokens=T, top_p=top_p, routed_scale=2.5, router_std=1 / 16.0, bias_amp=0.2)
+    d = S.make_layer(sh, seed=0)
+    d.update(n_group=n_group, topk_group=topk_group)
+    x = S.make_batch(sh, d, seed=0)
+    say(f"group-limited E={E} k={k} groups {topk_group}/{n_group} T={T}")
+    rids, _, _ = R.route(R.Layer(d), x)
+    gsz = E // n_group
+    assert all(len(set((rids[t][rids[t] >= 0] // gsz).tolist())) <= topk_group for t in range(T))
+    if T >= 9:  # the groups change some selections
+        free, _, _ = R.route(R.Layer({**d, "n_group": 0}), x)
+        assert np.any(free != rids)
+    full_parity(sh, d, x)
+
+
+DENSE = [(256, 128, 1), (320, 192, 3), (512, 256, 24), (256, 128, 300), (6144, 12288, 1),
+         (6144, 12288, 32)]
+
+
+@pytest.mark.parametrize("H,F,T", DENSE, ids=[f"H{h}F{f}T{t}" for h, f, t in DENSE])
+def test_dense_mlp(H, F, T):
+    """First-dense layers: moe_dense_forward against the oracle's dense MLP (fp32 within the
+    bar; bf16 exactly the RNE of the fp32 result).  The GLM-shaped 6144 x 12288 MLP at one
+    token (GEMV path) and 32 tokens (matrix cores)."""
+    say(f"dense MLP H={H} F={F} T={T}")
+    d = {}
+    for name, (n, kk) in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))):
+        d[name + "_q"], d[name + "_s"] = S.q4_normal(0, f"dense{H}x{F}/{name}", n, kk, 0.02)
+    x = S.tokens(S.custom("dense_x", hidden=H), T, seed=0)
+    dense = M.Dense.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    out = M.moe_dense_forward(dense, xd)
+    out_bf = M.moe_dense_forward(dense, xd, out_dtype=M.MOE_BF16)
+    torch.cuda.synchronize()
+    ref = R.dense_mlp(d["gate_q"], d["gate_s"], d["up_q"], d["up_s"], d["down_q"], d["down_s"], x)
+    got = out.cpu().numpy()
+    rel, mx = assert_close(got, ref, f"dense H={H} F={F} T={T}")
+    for t in range(T):
+        assert_close(got[t], ref[t], f"dense token {t}")
+    got_bf = out_bf.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got_bf, R.to_bf16_bits(got.astype(np.float64)))
+    say(f"dense H={H} F={F} T={T}: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
 def test_item_row_boundaries():
     """Experts routed exactly 66, 17, 16 and 33 rows and a 66-token shared expert.
 

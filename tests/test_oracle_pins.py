@@ -335,6 +335,101 @@ def test_topp_cut_inside_equal_gates():
     np.testing.assert_array_equal(w[0], np.float32([s9, s1, s1, 0.0]))
 
 
+# --------------------------------------------------------------------------- group-limited routing
+# Reading (the pages' engine asserts n_group == 1): DeepSeek-V3's group-limited noaux_tc,
+# groups of consecutive ids scored by the sum of their two largest choices.
+def _grp_layer(E, k, n_group, topk_group, **kw):
+    lay = _sel_layer(E, k, **kw)
+    lay.struct.n_group, lay.struct.topk_group = n_group, topk_group
+    return lay
+
+
+def test_group_limited_worked_example():
+    # 8 experts in 4 groups of 2: {0,1} {2,3} {4,5} {6,7}.  sigmoids 0.900/0.100, 0.599/0.599,
+    # 0.500/0.550, 0.198/0.198: group scores 1.000, 1.198, 1.050, 0.396, so groups 1 and 2
+    # are kept and expert 0 (the best single score) is out.  The top-2 of {2,3,4,5} is the
+    # tie 2, 3 (lower id first).  A group score of the maximum alone would keep groups 0
+    # and 1 (0.900 > 0.599 > 0.550) and pick 0, 2.
+    lg = np.array([[2.2, -2.2, 0.4, 0.4, 0.0, 0.2, -1.4, -1.4]])
+    ids, _, _ = R.select(_grp_layer(8, 2, 4, 2), lg)
+    assert ids[0].tolist() == [2, 3]
+    ids0, _, _ = R.select(_sel_layer(8, 2), lg)
+    assert ids0[0].tolist() == [0, 2]
+
+
+def test_group_limited_top_two_not_sum_of_all():
+    # groups of 4: {0..3} {4..7}; group 0 has two strong and two weak experts, group 1
+    # four medium ones.  Top-2 sums: g0 = 0.9 + 0.85, g1 = 0.7 + 0.7; the sum of all four
+    # would prefer group 1 (0.3 + 0.3 + 1.75 = 2.35 < 2.8).  One group kept, k = 2.
+    sig = np.array([0.9, 0.85, 0.3, 0.3, 0.7, 0.7, 0.7, 0.7])
+    lg = np.log(sig / (1 - sig))[None, :]
+    ids, _, _ = R.select(_grp_layer(8, 2, 2, 1), lg)
+    assert ids[0].tolist() == [0, 1]
+
+
+def test_group_limited_ties_to_lower_group_and_all_groups_kept():
+    # two groups with equal scores: the lower group id is kept
+    lg = np.array([[1.0, 0.5, 1.0, 0.5, -3.0, -3.0]])
+    ids, _, _ = R.select(_grp_layer(6, 2, 3, 1), lg)
+    assert ids[0].tolist() == [0, 1]
+    # every group kept: the same selection as without groups
+    sh = S.custom("grp", n_experts=64, top_k=8, tokens=32, bias_amp=0.3, top_p=0.8)
+    d = _layer(sh)
+    lgs = R.logits(R.Layer(d), S.make_batch(sh, d))
+    a = R.select(R.Layer({**d, "n_group": 8, "topk_group": 8}), lgs)
+    b = R.select(R.Layer(d), lgs)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_group_limited_bruteforce():
+    # E = 16 in 4 groups of 4, 2 groups kept, k = 4: (i) every pick lies in a kept group,
+    # (ii) no group outside the kept two has a larger top-2 score than a kept one,
+    # (iii) the picked set maximises the summed choice over all 4-subsets of the kept
+    # groups' experts (brute force), and the order is descending choice
+    sh = S.custom("grpbf", n_experts=16, top_k=4, tokens=24, bias_amp=0.2)
+    d = {**_layer(sh), "n_group": 4, "topk_group": 2}
+    L = R.Layer(d)
+    x = S.make_batch(sh, d)
+    ids, _, _ = R.route(L, x)
+    choice = _sig(R.logits(L, x)) + d["router_bias"].astype(np.float64)[None, :]
+    for t in range(x.shape[0]):
+        c = choice[t].reshape(4, 4)
+        top2 = np.sort(c, axis=1)[:, -2:].sum(axis=1)
+        kept = sorted(set((ids[t] // 4).tolist()))
+        assert len(kept) <= 2
+        out = [g for g in range(4) if g not in kept]
+        if len(kept) == 2:
+            assert all(top2[o] <= min(top2[kept]) for o in out)
+        allowed = [e for g in range(4) for e in range(4 * g, 4 * g + 4)
+                   if g in kept or (len(kept) < 2 and top2[g] >= max(top2[out]))]
+        best = max(itertools.combinations(allowed, 4), key=lambda S_: sum(choice[t][list(S_)]))
+        assert set(ids[t].tolist()) == set(best)
+        assert np.all(np.diff(choice[t][ids[t]]) <= 0)
+
+
+def test_group_limited_rejects_bad_groups():
+    lg = np.zeros((1, 8))
+    for ng, tg in [(3, 1), (8, 1), (4, 0), (4, 5), (4, 1)]:  # uneven, singletons, 0, > n, too few
+        with pytest.raises(ValueError):
+            R.select(_grp_layer(8, 4, ng, tg), lg)
+
+
+# --------------------------------------------------------------------------- first-dense MLP
+def test_dense_mlp_is_plain_swiglu():
+    H, F, T = 128, 192, 5
+    rng = np.random.default_rng(7)
+    gq, gs = R.quantize_gs64((rng.standard_normal((F, H)) * 0.05).astype(np.float32))
+    uq, us = R.quantize_gs64((rng.standard_normal((F, H)) * 0.05).astype(np.float32))
+    dq, ds = R.quantize_gs64((rng.standard_normal((H, F)) * 0.05).astype(np.float32))
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    out = R.dense_mlp(gq, gs, uq, us, dq, ds, x)
+    g = x.astype(np.float64) @ R.dequantize_gs64(gq, gs).T
+    u = x.astype(np.float64) @ R.dequantize_gs64(uq, us).T
+    ref = (g * expit(g) * u) @ R.dequantize_gs64(dq, ds).T
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
+
+
 # --------------------------------------------------------------------------- union
 def _union_bruteforce(E, ids, keff):
     T, k = ids.shape
