@@ -195,6 +195,83 @@ size_t moe_dense_workspace_bytes(const moe_dense *D, int32_t max_tokens);
 int moe_dense_forward(const moe_dense *D, const float *x, int32_t T, void *out, int32_t out_dtype,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* ---- expert residency tier ---------------------------------------------
+ * HBM as a cache over an expert bank in pinned host memory ([R] §1.3 cache resolution,
+ * §3 multi-level expert cache, §4 tier repin, §5 router-lookahead prefetch; [C] §2.1 VRAM
+ * expert tier).  One tier serves one layer (the pages keep one LRU per layer).
+ *
+ * The layer's ROUTED expert tensors (gate/up/down q and s in the moe_layer) are the
+ * backing store: stacked by expert id as usual, in pinned host memory (hipHostMalloc,
+ * e.g. torch's pin_memory; not hipHostRegister), given as the device-side addresses of
+ * that memory (hipHostGetDevicePointer), 16-byte aligned.  The router and
+ * the shared expert stay in device memory.  The tier's n_slots HBM slots each hold one
+ * expert (moe_tier_slot_bytes: gate q, gate s, up q, up s, down q, down s, each
+ * 256-byte aligned); the first n_pinned slots form the pinned hot store.
+ *
+ * Per forward, after the batch union, one workgroup resolves every union expert in
+ * ascending id order: a resident expert (pinned or cached) is a hit and its slot is
+ * stamped with the step number; a missing one takes a victim slot and is copied there
+ * from host memory.  Victims are the slots that are neither pinned nor holding an
+ * expert of this union, least recently used first (empty slots first, then the
+ * smallest stamp, ties to the lower slot index), handed to the misses in ascending
+ * expert id order ([R] §1.3: LRU, evict the least used).  Each union expert's heat and
+ * usage grow by its row count ([R] §1.2: eheat/eusage).  The copies run on the call's
+ * stream before the expert FFNs, which read every union expert from its slot.  Nothing
+ * is synchronised with or copied to the host.
+ *
+ * State (moe_tier_state_bytes, device, 256-byte aligned; all int32 unless stated, in
+ * this order, each array starting at a multiple of 4 bytes):
+ *   hdr[16]: [0] step count, [1] copies made by the last call, [2] hits, [3] misses,
+ *            [4] swaps by repin, [5] experts prefetched, [6] n_slots, [7] n_experts
+ *            (2-5 cumulative since moe_tier_init), rest 0;
+ *   slot_expert[S] (-1 = empty), slot_pinned[S] (0/1), slot_used[S] (stamp, -1 empty),
+ *   expert_slot[E] (-1 = not resident), heat[E] (uint32, halved by each repin pass),
+ *   usage[E] (uint32, never decayed), copy_list[2*min(E,S)] (expert, slot) of the last
+ *   call's copies; then, 16-byte aligned, moe_q4 table[3*E] (gate, up, down of every
+ *   resident expert; the FFNs' view).
+ * Calls on one tier must be ordered (one stream, or events between streams). */
+typedef struct {
+    int32_t n_slots;   /* S >= 1 */
+    int32_t n_pinned;  /* pinned slots 0 .. n_pinned-1 (fixed by moe_tier_init) */
+    void *slots;       /* device, n_slots * moe_tier_slot_bytes(L) bytes, 256-byte aligned */
+    void *state;       /* device, moe_tier_state_bytes(L, n_slots) bytes, 256-byte aligned */
+} moe_tier;
+
+size_t moe_tier_slot_bytes(const moe_layer *L);
+size_t moe_tier_state_bytes(const moe_layer *L, int32_t n_slots);
+
+/* Resets the tier: every slot empty, heat and usage 0, counters 0; then loads the
+ * experts pins[0 .. n_pin-1] (host array, distinct ids in [0, E), n_pin == tier->n_pinned
+ * <= min(n_slots, 256)) into slots 0 .. n_pin-1 as the pinned hot store ([R] §3.1: the
+ * caller picks them, e.g. the hottest experts of a usage histogram). */
+int moe_tier_init(const moe_layer *L, const moe_tier *tier, const int32_t *pins, int32_t n_pin,
+                  void *stream);
+
+/* moe_layer_forward with the routed experts read through the tier (above).  Needs
+ * n_slots - n_pinned >= min(E, T*k) (MOE_EUNSUPPORTED otherwise).  Same outputs,
+ * bit for bit, as moe_layer_forward on the same layer held in device memory. */
+int moe_tier_layer_forward(const moe_layer *L, const moe_tier *tier, const float *x, int32_t T,
+                           void *out, int32_t out_dtype, const moe_route_out *dbg, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Router-lookahead prefetch ([R] §5): makes the distinct experts of the predicted picks
+ * ids [T][k] (device, slots at or past keff[t] and ids outside [0, E) ignored) resident,
+ * as the resolution above does, without counting heat, usage, hits or misses and
+ * without advancing the step: fetched and already-resident experts are stamped with
+ * the current step.  Meant for the next layer's tier on a copy stream while this layer
+ * computes (the predicted ids from moe_route of that layer's router on this layer's
+ * input).  Needs n_slots - n_pinned >= min(E, T*k). */
+int moe_tier_prefetch(const moe_layer *L, const moe_tier *tier, const int32_t *ids,
+                      const int32_t *keff, int32_t T, void *stream);
+
+/* Heat-driven repin ([R] §4): up to max_swaps (1..4) times, the coldest pinned expert
+ * fc (lowest heat, ties to the lower expert id) is exchanged with the hottest unpinned
+ * expert fh (highest heat, ties to the lower id) if heat[fh] > heat[fc] + heat[fc]/4 + 4
+ * (integer division), else the pass stops.  An fh already cached takes over the pinned
+ * flag (fc's slot becomes an ordinary cache slot); otherwise fh is copied into fc's slot
+ * and fc leaves HBM.  Then every heat is halved (shift right by one). */
+int moe_tier_repin(const moe_layer *L, const moe_tier *tier, int32_t max_swaps, void *stream);
+
 /* Glue between stacked MoE layers -- not a step of the layer itself.  For each of
  * the T rows of H fp32 values: h_out = h + delta (delta NULL: h_out = h), then
  * x_out = h_out / sqrt(mean(h_out^2) + eps) (RMSNorm with unit gain), fp32 with

@@ -23,7 +23,9 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 1638
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
            "moe_layer_forward", "moe_residual_rmsnorm", "moe_strerror", "moe_prof_begin",
            "moe_prof_end", "moe_expert_ffn_probe", "moe_layer_forward_static", "moe_probe_read",
-           "moe_dense_workspace_bytes", "moe_dense_forward")
+           "moe_dense_workspace_bytes", "moe_dense_forward", "moe_tier_slot_bytes",
+           "moe_tier_state_bytes", "moe_tier_init", "moe_tier_layer_forward", "moe_tier_prefetch",
+           "moe_tier_repin")
 MOE_STATIC_SCRATCH_BYTES = 64 << 20
 MOE_GU_SWIGLU, MOE_GU_GATE, MOE_GU_UP = 0, 1, 2
 
@@ -53,6 +55,11 @@ class LayerC(ctypes.Structure):
 class DenseC(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("gate", Q4), ("up", Q4), ("down", Q4)]
+
+
+class TierC(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("n_pinned", ctypes.c_int32),
+                ("slots", ctypes.c_void_p), ("state", ctypes.c_void_p)]
 
 
 class ProfStatC(ctypes.Structure):
@@ -100,6 +107,19 @@ def lib():
     L.moe_dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseC), i32]
     L.moe_dense_forward.restype = ctypes.c_int
     L.moe_dense_forward.argtypes = [ctypes.POINTER(DenseC), vp, i32, vp, i32, vp, sz, vp]
+    T_ = ctypes.POINTER(TierC)
+    L.moe_tier_slot_bytes.restype = sz
+    L.moe_tier_slot_bytes.argtypes = [P]
+    L.moe_tier_state_bytes.restype = sz
+    L.moe_tier_state_bytes.argtypes = [P, i32]
+    L.moe_tier_init.restype = ctypes.c_int
+    L.moe_tier_init.argtypes = [P, T_, vp, i32, vp]
+    L.moe_tier_layer_forward.restype = ctypes.c_int
+    L.moe_tier_layer_forward.argtypes = [P, T_, vp, i32, vp, i32, ctypes.POINTER(RouteOutC), vp, sz, vp]
+    L.moe_tier_prefetch.restype = ctypes.c_int
+    L.moe_tier_prefetch.argtypes = [P, T_, vp, vp, i32, vp]
+    L.moe_tier_repin.restype = ctypes.c_int
+    L.moe_tier_repin.argtypes = [P, T_, i32, vp]
     L.moe_probe_read.restype = ctypes.c_int
     L.moe_probe_read.argtypes = [vp, sz, ctypes.c_uint32, vp, i32, vp]
     L.moe_layer_forward_static.restype = ctypes.c_int
@@ -308,6 +328,87 @@ def moe_dense_forward(dense: Dense, x, out=None, out_dtype: int = MOE_F32, ws=No
     _check(lib().moe_dense_forward(dense.ref(), _ptr(x), T, _ptr(out), out_dtype, _ptr(ws), ws.numel(),
                                    _stream(stream)), "moe_dense_forward")
     return out
+
+
+class Tier:
+    """A residency tier for one layer: n_slots HBM slots (the first n_pinned pinned) over
+    the layer's routed experts, which live in pinned host memory (see moe.h)."""
+
+    def __init__(self, layer: Layer, n_slots: int, n_pinned: int = 0, device="cuda"):
+        import torch
+        L = lib()
+        self.layer = layer
+        self.slot_bytes = int(L.moe_tier_slot_bytes(layer.ref()))
+        nb = int(L.moe_tier_state_bytes(layer.ref(), int(n_slots)))
+        if self.slot_bytes == 0 or nb == 0:
+            raise MoeError(MOE_EINVAL, "moe_tier_*_bytes")
+        self.slots = torch.empty(int(n_slots) * self.slot_bytes + 256, dtype=torch.uint8, device=device)
+        self.state = torch.empty(nb + 256, dtype=torch.uint8, device=device)
+        sp, tp = _align256(self.slots.data_ptr()), _align256(self.state.data_ptr())
+        self.c = TierC(int(n_slots), int(n_pinned), sp, tp)
+        self._state_off = tp - self.state.data_ptr()
+        self.n_slots, self.n_pinned, self.state_bytes = int(n_slots), int(n_pinned), nb
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def init(self, pins=(), stream=None):
+        arr = (ctypes.c_int32 * max(len(pins), 1))(*[int(p) for p in pins])
+        _check(lib().moe_tier_init(self.layer.ref(), self.ref(), arr, len(pins), _stream(stream)),
+               "moe_tier_init")
+
+    def forward(self, x, out=None, out_dtype: int = MOE_F32, dbg: dict | None = None, ws=None,
+                stream=None):
+        import torch
+        T, H = x.shape[0], self.layer.hidden
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32,
+                              device=x.device)
+        ws = self.layer.workspace(T, x.device) if ws is None else ws
+        rc = None
+        if dbg:
+            rc = RouteOutC(**{k: (v.data_ptr() if v is not None else None) for k, v in dbg.items()})
+        _check(lib().moe_tier_layer_forward(self.layer.ref(), self.ref(), _ptr(x), T, _ptr(out), out_dtype,
+                                            ctypes.byref(rc) if rc is not None else None, _ptr(ws),
+                                            ws.numel(), _stream(stream)), "moe_tier_layer_forward")
+        return out
+
+    def prefetch(self, ids, keff, stream=None):
+        _check(lib().moe_tier_prefetch(self.layer.ref(), self.ref(), _ptr(ids), _ptr(keff),
+                                       ids.shape[0], _stream(stream)), "moe_tier_prefetch")
+
+    def repin(self, max_swaps: int = 4, stream=None):
+        _check(lib().moe_tier_repin(self.layer.ref(), self.ref(), int(max_swaps), _stream(stream)),
+               "moe_tier_repin")
+
+    def read_state(self) -> dict:
+        """The state arrays (waits for the device), in the layout moe.h documents."""
+        import torch
+        torch.cuda.synchronize()
+        b = self.state[self._state_off:self._state_off + self.state_bytes].cpu().numpy()
+        S, E = self.n_slots, self.layer.n_experts
+        w = b.view(np.int32)
+        o = 0
+
+        def take(n):
+            nonlocal o
+            a = w[o:o + n].copy()
+            o += n
+            return a
+        hdr = take(16)
+        st = dict(step=int(hdr[0]), copies_last=int(hdr[1]), hits=int(hdr[2]), misses=int(hdr[3]),
+                  swaps=int(hdr[4]), prefetched=int(hdr[5]))
+        st["slot_expert"], st["slot_pinned"], st["slot_used"] = take(S), take(S), take(S)
+        st["expert_slot"] = take(E)
+        st["heat"], st["usage"] = take(E).view(np.uint32), take(E).view(np.uint32)
+        mc = max(min(E, S), 4)
+        cp = take(2 * mc).reshape(mc, 2)
+        st["copies"] = [tuple(int(v) for v in cp[i]) for i in range(st["copies_last"])]
+        return st
+
+
+def _align256(p: int) -> int:
+    return (p + 255) // 256 * 256
 
 
 def moe_residual_rmsnorm(h, delta=None, eps: float = 1e-6, h_out=None, x_out=None, stream=None):

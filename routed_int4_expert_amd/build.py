@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
-SOURCES = ["moe_api.cpp", "moe_static.hip", "prof.cpp", "route.hip", "union.hip", "ffn_gemv.hip", "ffn_mfma.hip", "combine.hip", "glue.hip", "probe.hip"]
+SOURCES = ["moe_api.cpp", "moe_static.hip", "prof.cpp", "route.hip", "union.hip", "ffn_gemv.hip", "ffn_mfma.hip", "combine.hip", "glue.hip", "probe.hip", "tier.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

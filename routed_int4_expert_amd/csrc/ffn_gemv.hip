@@ -326,15 +326,24 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         nrows = a.T == 1 ? 1 : off_p[e + 1] - r0;
         Fu = a.F;
         if (GU) {
-            const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
-            m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
-            m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
+            if (a.tab) {  // the residency tier's slots
+                m0 = a.tab[3 * e];
+                m1 = a.tab[3 * e + 1];
+            } else {
+                const size_t gq = (size_t)e * Fu * (H / 2), gs = (size_t)e * Fu * (H / 64);
+                m0.q = a.gate.q + gq; m0.s = a.gate.s + gs;
+                m1.q = a.up.q + gq;   m1.s = a.up.s + gs;
+            }
             rt = row_tok_p + r0;
             xin = a.x;
             out = a.h_routed;
         } else {
-            const size_t dq = (size_t)e * H * (Fu / 2), ds = (size_t)e * H * (Fu / 64);
-            m0.q = a.down.q + dq; m0.s = a.down.s + ds;
+            if (a.tab) {
+                m0 = a.tab[3 * e + 2];
+            } else {
+                const size_t dq = (size_t)e * H * (Fu / 2), ds = (size_t)e * H * (Fu / 64);
+                m0.q = a.down.q + dq; m0.s = a.down.s + ds;
+            }
             m1 = m0;
             rt = nullptr;
             xin = a.h_routed + (size_t)r0 * Fu;

@@ -410,7 +410,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             if (GU) {
                 K = a.H;
                 N = e >= 0 ? a.F : a.Fs;
-                if (e >= 0) {
+                if (e >= 0 && a.tab) {  // the residency tier's slots
+                    qb0 = a.tab[3 * e].q;     sb0 = a.tab[3 * e].s;
+                    qb1 = a.tab[3 * e + 1].q; sb1 = a.tab[3 * e + 1].s;
+                } else if (e >= 0) {
                     const size_t gq = (size_t)e * a.F * (a.H / 2), gs = (size_t)e * a.F * (a.H / 64);
                     qb0 = a.gate.q + gq; sb0 = a.gate.s + gs;
                     qb1 = a.up.q + gq;   sb1 = a.up.s + gs;
@@ -424,8 +427,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
                 if (e >= 0) {
-                    const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
-                    qb0 = a.down.q + dq; sb0 = a.down.s + ds;
+                    if (a.tab) {
+                        qb0 = a.tab[3 * e + 2].q; sb0 = a.tab[3 * e + 2].s;
+                    } else {
+                        const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
+                        qb0 = a.down.q + dq; sb0 = a.down.s + ds;
+                    }
                     abase = a.hr_frag;
                     nbase = a.hr_step;
                 } else {

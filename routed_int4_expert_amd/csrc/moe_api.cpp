@@ -245,6 +245,7 @@ static hipError_t run_union(const moe_layer &L, const int32_t *ids, const int32_
 static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *ws) {
     MfmaArgs m;
     m.gu_out = f.gu_out;
+    m.tab = f.tab;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
     m.x_step = at<float>(ws, p.x_step);
@@ -297,6 +298,7 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
                         int gu_out = kGuSwiglu) {
     FfnArgs a;
     a.gu_out = gu_out;
+    a.tab = nullptr;
     a.x = x;
     a.n_uniq = n_uniq;
     a.uniq = uniq;
@@ -327,6 +329,42 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
 }
 
 
+// ---------------------------------------------------------------- residency tier
+static int check_tier(const moe_tier *t) {
+    if (!t) return MOE_EINVAL;
+    if (t->n_slots < 1 || t->n_pinned < 0 || t->n_pinned > t->n_slots) return MOE_EINVAL;
+    if (t->n_slots > kTierMaxSlots || t->n_pinned > kTierMaxPins) return MOE_EUNSUPPORTED;
+    if (!t->slots || !t->state) return MOE_EINVAL;
+    if (((uintptr_t)t->slots & 255u) || ((uintptr_t)t->state & 255u)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+static TierArgs tier_args(const moe_layer &L, const moe_tier &t) {
+    TierArgs a;
+    a.lay = tier_layout(L.hidden, L.ffn, L.n_experts, t.n_slots);
+    a.slots = static_cast<uint8_t *>(t.slots);
+    a.state = static_cast<uint8_t *>(t.state);
+    a.gate = L.gate;
+    a.up = L.up;
+    a.down = L.down;
+    a.H = L.hidden;
+    a.F = L.ffn;
+    a.n_pinned = t.n_pinned;
+    return a;
+}
+
+// copies a resolution of T tokens can need: one per union expert, at most one per free slot
+int tier_jobs(const moe_layer &L, const TierArgs &t, int T) {
+    const long u = min((long)L.n_experts, (long)T * L.top_k);
+    const long free_slots = (long)t.lay.S - t.n_pinned;
+    return (int)min(u, free_slots);
+}
+
+// the unpinned slots hold a whole union of T tokens
+static bool tier_fits(const moe_layer &L, const moe_tier &t, int T) {
+    return (long)t.n_slots - t.n_pinned >= min((long)L.n_experts, (long)T * L.top_k);
+}
+
 // moe_layer_forward's host-only argument checks (no HIP call): MOE_OK or the error code.
 int layer_forward_validate(const moe_layer *L, const float *x, int32_t T, const void *out,
                            int32_t out_dtype) {
@@ -344,7 +382,7 @@ int device_ok() { return check_device(); }
 
 // The launch sequence of the layer on a validated call (T > 0, ws large enough for T).
 int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
-                      const moe_route_out *dbg, void *ws, hipStream_t st) {
+                      const moe_route_out *dbg, void *ws, hipStream_t st, const TierArgs *tier) {
     const Plan p = make_plan(*L, T);
     moe_route_out d;
     memset(&d, 0, sizeof(d));
@@ -359,8 +397,9 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
     int32_t *pick_row = d.pick_row ? d.pick_row : at<int32_t>(ws, p.pick_row);
 
     hipError_t e;
-    // one token: selection and union run inside the gate/up launch
-    const bool sel_in_ffn = T == 1;
+    // one token: selection and union run inside the gate/up launch (not with a residency
+    // tier, which resolves the union before the expert FFNs start)
+    const bool sel_in_ffn = T == 1 && !tier;
     float *y_routed = at<float>(ws, p.y_routed);
     FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
     if (sel_in_ffn) {
@@ -374,7 +413,7 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
     } else {
         e = run_route(*L, p, x, T, ids, w, keff, ws, st);
         // the union inside the first matrix-core preparation launch when it fits there
-        if (union_in_prep_fits(L->n_experts, T, L->top_k)) {
+        if (!tier && union_in_prep_fits(L->n_experts, T, L->top_k)) {
             a.union_in_prep = 1;
             a.uni = union_args(*L, ids, keff, T, n_uniq, uniq, off, row_tok, pick_row);
         } else if (e == hipSuccess) {
@@ -392,6 +431,18 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
     c.H = L->hidden;
     c.k = L->top_k;
     c.out_bf16 = out_dtype == MOE_BF16;
+    if (e == hipSuccess && tier) {
+        // residency tier: every union expert resident (copies from the backing store for
+        // the misses); the expert FFNs read them through the tier's table
+        TierResolveIn in;
+        memset(&in, 0, sizeof(in));
+        in.n_uniq = n_uniq;
+        in.uniq = uniq;
+        in.off = off;
+        e = launch_tier_resolve(*tier, in, st);
+        if (e == hipSuccess) e = launch_tier_copy(*tier, tier_jobs(*L, *tier, T), st);
+        a.tab = reinterpret_cast<const moe_q4 *>(tier->state + tier->lay.tab);
+    }
     if (e == hipSuccess) {
         if (sel_in_ffn) {
             a.fuse_select = 1;
@@ -538,7 +589,90 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
     if (T == 0) return MOE_OK;
     if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
     if ((rc = check_device())) return rc;
-    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream);
+    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream, nullptr);
+}
+
+size_t moe_tier_slot_bytes(const moe_layer *L) {
+    if (check_dims(L) != MOE_OK) return 0;
+    return tier_layout(L->hidden, L->ffn, L->n_experts, 1).slot;
+}
+
+size_t moe_tier_state_bytes(const moe_layer *L, int32_t n_slots) {
+    if (check_dims(L) != MOE_OK || n_slots < 1 || n_slots > kTierMaxSlots) return 0;
+    return tier_layout(L->hidden, L->ffn, L->n_experts, n_slots).total;
+}
+
+int moe_tier_init(const moe_layer *L, const moe_tier *tier, const int32_t *pins, int32_t n_pin,
+                  void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_tier(tier))) return rc;
+    if (n_pin != tier->n_pinned || (n_pin > 0 && !pins)) return MOE_EINVAL;
+    TierPins tp;
+    memset(&tp, 0, sizeof(tp));
+    unsigned char seen[MOE_MAX_EXPERTS];
+    memset(seen, 0, sizeof(seen));
+    for (int i = 0; i < n_pin; i++) {
+        if (pins[i] < 0 || pins[i] >= L->n_experts || seen[pins[i]]) return MOE_EINVAL;
+        seen[pins[i]] = 1;
+        tp.id[i] = pins[i];
+    }
+    if ((rc = check_experts(L, true, false))) return rc;
+    if ((rc = check_device())) return rc;
+    const TierArgs a = tier_args(*L, *tier);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_tier_init(a, tp, n_pin, st);
+    if (e == hipSuccess) e = launch_tier_copy(a, n_pin, st);
+    return launched(e);
+}
+
+int moe_tier_layer_forward(const moe_layer *L, const moe_tier *tier, const float *x, int32_t T,
+                           void *out, int32_t out_dtype, const moe_route_out *dbg, void *ws,
+                           size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = layer_forward_validate(L, x, T, out, out_dtype))) return rc;
+    if ((rc = check_tier(tier))) return rc;
+    if (T == 0) return MOE_OK;
+    if (!tier_fits(*L, *tier, T)) return MOE_EUNSUPPORTED;
+    if ((rc = check_ws(L, T, ws, ws_bytes))) return rc;
+    if ((rc = check_device())) return rc;
+    const TierArgs a = tier_args(*L, *tier);
+    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream, &a);
+}
+
+int moe_tier_prefetch(const moe_layer *L, const moe_tier *tier, const int32_t *ids,
+                      const int32_t *keff, int32_t T, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_T(T)) || (rc = check_tier(tier))) return rc;
+    if (T == 0) return MOE_OK;
+    if (!ids || !keff) return MOE_EINVAL;
+    if (!tier_fits(*L, *tier, T)) return MOE_EUNSUPPORTED;
+    if ((rc = check_experts(L, true, false))) return rc;
+    if ((rc = check_device())) return rc;
+    const TierArgs a = tier_args(*L, *tier);
+    TierResolveIn in;
+    memset(&in, 0, sizeof(in));
+    in.ids = ids;
+    in.keff = keff;
+    in.T = T;
+    in.k = L->top_k;
+    in.prefetch = 1;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_tier_resolve(a, in, st);
+    if (e == hipSuccess) e = launch_tier_copy(a, tier_jobs(*L, a, T), st);
+    return launched(e);
+}
+
+int moe_tier_repin(const moe_layer *L, const moe_tier *tier, int32_t max_swaps, void *stream) {
+    int rc;
+    if ((rc = check_dims(L)) || (rc = check_tier(tier))) return rc;
+    if (max_swaps < 1 || max_swaps > 4) return MOE_EINVAL;
+    if ((rc = check_experts(L, true, false))) return rc;
+    if ((rc = check_device())) return rc;
+    const TierArgs a = tier_args(*L, *tier);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_tier_repin(a, max_swaps, st);
+    if (e == hipSuccess) e = launch_tier_copy(a, max_swaps, st);
+    return launched(e);
 }
 
 size_t moe_dense_workspace_bytes(const moe_dense *D, int32_t max_tokens) {

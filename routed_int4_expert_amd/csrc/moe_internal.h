@@ -132,6 +132,9 @@ struct FfnArgs {
     int T, H, F, Fs, max_units;
     int with_routed, with_shared;
     int gu_out;  // what the gate/up step writes as h: kGuSwiglu, kGuGate or kGuUp
+    // routed expert e's gate, up and down matrices: tab[3e], tab[3e+1], tab[3e+2] (the
+    // residency tier's slots), or, when null, the stacked gate/up/down above
+    const moe_q4 *tab;
     // Selection and union inside the gate/up launch (one token): every routed
     // workgroup selects and builds the union in LDS from the router logits; the
     // first routed workgroup also writes them out through sel (ids, w, keff) and uni
@@ -172,6 +175,7 @@ struct MfmaArgs {
     int T, H, F, Fs, E, max_units, max_rows, max_items;
     int item_rows;  // rows per work item: 16 or kMfmaItemRows
     int gu_out;     // as FfnArgs::gu_out
+    const moe_q4 *tab;  // as FfnArgs::tab
     int with_routed, with_shared;
     int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
     UnionArgs uni;
@@ -200,9 +204,80 @@ bool union_in_prep_fits(int E, int T, int k);
 // launch sequence.  device_ok: the lazy once-per-device gfx950 check.
 int layer_forward_validate(const moe_layer *L, const float *x, int32_t T, const void *out,
                            int32_t out_dtype);
+struct TierArgs;
 int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, int32_t out_dtype,
-                      const moe_route_out *dbg, void *ws, hipStream_t st);
+                      const moe_route_out *dbg, void *ws, hipStream_t st, const TierArgs *tier);
 int device_ok();
+
+// ---------------------------------------------------------------- residency tier
+// Byte layout of a tier slot (one expert) and of the tier state (see moe.h).
+constexpr int kTierMaxSlots = 1024;
+constexpr int kTierMaxPins = 256;
+
+struct TierLayout {
+    size_t gq, gs, uq, us, dq, ds, slot;                        // within a slot; slot bytes
+    size_t hdr, slot_expert, slot_pinned, slot_used, expert_slot, heat, usage, copies, tab, total;
+    int S, E, max_copies;
+};
+
+__host__ __device__ inline size_t tier_align(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+__host__ __device__ inline TierLayout tier_layout(int H, int F, int E, int S) {
+    TierLayout t;
+    size_t o = 0;
+    const size_t wq = (size_t)F * H / 2, ws = (size_t)F * (H / 64) * 4;  // one matrix's codes, scales
+    t.gq = o; o = tier_align(o + wq, 256);
+    t.gs = o; o = tier_align(o + ws, 256);
+    t.uq = o; o = tier_align(o + wq, 256);
+    t.us = o; o = tier_align(o + ws, 256);
+    t.dq = o; o = tier_align(o + wq, 256);
+    t.ds = o; o = tier_align(o + ws, 256);
+    t.slot = o;
+    t.S = S;
+    t.E = E;
+    t.max_copies = E < S ? E : S;
+    if (t.max_copies < 4) t.max_copies = 4;  // a repin pass copies up to four experts
+    o = 0;
+    t.hdr = o; o += 16 * 4;
+    t.slot_expert = o; o += (size_t)S * 4;
+    t.slot_pinned = o; o += (size_t)S * 4;
+    t.slot_used = o; o += (size_t)S * 4;
+    t.expert_slot = o; o += (size_t)E * 4;
+    t.heat = o; o += (size_t)E * 4;
+    t.usage = o; o += (size_t)E * 4;
+    t.copies = o; o += (size_t)2 * t.max_copies * 4;
+    o = tier_align(o, 16);
+    t.tab = o; o += (size_t)3 * E * sizeof(moe_q4);
+    t.total = tier_align(o, 256);
+    return t;
+}
+
+struct TierArgs {
+    TierLayout lay;
+    uint8_t *slots;
+    uint8_t *state;
+    moe_q4 gate, up, down;  // the host backing store, stacked by expert id
+    int H, F, n_pinned;
+};
+
+struct TierPins {
+    int32_t id[kTierMaxPins];
+};
+
+// Resolution of a forward's union (n_uniq/uniq/off) or, for a prefetch, of the distinct
+// experts of predicted picks (ids/keff).
+struct TierResolveIn {
+    const int32_t *n_uniq, *uniq, *off;
+    const int32_t *ids, *keff;
+    int T, k, prefetch;
+};
+
+hipError_t launch_tier_init(const TierArgs &a, const TierPins &pins, int n_pin, hipStream_t st);
+hipError_t launch_tier_resolve(const TierArgs &a, const TierResolveIn &in, hipStream_t st);
+hipError_t launch_tier_repin(const TierArgs &a, int max_swaps, hipStream_t st);
+// copies the state's copy list (at most max_jobs entries) from the backing store into slots
+hipError_t launch_tier_copy(const TierArgs &a, int max_jobs, hipStream_t st);
+int tier_jobs(const moe_layer &L, const TierArgs &t, int T);
 
 // Bracketing HIP events around one kernel launch while moe_prof_begin() is active.
 struct ProfScope {

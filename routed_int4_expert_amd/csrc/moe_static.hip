@@ -62,5 +62,5 @@ extern "C" int moe_layer_forward_static(const moe_layer *L, const float *x, int3
     }
     void *ws = scratch_on(dev);
     if (!ws) return MOE_EDEVICE;
-    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream);
+    return layer_forward_run(L, x, T, out, out_dtype, dbg, ws, (hipStream_t)stream, nullptr);
 }
