@@ -457,17 +457,164 @@ def run_workload(wl, args, dev):
     return rec_out, extra
 
 
+def _device_address(t):
+    """Device-side address of a pinned host tensor (hipHostGetDevicePointer)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipHostGetDevicePointer.restype = ctypes.c_int
+    hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    p = ctypes.c_void_p()
+    if hip.hipHostGetDevicePointer(ctypes.byref(p), ctypes.c_void_p(t.data_ptr()), 0) != 0 or not p.value:
+        raise RuntimeError("hipHostGetDevicePointer failed")
+    return p.value
+
+
+def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
+    """Decode through n_layers GLM-shaped layers whose routed experts (5.4 GB each) live in
+    pinned host memory, each layer with a residency tier of n_slots HBM slots (n_pin pinned,
+    chosen from a usage warm-up).  One token per step, Zipf-skewed routing with top-p 0.7.
+    Timed without and with router-lookahead prefetch (layer l+1's router on layer l's
+    input, on a copy stream), and with every expert resident in HBM for comparison."""
+    import dataclasses
+    import torch
+    import routed_int4_expert_amd as M
+    from routed_int4_expert_amd import synth as S
+
+    sh = dataclasses.replace(S.SHAPES["glm_stack16"], name="glm_tier", tokens=1, layers=n_layers)
+    T, H, E = 1, sh.hidden, sh.n_experts
+    bank = bank_for(sh)
+    t0 = time.time()
+    layers, res_layers, tiers = [], [], []
+    for l in range(n_layers):
+        rw, rb = S.router(sh, 0, l)
+        perm = S.layer_perm(sh, 0, l)
+        host = bank.permuted(perm)
+        ts = {k: torch.from_numpy(host[k]).pin_memory() for k in S.Bank.ROUTED}
+        del host
+        ts.update({k: torch.from_numpy(getattr(bank, k)).to(dev) for k in S.Bank.SHARED})
+        ts["router_w"], ts["router_bias"] = torch.from_numpy(rw).to(dev), torch.from_numpy(rb).to(dev)
+        lay = M.Layer(S.layer_params(sh), ts)
+        for name in ("gate", "up", "down"):
+            setattr(lay.c, name, M.Q4(_device_address(ts[name + "_q"]), _device_address(ts[name + "_s"])))
+        layers.append(lay)
+        rts = {k: v.to(dev) if k in S.Bank.ROUTED else v for k, v in ts.items()}
+        res_layers.append(M.Layer(S.layer_params(sh), rts))
+    log(f"glm_tier: {n_layers} layers in pinned host memory ({n_layers * 5.46:.1f} GB) and resident "
+        f"copies ready in {time.time() - t0:.1f} s")
+    npool = 64
+    xs = torch.from_numpy(S.tokens(sh, npool, seed=0)).to(dev)
+    hbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
+    xbuf = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = layers[0].workspace(T, dev)
+    ws2 = layers[0].workspace(T, dev)
+    pid = torch.empty((T, sh.top_k), dtype=torch.int32, device=dev)
+    pw = torch.empty((T, sh.top_k), dtype=torch.float32, device=dev)
+    pk = torch.empty((T,), dtype=torch.int32, device=dev)
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+
+    def step(i, fwd_of, prefetch=False):
+        x = xs[i % npool:i % npool + 1]
+        M.moe_residual_rmsnorm(x, None, h_out=hbuf, x_out=xbuf[0])
+        for l in range(n_layers):
+            if l > 0:
+                M.moe_residual_rmsnorm(hbuf, out, h_out=hbuf, x_out=xbuf[l])
+            if prefetch and l + 1 < n_layers:
+                ev = torch.cuda.Event()
+                ev.record(comp)
+                copy.wait_event(ev)
+                with torch.cuda.stream(copy):
+                    M.moe_route(layers[l + 1], xbuf[l], pid, pw, pk, ws=ws2, stream=copy)
+                    tiers[l + 1].prefetch(pid, pk, stream=copy)
+            if prefetch and l > 0:
+                comp.wait_stream(copy)
+            fwd_of(l, xbuf[l])
+
+    def tier_fwd(l, x):
+        tiers[l].forward(x, out=out, ws=ws)
+
+    def res_fwd(l, x):
+        M.moe_layer_forward(res_layers[l], x, out=out, ws=ws)
+
+    # usage warm-up with unpinned tiers, then autopin the hottest experts of each layer
+    warm = [M.Tier(layers[l], n_slots, 0) for l in range(n_layers)]
+    for w in warm:
+        w.init([])
+    tiers[:] = warm
+    for i in range(32):
+        step(i, tier_fwd)
+    pins = []
+    for w in warm:
+        u = w.read_state()["usage"].astype(np.int64)
+        pins.append([int(e) for e in np.argsort(-u, kind="stable")[:n_pin]])
+    del warm
+    tiers[:] = [M.Tier(layers[l], n_slots, n_pin) for l in range(n_layers)]
+    res = {}
+    K = max(args.steps, 32)
+    for mode in ("no_prefetch", "prefetch"):
+        for l in range(n_layers):
+            tiers[l].init(pins[l])
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step(1000 + i, tier_fwd, prefetch=(mode == "prefetch"))
+        torch.cuda.synchronize()
+        st0 = [t.read_state() for t in tiers]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            step(2000 + i, tier_fwd, prefetch=(mode == "prefetch"))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        st1 = [t.read_state() for t in tiers]
+        hits = sum(b["hits"] - a["hits"] for a, b in zip(st0, st1))
+        miss = sum(b["misses"] - a["misses"] for a, b in zip(st0, st1))
+        pref = sum(b["prefetched"] - a["prefetched"] for a, b in zip(st0, st1))
+        copied = (miss + pref) * S.expert_bytes(sh)  # misses found resident by a prefetch are not copied twice
+        res[mode] = dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), hit_rate=hits / max(hits + miss, 1),
+                         misses_per_step=miss / K, prefetched_per_step=pref / K,
+                         host_copy_gbps=copied / (K * ms * 1e-3) / 1e9)
+        log(f"glm_tier {mode}: {ms * 1e3:.0f} us/step, hit rate {res[mode]['hit_rate']:.2f}, "
+            f"{res[mode]['misses_per_step']:.1f} misses/step")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        step(2000 + i, res_fwd)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_res = e0.elapsed_time(e1) / K
+    rec = {
+        "value": res["prefetch"]["tokens_per_s"], "unit": "tokens/s",
+        "ms_per_step": res["prefetch"]["ms_per_step"],
+        "config": {"workload": f"glm_tier: {n_layers} GLM-shaped layers, routed experts in pinned host "
+                               f"memory ({n_layers * 5.46:.1f} GB), {n_slots} HBM slots per layer "
+                               f"({n_pin} pinned from a usage warm-up), 1 token/step, top-p 0.7, "
+                               "Zipf(1.1) bias",
+                   "tokens_per_step": T, "layers_per_step": n_layers, "slots_per_layer": n_slots,
+                   "pinned_per_layer": n_pin, "working_set_gb": n_layers * (E + 1) * S.expert_bytes(sh) / 1e9,
+                   "cache_gb": n_layers * n_slots * S.expert_bytes(sh) / 1e9},
+        "tier": res,
+        "all_resident_ms_per_step": ms_res,
+    }
+    del layers, res_layers, tiers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all", "glm_tier"] + sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None,
                     help="resident layer copies cycled per step (default: per workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-tier", action="store_true", help="skip the residency-tier workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-long device buffer 13 times (calibrates the HBM "
                          "byte counters against a transfer of known size) and exit")
@@ -500,7 +647,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    order = DEFAULT_ORDER if args.workload == "all" else (args.workload,)
+    order = DEFAULT_ORDER if args.workload == "all" else (() if args.workload == "glm_tier" else (args.workload,))
     head, head_extra, subs = None, None, {}
     for wl in order:
         rec, extra = run_workload(wl, args, dev)
@@ -512,6 +659,12 @@ def main():
                                             "kernels_us_per_step")}
             log(f"{wl}: {rec['value']:.0f} tokens/s, {rec['ms_per_step'] * 1e3:.1f} us/step, "
                 f"gate/up {rec['roofline']['frac']:.2f} of HBM peak")
+    if args.workload in ("all", "glm_tier") and not args.no_tier:
+        log("glm_tier: residency tier over pinned host memory")
+        subs["glm_tier"] = run_tier(args, dev)
+    if head is None:  # the tier workload alone
+        print(json.dumps(subs["glm_tier"]), flush=True)
+        return
     if subs:
         head["workloads"] = subs
     if not args.no_probe:
