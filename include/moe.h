@@ -87,6 +87,14 @@ typedef struct {
      * (MOE_EINVAL otherwise). */
     int32_t n_group;
     int32_t topk_group;
+    /* Activations entering the expert products: 0 or 16 (default), 16-bit fixed point
+     * per block as described at moe_expert_ffn; 8, the pages' opt-in quantised-activation
+     * path ([C] §2.2: the integer path quantises activations and is opt-in because it
+     * changes results): per block (the same blocks: 32 values for T <= 4, 256 above) the
+     * codes rint(x * 2^n) in [-127, 127] with n the largest integer (at most 149) for
+     * which max|x| * 2^n <= 127, for x and for the SwiGLU output; the matrix-core path
+     * then runs one int8 product per group instead of two.  Other values: MOE_EINVAL. */
+    int32_t act_bits;
 } moe_layer;
 
 /* Optional routing outputs of moe_layer_forward.  Any member may be NULL. */

@@ -40,6 +40,7 @@ class RefLayer(ctypes.Structure):
         ("sh_up_q", ctypes.c_void_p), ("sh_up_s", ctypes.c_void_p),
         ("sh_down_q", ctypes.c_void_p), ("sh_down_s", ctypes.c_void_p),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+        ("act_bits", ctypes.c_int32), ("act_block", ctypes.c_int32),
     ]
 
 
@@ -66,6 +67,7 @@ def _load():
         "moe_ref_layer_forward": (ctypes.c_int, [L, vp, i32, vp, i32, vp]),
         "moe_ref_rmsnorm": (ctypes.c_int, [vp, i32, i32, ctypes.c_double, vp]),
         "moe_ref_dense_mlp": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp]),
+        "moe_ref_quant_act8": (None, [vp, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -103,11 +105,13 @@ class Layer:
         self.top_p, self.norm_topk = float(d["top_p"]), int(d["norm_topk"])
         self.routed_scale = float(d["routed_scale"])
         self.n_group, self.topk_group = int(d.get("n_group", 0)), int(d.get("topk_group", 0))
+        self.act_bits, self.act_block = int(d.get("act_bits", 0)), int(d.get("act_block", 0))
         s = RefLayer()
         s.hidden, s.n_experts, s.ffn = self.hidden, self.n_experts, self.ffn
         s.shared_ffn, s.top_k, s.top_p = self.shared_ffn, self.top_k, self.top_p
         s.norm_topk, s.routed_scale = self.norm_topk, self.routed_scale
         s.n_group, s.topk_group = self.n_group, self.topk_group
+        s.act_bits, s.act_block = self.act_bits, self.act_block
         for k in self.FIELDS:
             setattr(s, k, _p(self.d[k]) if self.d[k] is not None and self.d[k].size else None)
         self.struct = s
@@ -230,6 +234,14 @@ def dense_mlp(gq, gs, uq, us, dq, ds, x: np.ndarray) -> np.ndarray:
     T = x.shape[0]
     out = np.empty((T, H), np.float64)
     _check(_load().moe_ref_dense_mlp(*[_p(a) for a in arrs], H, F, _p(x), T, _p(out)), "dense_mlp")
+    return out
+
+
+def quant_act8(v: np.ndarray, block: int) -> np.ndarray:
+    """The opt-in 8-bit activation rule on one row (fp64 in, fp64 values c * 2^-n out)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    _load().moe_ref_quant_act8(_p(v), v.size, int(block), _p(out))
     return out
 
 

@@ -106,6 +106,8 @@ static int ref_layer_ok(const moe_ref_layer *L) {
     if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > 64) return 0;
     if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return 0;
     if (L->n_group < 0) return 0;
+    if (L->act_bits != 0 && L->act_bits != 16 && L->act_bits != 8) return 0;
+    if (L->act_bits == 8 && L->act_block <= 0) return 0;
     if (L->n_group > 256) return 0;
     if (L->n_group > 1) { /* equal groups of at least two experts, enough experts kept */
         if (L->n_experts % L->n_group != 0 || L->n_experts / L->n_group < 2) return 0;
@@ -333,26 +335,60 @@ int moe_ref_union(int32_t E, int32_t k, const int32_t *ids, const int32_t *keff,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Opt-in 8-bit activations ([C] §2.2)                                         */
+/* ------------------------------------------------------------------------- */
+
+/* The pages' integer (IDOT) path quantises the activations to int8 once per layer and
+ * is opt-in because it changes the results ([C] §2.2).  They give no quantiser; the
+ * reading here: symmetric, one power-of-two step per block of consecutive values, the
+ * largest step exponent that keeps the block's largest magnitude within 127. */
+void moe_ref_quant_act8(const double *v, int32_t K, int32_t block, double *out) {
+    for (int32_t b0 = 0; b0 < K; b0 += block) {
+        const int32_t b1 = b0 + block < K ? b0 + block : K;
+        double amax = 0.0;
+        for (int32_t i = b0; i < b1; i++)
+            if (fabs(v[i]) > amax) amax = fabs(v[i]);
+        if (amax == 0.0) {
+            for (int32_t i = b0; i < b1; i++) out[i] = 0.0;
+            continue;
+        }
+        int n = 149; /* the largest n <= 149 with amax * 2^n <= 127 */
+        while (ldexp(amax, n) > 127.0) n--;
+        for (int32_t i = b0; i < b1; i++) out[i] = ldexp(nearbyint(ldexp(v[i], n)), -n);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Step 4: expert FFN ([R] §1.3: gate, up, SiLU, down)                        */
 /* ------------------------------------------------------------------------- */
 
-int moe_ref_swiglu(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
-                   const uint8_t *dq, const float *ds, int32_t H, int32_t F,
-                   const float *x, double *y) {
+/* act_block > 0: the opt-in 8-bit activations, x and the SwiGLU output quantised per
+ * act_block values before their products. */
+static int ref_swiglu_q(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
+                        const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+                        const float *x, double *y, int32_t act_block) {
     if (!gq || !gs || !uq || !us || !dq || !ds || !x || !y) return REF_EINVAL;
-    if (H <= 0 || F <= 0 || H % 64 != 0 || F % 64 != 0) return REF_EINVAL;
+    if (H <= 0 || F <= 0 || H % 64 != 0 || F % 64 != 0 || act_block < 0) return REF_EINVAL;
     double *hbuf = (double *)malloc(sizeof(double) * (size_t)F);
-    if (!hbuf) return REF_EINVAL;
+    double *xin = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!hbuf || !xin) {
+        free(hbuf);
+        free(xin);
+        return REF_EINVAL;
+    }
+    for (int32_t h = 0; h < H; h++) xin[h] = (double)x[h];
+    if (act_block > 0) moe_ref_quant_act8(xin, H, act_block, xin);
 #pragma omp parallel for schedule(static)
     for (int32_t f = 0; f < F; f++) {
         double g = 0.0, u = 0.0;
         for (int32_t h = 0; h < H; h++) {
-            g += ref_weight(gq, gs, H, f, h) * (double)x[h];
-            u += ref_weight(uq, us, H, f, h) * (double)x[h];
+            g += ref_weight(gq, gs, H, f, h) * xin[h];
+            u += ref_weight(uq, us, H, f, h) * xin[h];
         }
         double silu = g / (1.0 + exp(-g)); /* SiLU(g) = g * sigmoid(g) */
         hbuf[f] = silu * u;
     }
+    if (act_block > 0) moe_ref_quant_act8(hbuf, F, act_block, hbuf);
 #pragma omp parallel for schedule(static)
     for (int32_t n = 0; n < H; n++) {
         double acc = 0.0;
@@ -360,8 +396,18 @@ int moe_ref_swiglu(const uint8_t *gq, const float *gs, const uint8_t *uq, const 
         y[n] = acc;
     }
     free(hbuf);
+    free(xin);
     return 0;
 }
+
+int moe_ref_swiglu(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
+                   const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+                   const float *x, double *y) {
+    return ref_swiglu_q(gq, gs, uq, us, dq, ds, H, F, x, y, 0);
+}
+
+/* the activation block of a layer: act_block values when the 8-bit path is on, else 0 */
+static int32_t ref_act_block(const moe_ref_layer *L) { return L->act_bits == 8 ? L->act_block : 0; }
 
 /* Expert e's tensors inside the stacked arrays. */
 static void ref_expert_ptrs(const moe_ref_layer *L, int32_t e, const uint8_t **gq,
@@ -387,8 +433,8 @@ int moe_ref_expert_ffn(const moe_ref_layer *L, const float *x, int32_t T,
             ref_expert_ptrs(L, e, &gq, &gs, &uq, &us, &dq, &ds);
             int32_t t = row_tok[r];
             if (t < 0 || t >= T) return REF_EINVAL;
-            int rc = moe_ref_swiglu(gq, gs, uq, us, dq, ds, H, L->ffn, x + (int64_t)t * H,
-                                    y_rows + (int64_t)r * H);
+            int rc = ref_swiglu_q(gq, gs, uq, us, dq, ds, H, L->ffn, x + (int64_t)t * H,
+                                  y_rows + (int64_t)r * H, ref_act_block(L));
             if (rc) return rc;
         }
     }
@@ -428,14 +474,14 @@ int moe_ref_layer_forward(const moe_ref_layer *L, const float *x, int32_t T,
             const uint8_t *gq, *uq, *dq;
             const float *gs, *us, *ds;
             ref_expert_ptrs(L, ids[j], &gq, &gs, &uq, &us, &dq, &ds);
-            rc = moe_ref_swiglu(gq, gs, uq, us, dq, ds, H, L->ffn, xt, y);
+            rc = ref_swiglu_q(gq, gs, uq, us, dq, ds, H, L->ffn, xt, y, ref_act_block(L));
             if (rc) break;
             for (int32_t h = 0; h < H; h++) ot[h] += (double)w[j] * y[h];
         }
         /* the shared expert: every token, weight 1, not scaled */
         if (rc == 0 && L->shared_ffn > 0) {
-            rc = moe_ref_swiglu(L->sh_gate_q, L->sh_gate_s, L->sh_up_q, L->sh_up_s,
-                                L->sh_down_q, L->sh_down_s, H, L->shared_ffn, xt, y);
+            rc = ref_swiglu_q(L->sh_gate_q, L->sh_gate_s, L->sh_up_q, L->sh_up_s,
+                              L->sh_down_q, L->sh_down_s, H, L->shared_ffn, xt, y, ref_act_block(L));
             if (rc) break;
             for (int32_t h = 0; h < H; h++) ot[h] += y[h];
         }

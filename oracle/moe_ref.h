@@ -50,6 +50,8 @@ typedef struct {
     const uint8_t *sh_down_q; const float *sh_down_s;  /* [H][Fs/2], [H][Fs/64] */
     int32_t n_group;      /* expert groups for group-limited routing; 0 or 1 = none */
     int32_t topk_group;   /* groups kept when n_group > 1 */
+    int32_t act_bits;     /* 8: the opt-in 8-bit activations (below); 0 = exact */
+    int32_t act_block;    /* values per activation block when act_bits == 8 */
 } moe_ref_layer;
 
 /* ---- int4 codec ([Q] §5.2) ------------------------------------------------ */
@@ -78,6 +80,13 @@ int moe_ref_route(const moe_ref_layer *L, const float *x, int32_t T,
 int moe_ref_union(int32_t E, int32_t k, const int32_t *ids, const int32_t *keff, int32_t T,
                   int32_t *n_uniq, int32_t *uniq, int32_t *off, int32_t *row_tok,
                   int32_t *pick_row);
+
+/* ---- opt-in 8-bit activations ([C] §2.2) --------------------------------- */
+/* Each block of `block` consecutive values of v[K] (the last one may be shorter) is
+ * replaced by c * 2^-n with n the largest integer (at most 149) for which
+ * max|v_block| * 2^n <= 127 and c = rint(v * 2^n) (round half to even), in [-127, 127];
+ * an all-zero block stays zero.  out may alias v. */
+void moe_ref_quant_act8(const double *v, int32_t K, int32_t block, double *out);
 
 /* ---- step 4: one expert's SwiGLU FFN on one token ([R] §1.3) ------------- */
 /* y[H] = Wd * (silu(Wg x) .* (Wu x)); Wg/Wu [F][H], Wd [H][F]. */

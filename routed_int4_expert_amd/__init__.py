@@ -48,7 +48,7 @@ class LayerC(ctypes.Structure):
         ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
         ("gate", Q4), ("up", Q4), ("down", Q4),
         ("sh_gate", Q4), ("sh_up", Q4), ("sh_down", Q4),
-        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+        ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("act_bits", ctypes.c_int32),
     ]
 
 
@@ -163,7 +163,8 @@ class Layer:
 
     def __init__(self, params: dict, tensors: dict):
         self.params = {k: params[k] for k in PARAMS}
-        self.params.update(n_group=int(params.get("n_group", 0)), topk_group=int(params.get("topk_group", 0)))
+        self.params.update(n_group=int(params.get("n_group", 0)), topk_group=int(params.get("topk_group", 0)),
+                           act_bits=int(params.get("act_bits", 0)))
         self.t = dict(tensors)
         c = LayerC()
         c.hidden, c.n_experts = int(params["hidden"]), int(params["n_experts"])
@@ -171,6 +172,7 @@ class Layer:
         c.top_p, c.norm_topk = float(params["top_p"]), int(params["norm_topk"])
         c.routed_scale = float(params["routed_scale"])
         c.n_group, c.topk_group = self.params["n_group"], self.params["topk_group"]
+        c.act_bits = self.params["act_bits"]
         g = self.t.get
         c.router_w = _ptr(g("router_w"))
         c.router_bias = _ptr(g("router_bias"))

@@ -210,7 +210,7 @@ __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
 }
 
 __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, int rowpitch, int K, int n8,
-                                             int i0, int nt) {
+                                             int i0, int nt, int act8) {
     uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
 #pragma unroll
     for (int b = 0; b < kStageBatch; b++) {
@@ -228,12 +228,14 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         mb = max(mb, dpp_u32<0x4E>(mb));
         const bool finite = mb < 0x7F800000u;
         const bool live = finite && mb != 0u;
-        const int n = live ? x16_shift(mb) : 0;
+        // 16-bit blocks, or the opt-in 8-bit codes (hi then 0, lo the code)
+        const int n = live ? (act8 ? x8_shift(mb) : x16_shift(mb)) : 0;
+        const float lim = act8 ? 127.0f : kX16Max;
         int x16[8], hi[8], lo[8];
         int ps = 0;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            x16[e] = live ? (int)fminf(fmaxf(rintf(ldexpf(xe[e], n)), -kX16Max), kX16Max) : 0;
+            x16[e] = live ? (int)fminf(fmaxf(rintf(ldexpf(xe[e], n)), -lim), lim) : 0;
             hi[e] = (x16[e] + 128) >> 8;
             lo[e] = x16[e] - (hi[e] << 8);
             ps += x16[e];
@@ -258,12 +260,13 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
 // The thread's batches from item `first` on (its number among the nt threads, for a
 // whole staging).
 __device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
-                                           const int32_t *rt, int rc, int R, int K, int first, int nt) {
+                                           const int32_t *rt, int rc, int R, int K, int first, int nt,
+                                           int act8) {
     const int n8 = R * (K / 8);
     for (int i0 = first; i0 < n8; i0 += kStageBatch * nt) {
         StageBatch sb;
         stage_issue(sb, xin, rt, rc, K, n8, i0, nt);
-        stage_commit(sb, xs, rowpitch, K, n8, i0, nt);
+        stage_commit(sb, xs, rowpitch, K, n8, i0, nt, act8);
     }
 }
 
@@ -297,7 +300,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
             select_union_one(a, lds, bx == 0 && unit == 0);
         else
             stage_rows(xs, (H / 32) * kChunkPitch, a.x, nullptr, 0, 1, H, (int)threadIdx.x - kWave,
-                       blockDim.x - kWave);
+                       blockDim.x - kWave, a.act8);
         __syncthreads();
         const int k = a.sel.k, E = a.sel.E;
         n_uniq_p = lds + 2 * k + 1;
@@ -412,8 +415,9 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         StageBatch sb0;
         stage_issue(sb0, xin, rt, 0, K, n80, tid, blockDim.x);
         load_step(0, q, sc);
-        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x);
-        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x);
+        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x, a.act8);
+        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x,
+                   a.act8);
         __syncthreads();
     }
 
@@ -421,7 +425,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         const int R = min(RM, nrows - rc);
         if (rc > 0) {
             __syncthreads();  // previous rows fully consumed
-            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x);
+            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x, a.act8);
             __syncthreads();
         }
 

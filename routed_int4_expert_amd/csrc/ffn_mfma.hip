@@ -70,6 +70,7 @@ struct PrepJob {
     uint8_t *frag;
     float *step;
     int blocks;  // workgroups of 256 threads this job takes
+    int act8;    // the opt-in 8-bit codes (hi bytes 0, lo bytes the code)
 };
 
 __device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
@@ -102,11 +103,12 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     for (int m = 1; m < 32; m <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, m, kWave));
     const bool finite = mb < 0x7F800000u;
     const bool nz = finite && mb != 0u;
-    const int sh = nz ? x16_shift(mb) : 0;
+    const int sh = nz ? (j.act8 ? x8_shift(mb) : x16_shift(mb)) : 0;
+    const float lim = j.act8 ? 127.0f : 32639.0f;
     int hi[8], lo[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) {
-        const int x16 = nz ? (int)rintf(ldexpf(e[s], sh)) : 0;
+        const int x16 = nz ? (int)fminf(fmaxf(rintf(ldexpf(e[s], sh)), -lim), lim) : 0;
         hi[s] = (x16 + 128) >> 8;
         lo[s] = x16 - 256 * hi[s];
     }
@@ -121,8 +123,9 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     if (in_rows && w == 0) j.step[(size_t)row * NC + c] = finite ? (nz ? ldexpf(1.0f, -sh) : 0.0f) : __builtin_nanf("");
 }
 
-static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step) {
+static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step, int act8 = 0) {
     PrepJob j;
+    j.act8 = act8;
     j.src = src;
     j.rows = rows;
     j.K = K;
@@ -331,7 +334,9 @@ struct ChunkRegs {
 // VALU instructions do not overlap; with two compute waves per SIMD one wave's VALU
 // work runs while the other's MFMAs execute.  The register budget of three waves per
 // SIMD leaves the loaders two chunks in flight.
-template <bool GU, int IRB>
+// A8: the opt-in 8-bit activations, whose hi bytes are zero: one MFMA per group (the lo
+// bytes) and no shift-add.
+template <bool GU, int IRB, bool A8>
 __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
     constexpr int kThreads = kMfmaThreads, NBL = kNBL;
     using Buf = MfmaBuf<IRB>;
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
                     const uint8_t *ar = tile + (16 * rb + j) * kRowPitch + gi * kGroupBytes + 16 * p;
-                    o.a[rb][0] = *reinterpret_cast<const i32x4_t *>(ar);
+                    if constexpr (!A8) o.a[rb][0] = *reinterpret_cast<const i32x4_t *>(ar);
                     o.a[rb][1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
                 }
 #pragma unroll
@@ -617,9 +622,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 i32x4_t gh[RB][NBL], gl[RB][NBL];
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
+                    if constexpr (!A8) {
 #pragma unroll
-                    for (int b = 0; b < NBL; b++)
-                        gh[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][0], cur.bo[b], zero, 0, 0, 0);
+                        for (int b = 0; b < NBL; b++)
+                            gh[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][0], cur.bo[b], zero, 0, 0, 0);
+                    }
 #pragma unroll
                     for (int b = 0; b < NBL; b++)
                         gl[rb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.a[rb][1], cur.bo[b], zero, 0, 0, 0);
@@ -633,8 +640,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                     for (int b = 0; b < NBL; b++)
 #pragma unroll
-                        for (int v = 0; v < 4; v++)
-                            csum[rb][b][v] = fmaf(sc4[b][gi], (float)(gh[rb][b][v] * 256 + gl[rb][b][v]), csum[rb][b][v]);
+                        for (int v = 0; v < 4; v++) {
+                            if constexpr (A8)
+                                csum[rb][b][v] = fmaf(sc4[b][gi], (float)gl[rb][b][v], csum[rb][b][v]);
+                            else
+                                csum[rb][b][v] = fmaf(sc4[b][gi], (float)(gh[rb][b][v] * 256 + gl[rb][b][v]), csum[rb][b][v]);
+                        }
                 if (gi + 1 < kCG) cur = nxt;
             }
             // the chunk's sums times the row steps (over 16: the codes entered as 16 q)
@@ -690,7 +701,7 @@ static int mfma_cus() {
     return cus;
 }
 
-template <bool GU, int IRB>
+template <bool GU, int IRB, bool A8>
 static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
     const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
     const int nb = (nmax + (GU ? 127 : 255)) / (GU ? 128 : 256);
@@ -700,19 +711,22 @@ static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char
     long G = mfma_cus();
     if ((total_max + G - 1) / G > kMaxWorkPerWg) G = (total_max + kMaxWorkPerWg - 1) / kMaxWorkPerWg;
     const size_t lds = 2 * (size_t)MfmaBuf<IRB>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB, A8>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipGetLastError();
     ProfScope prof(name, st);
-    q4_mfma_kernel<GU, IRB><<<(int)G, kMfmaThreads, lds, st>>>(a);
+    q4_mfma_kernel<GU, IRB, A8><<<(int)G, kMfmaThreads, lds, st>>>(a);
     return hipGetLastError();
 }
 
 // the work items' row count (16 or 32) selects the kernel
 template <bool GU>
 static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
-    return a.item_rows > 16 ? launch_gemm_rb<GU, 2>(a, shared_items, name, st)
-                            : launch_gemm_rb<GU, 1>(a, shared_items, name, st);
+    if (a.act8)
+        return a.item_rows > 16 ? launch_gemm_rb<GU, 2, true>(a, shared_items, name, st)
+                                : launch_gemm_rb<GU, 1, true>(a, shared_items, name, st);
+    return a.item_rows > 16 ? launch_gemm_rb<GU, 2, false>(a, shared_items, name, st)
+                            : launch_gemm_rb<GU, 1, false>(a, shared_items, name, st);
 }
 
 // x prepared once with the work list; gate/up for every item; the routed and shared
@@ -730,7 +744,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     it.n_items = a.n_items;
     it.with_union = a.union_in_prep;
     it.uni = a.uni;
-    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step), none, it, "prep_x+items", st);
+    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step, a.act8), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + a.item_rows - 1) / a.item_rows : 0;
     if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
@@ -739,8 +753,8 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     ItemsJob no_items = it;
     no_items.items = nullptr;
     no_items.with_union = 0;
-    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step) : none,
-                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step) : none,
+    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step, a.act8) : none,
+                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step, a.act8) : none,
                     no_items, "prep_h", st);
     if (e != hipSuccess) return e;
     return launch_gemm<false>(a, shared_items, "ffn_down_mfma", st);

@@ -33,6 +33,7 @@ static int check_dims(const moe_layer *L) {
     if (!(L->top_p >= 0.0f && L->top_p <= 1.0f)) return MOE_EINVAL;  // also rejects NaN
     if (!isfinite(L->routed_scale)) return MOE_EINVAL;
     if (L->n_experts > MOE_MAX_EXPERTS || L->top_k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
+    if (L->act_bits != 0 && L->act_bits != 16 && L->act_bits != 8) return MOE_EINVAL;
     if (L->n_group < 0) return MOE_EINVAL;
     if (L->n_group > 1) {
         if (L->n_group > 64 || L->n_experts % L->n_group || L->n_experts / L->n_group < 2) return MOE_EINVAL;
@@ -246,6 +247,7 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     MfmaArgs m;
     m.gu_out = f.gu_out;
     m.tab = f.tab;
+    m.act8 = f.act8;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
     m.x_step = at<float>(ws, p.x_step);
@@ -299,6 +301,7 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     FfnArgs a;
     a.gu_out = gu_out;
     a.tab = nullptr;
+    a.act8 = L.act_bits == 8 ? 1 : 0;
     a.x = x;
     a.n_uniq = n_uniq;
     a.uniq = uniq;

@@ -42,6 +42,21 @@ __device__ __forceinline__ int x16_shift(uint32_t mb) {
     return min(k + 127 - ef + bias, 149);
 }
 
+// The opt-in 8-bit activations: x8 = rint(x * 2^n) with n the largest integer for which
+// max|x| * 2^n <= 127 (at most 149), step 2^-n; with the hi/lo byte split of the 16-bit
+// form, hi is then 0 and lo the code.  mb: the bit pattern of max|x| (finite, nonzero).
+__device__ __forceinline__ int x8_shift(uint32_t mb) {
+    int bias = 0;
+    if (mb < 0x00800000u) {
+        mb = __float_as_uint(__uint_as_float(mb) * 18446744073709551616.0f);
+        bias = 64;
+    }
+    const int ef = (int)(mb >> 23);
+    // 1.f * 2^6 <= 127 iff the mantissa is at most 63 / 64 (8,257,536 / 2^23)
+    const int k = (mb & 0x7FFFFFu) <= 8257536u ? 6 : 5;
+    return min(k + 127 - ef + bias, 149);
+}
+
 // ---------------------------------------------------------------- router tiling
 // Router logits are a [T][E] x [E][H]^T product in fp64, tiled 64 tokens x 64
 // experts per workgroup with a split over H so small batches still cover the chip.
@@ -135,6 +150,7 @@ struct FfnArgs {
     // routed expert e's gate, up and down matrices: tab[3e], tab[3e+1], tab[3e+2] (the
     // residency tier's slots), or, when null, the stacked gate/up/down above
     const moe_q4 *tab;
+    int act8;  // opt-in 8-bit activation blocks (moe_layer::act_bits == 8)
     // Selection and union inside the gate/up launch (one token): every routed
     // workgroup selects and builds the union in LDS from the router logits; the
     // first routed workgroup also writes them out through sel (ids, w, keff) and uni
@@ -176,6 +192,7 @@ struct MfmaArgs {
     int item_rows;  // rows per work item: 16 or kMfmaItemRows
     int gu_out;     // as FfnArgs::gu_out
     const moe_q4 *tab;  // as FfnArgs::tab
+    int act8;           // as FfnArgs::act8
     int with_routed, with_shared;
     int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
     UnionArgs uni;

@@ -86,6 +86,8 @@ def call_forward(c, T=4, x=0x20000, out=0x30000, dtype=0, ws=0x40000, wsb=None):
     (dict(n_group=8, topk_group=1), M.MOE_EINVAL),   # 2 experts kept < top-4
     (dict(n_group=16, topk_group=8), M.MOE_EINVAL),  # single-expert groups
     (dict(n_group=-1), M.MOE_EINVAL),
+    (dict(act_bits=4), M.MOE_EINVAL),
+    (dict(act_bits=-8), M.MOE_EINVAL),
 ])
 def test_forward_validation_codes(kw, code):
     assert call_forward(_layer(**kw)) == code

@@ -244,6 +244,26 @@ def test_dense_mlp(H, F, T):
     say(f"dense H={H} F={F} T={T}: rel-L2 {rel:.2e} max-abs {mx:.2e}")
 
 
+ACT8 = [(1, 256, 128), (3, 320, 192), (24, 256, 128), (40, 512, 256), (300, 256, 128)]
+
+
+@pytest.mark.parametrize("T,H,F", ACT8, ids=[f"T{t}H{h}F{f}" for t, h, f in ACT8])
+def test_act8_opt_in_path(T, H, F):
+    """The opt-in 8-bit activations on the GEMV path (T <= 4: blocks of 32) and the
+    matrix-core path (blocks of 256, one int8 product per group) against the oracle of the
+    same quantisation: routing and union exact, expert rows and layer within the bar."""
+    sh = S.custom(f"act8_{T}", hidden=H, n_experts=24, ffn=F, shared_ffn=128, top_k=4, tokens=T,
+                  top_p=0.9, routed_scale=2.5, bias_amp=0.2)
+    d = S.make_layer(sh, seed=0)
+    d.update(act_bits=8, act_block=32 if T <= 4 else 256)
+    x = S.make_batch(sh, d, seed=0)
+    say(f"act8 T={T} H={H} F={F}")
+    full_parity(sh, d, x)
+    exact = R.layer_forward(R.Layer({**d, "act_bits": 0}), x)
+    q8 = R.layer_forward(R.Layer(d), x)
+    say(f"act8 T={T}: oracle 8-bit vs exact rel-L2 {np.linalg.norm(q8 - exact) / np.linalg.norm(exact):.2e}")
+
+
 def test_item_row_boundaries():
     """Experts routed exactly 66, 17, 16 and 33 rows and a 66-token shared expert.
 
@@ -515,6 +535,29 @@ def test_glm_prefill_workload(glm_bank):
     for t in range(sh.tokens):
         assert_close(got[t], ref[t], f"glm prefill token {t}")
     say(f"GLM prefill all tokens: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_glm_act8(glm_bank):
+    """The GLM-shaped layer with the opt-in 8-bit activations: one-token decode (GEMV path)
+    and the first 64 tokens of the prefill batch (matrix-core path), every token against the
+    oracle of the same quantisation."""
+    for name, T, block in (("glm_decode", 1, 32), ("glm_prefill", 64, 256)):
+        sh = S.SHAPES[name]
+        d = S.make_layer(sh, seed=0, bank=glm_bank)
+        d.update(act_bits=8, act_block=block)
+        x = np.ascontiguousarray(S.make_batch(sh, d, seed=0)[:T])
+        layer = M.Layer.from_host(d, DEV)
+        xd = torch.from_numpy(x).to(DEV)
+        check_routing(d, layer, x, xd, sh)
+        out = M.moe_layer_forward(layer, xd)
+        torch.cuda.synchronize()
+        ref = R.layer_forward(R.Layer(d), x)
+        rel, mx = assert_close(out.cpu().numpy(), ref, f"{name} act8")
+        exact = R.layer_forward(R.Layer({**d, "act_bits": 0}), x)
+        say(f"{name} act8 T={T}: rel-L2 {rel:.2e} against the 8-bit oracle, "
+            f"{np.linalg.norm(ref - exact) / np.linalg.norm(exact):.2e} 8-bit oracle against exact")
+        del layer
 
 
 @pytest.mark.timeout(1200)

@@ -430,6 +430,73 @@ def test_dense_mlp_is_plain_swiglu():
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-13)
 
 
+# --------------------------------------------------------------------------- opt-in 8-bit activations
+def test_quant_act8_worked_examples():
+    # largest |x| 1.0: step 2^-6 (64 <= 127 < 128); codes rint(64 x)
+    v = np.array([1.0, 0.5, -0.25, 0.3])
+    np.testing.assert_array_equal(R.quant_act8(v, 4), np.array([64, 32, -16, 19]) / 64.0)
+    # 127 itself: step 1; 127.5: step 2 (codes rint(x / 2), halves to even)
+    np.testing.assert_array_equal(R.quant_act8(np.array([127.0, 3.0, -2.5]), 3), [127.0, 3.0, -2.0])
+    np.testing.assert_array_equal(R.quant_act8(np.array([127.5, 3.0, 5.0]), 3), [128.0, 4.0, 4.0])
+    # halfway codes go to the even one: 0.5 / 64 -> 0, 1.5 / 64 -> 2 / 64 (block max 1)
+    np.testing.assert_array_equal(R.quant_act8(np.array([1.0, 0.5 / 64, 1.5 / 64]), 3),
+                                  [1.0, 0.0, 2 / 64])
+    # blocks restart; the last one may be short; an all-zero block stays zero
+    v = np.array([2.0, 1.0, 0.0, 0.0, 100.0, 0.75])
+    np.testing.assert_array_equal(R.quant_act8(v, 2), [2.0, 1.0, 0.0, 0.0, 100.0, 1.0])
+
+
+def test_quant_act8_bounds_and_exact_integers():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(1000) * np.exp(rng.uniform(-20, 20, 1000))
+    q = R.quant_act8(v, 32)
+    for b in range(0, 1000, 32):
+        blk, qb = v[b:b + 32], q[b:b + 32]
+        amax = np.abs(blk).max()
+        n = 6 - int(np.floor(np.log2(amax)))       # 2^(n-1) <= 64 / amax... refined below
+        while amax * 2.0 ** n > 127:
+            n -= 1
+        while amax * 2.0 ** (n + 1) <= 127:
+            n += 1
+        codes = qb * 2.0 ** n
+        assert np.all(codes == np.round(codes)) and np.abs(codes).max() <= 127
+        assert np.abs(codes).max() >= 63.5           # the largest maps into [64, 127]
+        assert np.all(np.abs(blk - qb) <= 2.0 ** -(n + 1))
+    ints = rng.integers(-127, 128, 256).astype(np.float64)
+    ints[7] = 127
+    np.testing.assert_array_equal(R.quant_act8(ints, 256), ints)   # step 1: unchanged
+
+
+def test_layer_act8_quantises_x_and_the_swiglu_output():
+    # the 8-bit layer equals a dense evaluation in which x (per block) and the SwiGLU
+    # output (per block) go through the pinned quantiser above
+    sh = S.custom("act8", n_experts=8, top_k=2, tokens=5, hidden=320, ffn=192, shared_ffn=128)
+    d = {**_layer(sh), "act_bits": 8, "act_block": 32}
+    x = S.make_batch(sh, d)
+    out = R.layer_forward(R.Layer(d), x)
+    ids, w, keff = R.route(R.Layer(d), x)
+
+    def ffn(gq, gs, uq, us, dq, ds_, xv):
+        xq = R.quant_act8(xv.astype(np.float64), 32)
+        g = R.dequantize_gs64(gq, gs) @ xq
+        u = R.dequantize_gs64(uq, us) @ xq
+        h = R.quant_act8(g * expit(g) * u, 32)
+        return R.dequantize_gs64(dq, ds_) @ h
+
+    for t in range(5):
+        ref = ffn(d["sh_gate_q"], d["sh_gate_s"], d["sh_up_q"], d["sh_up_s"], d["sh_down_q"],
+                  d["sh_down_s"], x[t])
+        for j in range(keff[t]):
+            e = ids[t, j]
+            ref = ref + float(w[t, j]) * ffn(d["gate_q"][e], d["gate_s"][e], d["up_q"][e], d["up_s"][e],
+                                             d["down_q"][e], d["down_s"][e], x[t])
+        np.testing.assert_allclose(out[t], ref, rtol=1e-9, atol=1e-12)
+    # and it differs from the exact layer by the int8 rounding, well above the 16-bit path's
+    exact = R.layer_forward(R.Layer({**d, "act_bits": 0}), x)
+    rel = np.linalg.norm(out - exact) / np.linalg.norm(exact)
+    assert 1e-4 < rel < 2e-2, rel
+
+
 # --------------------------------------------------------------------------- union
 def _union_bruteforce(E, ids, keff):
     T, k = ids.shape
