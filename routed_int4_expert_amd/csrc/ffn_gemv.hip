@@ -15,7 +15,7 @@
 // (and the word shifted right by 4) gives the even (odd) elements as four unsigned
 // bytes, three bit operations for eight codes.  Activations are staged per 32-element
 // chunk in 16-bit fixed point: x16 = rint(x * 2^n) with the power-of-two step 2^-n
-// that maps max|x| to at most 32639 (x16_shift), split into two signed bytes
+// that maps max|x| to at most 32639 (act_shift), split into two signed bytes
 // x16 = 256 hi + lo; v_dot4_i32_i8 accumulates u * hi and u * lo exactly in int32,
 // and per chunk
 //   sum(q x16) = 256 sum(u hi) + sum(u lo) - 8 sum(x16)
@@ -115,7 +115,8 @@ __device__ __forceinline__ void select_union_one(const FfnArgs &a, int32_t *lds,
     // SIMD with older workgroups' streaming waves, which the arbiter would favour:
     // the selecting wave runs at raised issue priority until the union is built.
     __builtin_amdgcn_s_setprio(3);
-    select_token(a.sel, 0, lane, ids_l, w_l, keff_l, nullptr, nullptr, &ps_sel);
+    // (one group: the host sends group-limited layers to the selection kernels)
+    select_token_impl<false>(a.sel, 0, lane, ids_l, w_l, keff_l, nullptr, nullptr, &ps_sel, nullptr);
     wave_lds_sync();
     const int keff = *keff_l;
     const int my = lane < keff ? ids_l[lane] : -1;
@@ -210,7 +211,7 @@ __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
 }
 
 __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, int rowpitch, int K, int n8,
-                                             int i0, int nt, int act8) {
+                                             int i0, int nt) {
     uint32_t *xw = reinterpret_cast<uint32_t *>(xs);
 #pragma unroll
     for (int b = 0; b < kStageBatch; b++) {
@@ -228,9 +229,9 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
         mb = max(mb, dpp_u32<0x4E>(mb));
         const bool finite = mb < 0x7F800000u;
         const bool live = finite && mb != 0u;
-        // 16-bit blocks, or the opt-in 8-bit codes (hi then 0, lo the code)
-        const int n = live ? (act8 ? x8_shift(mb) : x16_shift(mb)) : 0;
-        const float lim = act8 ? 127.0f : kX16Max;
+        constexpr ActRule rule = act_rule(0);
+        const int n = live ? act_shift(mb, rule) : 0;
+        constexpr float lim = rule.lim;
         int x16[8], hi[8], lo[8];
         int ps = 0;
 #pragma unroll
@@ -260,13 +261,12 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
 // The thread's batches from item `first` on (its number among the nt threads, for a
 // whole staging).
 __device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
-                                           const int32_t *rt, int rc, int R, int K, int first, int nt,
-                                           int act8) {
+                                           const int32_t *rt, int rc, int R, int K, int first, int nt) {
     const int n8 = R * (K / 8);
     for (int i0 = first; i0 < n8; i0 += kStageBatch * nt) {
         StageBatch sb;
         stage_issue(sb, xin, rt, rc, K, n8, i0, nt);
-        stage_commit(sb, xs, rowpitch, K, n8, i0, nt, act8);
+        stage_commit(sb, xs, rowpitch, K, n8, i0, nt);
     }
 }
 
@@ -300,7 +300,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
             select_union_one(a, lds, bx == 0 && unit == 0);
         else
             stage_rows(xs, (H / 32) * kChunkPitch, a.x, nullptr, 0, 1, H, (int)threadIdx.x - kWave,
-                       blockDim.x - kWave, a.act8);
+                       blockDim.x - kWave);
         __syncthreads();
         const int k = a.sel.k, E = a.sel.E;
         n_uniq_p = lds + 2 * k + 1;
@@ -415,9 +415,8 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         StageBatch sb0;
         stage_issue(sb0, xin, rt, 0, K, n80, tid, blockDim.x);
         load_step(0, q, sc);
-        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x, a.act8);
-        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x,
-                   a.act8);
+        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x);
+        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x);
         __syncthreads();
     }
 
@@ -425,7 +424,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         const int R = min(RM, nrows - rc);
         if (rc > 0) {
             __syncthreads();  // previous rows fully consumed
-            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x, a.act8);
+            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x);
             __syncthreads();
         }
 
@@ -627,15 +626,78 @@ static hipError_t dispatch(const FfnArgs &a, int N, int K, int rm, hipStream_t s
     return hipErrorInvalidValue;
 }
 
+// The opt-in 8-bit activations on this path: rows of K values replaced, per block of 32
+// (the staging chunk), by c * 2^-n with c = rint(x * 2^n) in [-127, 127] and n the 8-bit
+// rule's shift (act_shift).  The kernels above then stage such a block exactly: its
+// 16-bit shift is n + 8 (max|c| is in [64, 127]), so x16 = 256 c, hi = c and lo = 0, and the
+// integer products equal those of the 8-bit codes.  One thread per block; dst may alias src.
+__global__ __launch_bounds__(256) void quant_act8_kernel(const float *src, float *dst, int rows, int K) {
+    const int nb = K / 32;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= rows * nb) return;
+    const float4 *p = reinterpret_cast<const float4 *>(src + (size_t)(b / nb) * K + 32 * (b % nb));
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = p[i];
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        mb = max(mb, max(max(__float_as_uint(v[i].x) & 0x7FFFFFFFu, __float_as_uint(v[i].y) & 0x7FFFFFFFu),
+                         max(__float_as_uint(v[i].z) & 0x7FFFFFFFu, __float_as_uint(v[i].w) & 0x7FFFFFFFu)));
+    const bool finite = mb < 0x7F800000u;
+    const int n = (finite && mb) ? act_shift(mb, act_rule(1)) : 0;
+    auto q = [&](float x) __attribute__((always_inline)) {
+        if (!finite) return __int_as_float(0x7FC00000);  // a non-finite block stays non-finite
+        return ldexpf(fminf(fmaxf(rintf(ldexpf(x, n)), -127.0f), 127.0f), -n);
+    };
+    float4 *o = reinterpret_cast<float4 *>(dst + (size_t)(b / nb) * K + 32 * (b % nb));
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = make_float4(q(v[i].x), q(v[i].y), q(v[i].z), q(v[i].w));
+}
+
+static hipError_t launch_quant_act8(const float *src, float *dst, int rows, int K, hipStream_t st) {
+    const int n = rows * (K / 32);
+    if (n <= 0) return hipSuccess;
+    ProfScope prof("quant_act8", st);
+    quant_act8_kernel<<<(n + 255) / 256, 256, 0, st>>>(src, dst, rows, K);
+    return hipGetLastError();
+}
+
+static hipError_t launch_ffn_gemv_16(const FfnArgs &a, hipStream_t st);
+static hipError_t launch_ffn_gemv_16_gateup(const FfnArgs &a, hipStream_t st);
+static hipError_t launch_ffn_gemv_16_down(const FfnArgs &a, hipStream_t st);
+
+// The opt-in 8-bit path: x quantised into the workspace, the gate/up kernels, h
+// quantised in place, the down kernels.
+hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
+    if (!a.act8) return launch_ffn_gemv_16(a, st);
+    FfnArgs q = a;
+    hipError_t e = launch_quant_act8(a.x, a.xq, a.T, a.H, st);
+    q.x = a.xq;
+    if (e == hipSuccess) e = launch_ffn_gemv_16_gateup(q, st);
+    if (e == hipSuccess && a.with_routed) e = launch_quant_act8(a.h_routed, a.h_routed, a.rows_max, a.F, st);
+    if (e == hipSuccess && a.with_shared) e = launch_quant_act8(a.h_shared, a.h_shared, a.T, a.Fs, st);
+    if (e == hipSuccess) e = launch_ffn_gemv_16_down(q, st);
+    return e;
+}
+
 // Gate/up then down.  Routed and shared units share a launch when their
 // reduction lengths give the same lane split; otherwise each has its own.
-hipError_t launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
+static hipError_t launch_ffn_gemv_16(const FfnArgs &a, hipStream_t st) {
+    hipError_t e = launch_ffn_gemv_16_gateup(a, st);
+    if (e != hipSuccess) return e;
+    return launch_ffn_gemv_16_down(a, st);
+}
+
+static hipError_t launch_ffn_gemv_16_gateup(const FfnArgs &a, hipStream_t st) {
+    const int nmax = a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F;
+    return dispatch<true>(a, nmax, a.H, rows_per_pass(a.T, a.H), st);
+}
+
+static hipError_t launch_ffn_gemv_16_down(const FfnArgs &a, hipStream_t st) {
     hipError_t e;
     const bool same_down = !a.with_shared || !a.with_routed ||
                            lanes_per_row(a.F) == lanes_per_row(a.Fs);
-    const int nmax = a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F;
-    e = dispatch<true>(a, nmax, a.H, rows_per_pass(a.T, a.H), st);
-    if (e != hipSuccess) return e;
     if (same_down) {
         // one launch; the LDS is sized for the longer of the two reductions
         const int K = a.with_routed ? a.F : a.Fs;

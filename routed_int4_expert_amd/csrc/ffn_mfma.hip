@@ -12,7 +12,7 @@
 //    enter the matrix core exactly ("colibrì 深度拆解" §5.2 packing).
 //  - A (activations): prepared once per row and 256-element K chunk as 16-bit
 //    fixed point, x16 = rint(x * 2^n) with the power-of-two step 2^-n that maps
-//    max|x| to at most 32639 (x16_shift), split into signed bytes
+//    max|x| to at most 32639 (act_shift), split into signed bytes
 //    x16 = 256 hi + lo (the unsigned-offset and split identities of
 //    "colibri 开发演进实录" §2.2, K1, with the offset removed by the sign-carrying
 //    codes), in the codes' element order (per word: 0,2,4,6 then 1,3,5,7),
@@ -58,7 +58,7 @@ constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct L
 constexpr int kCodePitch = 144;
 
 // ------------------------------------------------------------------ prep
-// Rows of K fp32 values -> per 256-element chunk c: step[row][c] = 2^-x16_shift(max|x|)
+// Rows of K fp32 values -> per 256-element chunk c: step[row][c] = 2^-act_shift(max|x|)
 // (NaN if the chunk holds a non-finite value, 0 if it is all zero) and, per 64-group
 // G, 128 bytes: for word w (elements 64G + 8w .. +7) the hi bytes of its even
 // elements (0,2,4,6) and of its odd ones at 8w, the lo bytes likewise at 64 + 8w.
@@ -103,8 +103,9 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     for (int m = 1; m < 32; m <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, m, kWave));
     const bool finite = mb < 0x7F800000u;
     const bool nz = finite && mb != 0u;
-    const int sh = nz ? (j.act8 ? x8_shift(mb) : x16_shift(mb)) : 0;
-    const float lim = j.act8 ? 127.0f : 32639.0f;
+    const ActRule rule = act_rule(j.act8);
+    const int sh = nz ? act_shift(mb, rule) : 0;
+    const float lim = rule.lim;
     int hi[8], lo[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) {
@@ -335,8 +336,10 @@ struct ChunkRegs {
 // work runs while the other's MFMAs execute.  The register budget of three waves per
 // SIMD leaves the loaders two chunks in flight.
 // A8: the opt-in 8-bit activations, whose hi bytes are zero: one MFMA per group (the lo
-// bytes) and no shift-add.
-template <bool GU, int IRB, bool A8>
+// bytes) and no shift-add.  TAB: routed experts read through the residency tier's
+// pointer table (a separate instantiation: the table lookups would otherwise add
+// register pressure to the default kernel).
+template <bool GU, int IRB, bool A8, bool TAB>
 __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
     constexpr int kThreads = kMfmaThreads, NBL = kNBL;
     using Buf = MfmaBuf<IRB>;
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             if (GU) {
                 K = a.H;
                 N = e >= 0 ? a.F : a.Fs;
-                if (e >= 0 && a.tab) {  // the residency tier's slots
+                if (TAB && e >= 0) {  // the residency tier's slots
                     qb0 = a.tab[3 * e].q;     sb0 = a.tab[3 * e].s;
                     qb1 = a.tab[3 * e + 1].q; sb1 = a.tab[3 * e + 1].s;
                 } else if (e >= 0) {
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
                 if (e >= 0) {
-                    if (a.tab) {
+                    if constexpr (TAB) {
                         qb0 = a.tab[3 * e + 2].q; sb0 = a.tab[3 * e + 2].s;
                     } else {
                         const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
@@ -701,7 +704,7 @@ static int mfma_cus() {
     return cus;
 }
 
-template <bool GU, int IRB, bool A8>
+template <bool GU, int IRB, bool A8, bool TAB>
 static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
     const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
     const int nb = (nmax + (GU ? 127 : 255)) / (GU ? 128 : 256);
@@ -711,22 +714,27 @@ static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char
     long G = mfma_cus();
     if ((total_max + G - 1) / G > kMaxWorkPerWg) G = (total_max + kMaxWorkPerWg - 1) / kMaxWorkPerWg;
     const size_t lds = 2 * (size_t)MfmaBuf<IRB>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB, A8>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB, A8, TAB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipGetLastError();
     ProfScope prof(name, st);
-    q4_mfma_kernel<GU, IRB, A8><<<(int)G, kMfmaThreads, lds, st>>>(a);
+    q4_mfma_kernel<GU, IRB, A8, TAB><<<(int)G, kMfmaThreads, lds, st>>>(a);
     return hipGetLastError();
 }
 
 // the work items' row count (16 or 32) selects the kernel
 template <bool GU>
 static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
-    if (a.act8)
-        return a.item_rows > 16 ? launch_gemm_rb<GU, 2, true>(a, shared_items, name, st)
-                                : launch_gemm_rb<GU, 1, true>(a, shared_items, name, st);
-    return a.item_rows > 16 ? launch_gemm_rb<GU, 2, false>(a, shared_items, name, st)
-                            : launch_gemm_rb<GU, 1, false>(a, shared_items, name, st);
+#define MOE_GEMM_CASE(A8, TAB)                                                                  \
+    if (!!a.act8 == A8 && (a.tab != nullptr) == TAB)                                            \
+        return a.item_rows > 16 ? launch_gemm_rb<GU, 2, A8, TAB>(a, shared_items, name, st)     \
+                                : launch_gemm_rb<GU, 1, A8, TAB>(a, shared_items, name, st);
+    MOE_GEMM_CASE(false, false)
+    MOE_GEMM_CASE(true, false)
+    MOE_GEMM_CASE(false, true)
+    MOE_GEMM_CASE(true, true)
+#undef MOE_GEMM_CASE
+    return hipErrorInvalidValue;
 }
 
 // x prepared once with the work list; gate/up for every item; the routed and shared

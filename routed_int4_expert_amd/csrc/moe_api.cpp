@@ -150,6 +150,7 @@ Plan make_plan(const moe_layer &L, int T) {
     p.h_shared = take(Tz * Fs * 4);
     p.y_routed = take(Tz * k * H * 4);
     p.y_shared = take(Tz * H * 4);
+    if (L.act_bits == 8 && Tz <= (size_t)kGemvMaxTokens) p.xq = take(Tz * H * 4);
     if (Tz > (size_t)kGemvMaxTokens) {
         // fragment rows padded to whole 4-group chunks
         const size_t gh = mfma_groups_padded((int)H), gf = mfma_groups_padded((int)F),
@@ -302,6 +303,8 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     a.gu_out = gu_out;
     a.tab = nullptr;
     a.act8 = L.act_bits == 8 ? 1 : 0;
+    a.xq = p.xq ? at<float>(ws, p.xq) : nullptr;
+    a.rows_max = T * L.top_k;
     a.x = x;
     a.n_uniq = n_uniq;
     a.uniq = uniq;
@@ -401,8 +404,9 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
 
     hipError_t e;
     // one token: selection and union run inside the gate/up launch (not with a residency
-    // tier, which resolves the union before the expert FFNs start)
-    const bool sel_in_ffn = T == 1 && !tier;
+    // tier, which resolves the union before the expert FFNs start, nor with group-limited
+    // routing, which the in-launch selection leaves to the selection kernels)
+    const bool sel_in_ffn = T == 1 && !tier && L->n_group <= 1;
     float *y_routed = at<float>(ws, p.y_routed);
     FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
     if (sel_in_ffn) {

@@ -22,38 +22,35 @@ __device__ __forceinline__ float gate_up_out(int mode, float g, float u) {
     return mode == kGuSwiglu ? g / (1.0f + expf(-g)) * u : (mode == kGuGate ? g : u);
 }
 
-// ---------------------------------------------------------------- 16-bit activations
-// Both expert-FFN paths take activations as 16-bit fixed point per block: x16 =
-// rint(x * 2^n) with n the largest integer for which max|x| * 2^n <= 32639 = 127 * 256
-// + 127 (so hi = (x16 + 128) >> 8 and lo = x16 - 256 hi are signed bytes), and step
-// 2^-n.  A power-of-two step scales exactly: values with at most 15 significant bits
-// relative to the block's largest are represented exactly.  mb: the bit pattern of
-// max|x| (finite, nonzero).  Subnormal maxima are first scaled by 2^64 (exactly); n is
-// at most 149, so the step 2^-n stays representable.
-__device__ __forceinline__ int x16_shift(uint32_t mb) {
-    int bias = 0;
-    if (mb < 0x00800000u) {
-        mb = __float_as_uint(__uint_as_float(mb) * 18446744073709551616.0f);
-        bias = 64;
-    }
-    const int ef = (int)(mb >> 23);
-    // 1.f * 2^14 <= 32639 iff the mantissa is at most 16255 / 16384 (8,322,560 / 2^23)
-    const int k = (mb & 0x7FFFFFu) <= 8322560u ? 14 : 13;
-    return min(k + 127 - ef + bias, 149);
+// ---------------------------------------------------------------- activation blocks
+// Both expert-FFN paths take activations as fixed point per block: x16 = rint(x * 2^n)
+// with n the largest integer for which max|x| * 2^n <= 32639 = 127 * 256 + 127 (so
+// hi = (x16 + 128) >> 8 and lo = x16 - 256 hi are signed bytes), and step 2^-n; or, on
+// the opt-in 8-bit path, the same with 127 as the limit (hi is then 0 and lo the code).
+// A power-of-two step scales exactly: values with at most 15 (7) significant bits
+// relative to the block's largest are represented exactly.  Subnormal maxima are first
+// scaled by 2^64 (exactly); n is at most 149, so the step 2^-n stays representable.
+// The activation rule as wave-uniform constants: the largest mantissa (bits) for which
+// the larger shift applies, that shift, and the code limit (16-bit: 8,322,560, 14, 32639;
+// 8-bit: 8,257,536, 6, 127), so one staging path serves both with no per-element select.
+struct ActRule {
+    uint32_t thr;
+    int khi;
+    float lim;
+};
+__host__ __device__ constexpr ActRule act_rule(int act8) {
+    return ActRule{act8 ? 8257536u : 8322560u, act8 ? 6 : 14, act8 ? 127.0f : 32639.0f};
 }
-
-// The opt-in 8-bit activations: x8 = rint(x * 2^n) with n the largest integer for which
-// max|x| * 2^n <= 127 (at most 149), step 2^-n; with the hi/lo byte split of the 16-bit
-// form, hi is then 0 and lo the code.  mb: the bit pattern of max|x| (finite, nonzero).
-__device__ __forceinline__ int x8_shift(uint32_t mb) {
+// n for the bit pattern mb of max|x| (finite, nonzero): 1.f * 2^khi <= limit iff the
+// mantissa bits are at most thr
+__device__ __forceinline__ int act_shift(uint32_t mb, const ActRule &r) {
     int bias = 0;
     if (mb < 0x00800000u) {
         mb = __float_as_uint(__uint_as_float(mb) * 18446744073709551616.0f);
         bias = 64;
     }
     const int ef = (int)(mb >> 23);
-    // 1.f * 2^6 <= 127 iff the mantissa is at most 63 / 64 (8,257,536 / 2^23)
-    const int k = (mb & 0x7FFFFFu) <= 8257536u ? 6 : 5;
+    const int k = (mb & 0x7FFFFFu) <= r.thr ? r.khi : r.khi - 1;
     return min(k + 127 - ef + bias, 149);
 }
 
@@ -83,6 +80,7 @@ struct Plan {
     size_t h_shared;  // fp32 [T][Fs]
     size_t y_routed;  // fp32 [T*k][H]  unweighted expert outputs per routed row
     size_t y_shared;  // fp32 [T][H]
+    size_t xq;        // fp32 [T][H] x in 8-bit blocks (opt-in 8-bit path, T <= kGemvMaxTokens), or 0
     size_t x_frag, x_step, hr_frag, hr_step, hs_frag, hs_step;  // matrix-core path (T > kGemvMaxTokens)
     size_t items, n_items;  // matrix-core work list
     int max_items;
@@ -151,6 +149,8 @@ struct FfnArgs {
     // residency tier's slots), or, when null, the stacked gate/up/down above
     const moe_q4 *tab;
     int act8;  // opt-in 8-bit activation blocks (moe_layer::act_bits == 8)
+    float *xq;     // T <= kGemvMaxTokens with act8: x in 8-bit blocks (workspace [T][H])
+    int rows_max;  // routed rows the batch can have (T * k)
     // Selection and union inside the gate/up launch (one token): every routed
     // workgroup selects and builds the union in LDS from the router logits; the
     // first routed workgroup also writes them out through sel (ids, w, keff) and uni

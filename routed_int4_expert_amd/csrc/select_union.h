@@ -126,10 +126,13 @@ __device__ __forceinline__ double sum_partials(const SelectArgs &a, int t, int e
 
 // lg: this token's E logits already summed (in LDS), or null to sum them here; both
 // unused when the router gave the gates and keys.
-__device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
-                                             float *w, int32_t *keff_out, int32_t *ids_copy,
-                                             int32_t *keff_copy, PickScratch *ps,
-                                             const double *lg = nullptr) {
+// GROUPED: group-limited routing (a.n_group > 1), a separate instantiation so that the
+// one-group selection on the decode critical path carries none of its code.
+template <bool GROUPED>
+__device__ __forceinline__ void select_token_impl(const SelectArgs &a, int t, int lane, int32_t *ids,
+                                                  float *w, int32_t *keff_out, int32_t *ids_copy,
+                                                  int32_t *keff_copy, PickScratch *ps,
+                                                  const double *lg) {
     constexpr int EPL = MOE_MAX_EXPERTS / kWave;  // experts per lane (4)
     double sig[EPL];
     unsigned long long key[EPL];
@@ -152,7 +155,7 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
     // group g = experts [g*gs, (g+1)*gs); its score is the sum of its two largest choices;
     // the topk_group best groups (equal scores: lower id) stay, the other experts' keys
     // become 0, below every live key, so they are never picked.
-    if (a.n_group > 1) {
+    if constexpr (GROUPED) {
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
             const int e = lane + kWave * i;
@@ -193,11 +196,14 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
     // (no key equal to the k-th is left out), which ends the search early.  Bits above
     // the highest one in which the live keys differ are the same in all of them, so
     // thr starts with them and the search starts below (there are at least k live keys).
-    // live keys: experts below E (and in a kept group); every live key is nonzero
+    // live keys: experts below E (and, grouped, in a kept group); every live key is nonzero
+    auto live = [&](int i) __attribute__((always_inline)) {
+        return GROUPED ? key[i] != 0ull : (lane + kWave * i) < a.E;
+    };
     unsigned long long kand = ~0ull, kor = 0ull;
 #pragma unroll
     for (int i = 0; i < EPL; i++)
-        if (key[i] != 0ull) {
+        if (live(i)) {
             kand &= key[i];
             kor |= key[i];
         }
@@ -234,7 +240,7 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         int eq_before = 0;
 #pragma unroll
         for (int i = 0; i < EPL; i++) {
-            const unsigned long long eqm = __ballot(key[i] == thr && key[i] != 0ull);
+            const unsigned long long eqm = __ballot(key[i] == thr && live(i));
             const int r = eq_before + __popcll(eqm & below);
             sel[i] = key[i] > thr || (((eqm >> lane) & 1ull) && r < need);
             eq_before += __popcll(eqm);
@@ -350,6 +356,16 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lan
         *keff_out = keff;
         if (keff_copy) *keff_copy = keff;
     }
+}
+
+__device__ __forceinline__ void select_token(const SelectArgs &a, int t, int lane, int32_t *ids,
+                                             float *w, int32_t *keff_out, int32_t *ids_copy,
+                                             int32_t *keff_copy, PickScratch *ps,
+                                             const double *lg = nullptr) {
+    if (a.n_group > 1)
+        select_token_impl<true>(a, t, lane, ids, w, keff_out, ids_copy, keff_copy, ps, lg);
+    else
+        select_token_impl<false>(a, t, lane, ids, w, keff_out, ids_copy, keff_copy, ps, lg);
 }
 
 // LDS words union_block needs for E experts and T tokens.
