@@ -50,10 +50,16 @@ WORKLOADS = {
                    "Zipf(1.1) bias, RMSNorm + residual between layers, fp32",
     "glm_rows256": "grouped-GEMM microbenchmark: 16 GLM-shaped experts + shared, 512 tokens top-8 "
                    "(~256 rows per expert), fp32 out",
+    "glm_prefill_act8": "glm_prefill with the opt-in 8-bit activations (int8 codes per 256-value "
+                        "block, one int8 product per group)",
+    "glm_verify16": "the GLM-shaped decode layer on 16 tokens per step (a multi-token verification "
+                    "or small prefill chunk: 1-2 rows per union expert), fp32 out",
 }
-DEFAULT_ORDER = ("glm_decode", "small_decode", "glm_prefill", "glm_stack16", "glm_rows256")
+DEFAULT_ORDER = ("glm_decode", "small_decode", "glm_verify16", "glm_prefill", "glm_prefill_act8",
+                 "glm_stack16", "glm_rows256")
 # resident layer copies cycled per step (enough distinct HBM to defeat the last-level cache)
-COPIES = {"glm_decode": 8, "small_decode": 8, "glm_prefill": 2, "glm_stack16": 16, "glm_rows256": 2}
+COPIES = {"glm_decode": 8, "small_decode": 8, "glm_prefill": 2, "glm_stack16": 16, "glm_rows256": 2,
+          "glm_prefill_act8": 2, "glm_verify16": 8}
 
 
 def log(msg):
@@ -92,7 +98,7 @@ def bank_for(sh):
     return _BANKS[key]
 
 
-def build_layers(sh, n_layers, dev, shared_router=False):
+def build_layers(sh, n_layers, dev, shared_router=False, act_bits=0):
     """n_layers resident copies of the layer: distinct HBM, experts permuted per copy.
     With shared_router every copy uses copy 0's router (the prefill tokens are built
     for that router)."""
@@ -110,7 +116,7 @@ def build_layers(sh, n_layers, dev, shared_router=False):
         ts.update({k: base[k].clone() for k in S.Bank.SHARED})
         ts["router_w"] = torch.from_numpy(rw).to(dev)
         ts["router_bias"] = torch.from_numpy(rb).to(dev)
-        layers.append(M.Layer(S.layer_params(sh), ts))
+        layers.append(M.Layer({**S.layer_params(sh), "act_bits": act_bits}, ts))
         routers.append((rw, rb))
     del base
     torch.cuda.synchronize()
@@ -223,12 +229,19 @@ def run_workload(wl, args, dev):
     import routed_int4_expert_amd as M
     from routed_int4_expert_amd import synth as S
 
-    sh = S.SHAPES[wl]
+    import dataclasses
+    act_bits = 8 if wl.endswith("_act8") else 0
+    base_wl = wl[:-len("_act8")] if act_bits else wl
+    if base_wl == "glm_verify16":
+        sh = dataclasses.replace(S.SHAPES["glm_decode"], tokens=16)
+    else:
+        sh = S.SHAPES[base_wl]
     T, H, F, Fs, E = sh.tokens, sh.hidden, sh.ffn, sh.shared_ffn, sh.n_experts
     stack = wl == "glm_stack16"
     nlay = COPIES[wl] if args.layers is None else (sh.layers if stack else args.layers)
-    bank, layers, routers = build_layers(sh, nlay, dev, shared_router=(wl == "glm_prefill"))
-    if wl == "glm_prefill":
+    bank, layers, routers = build_layers(sh, nlay, dev, shared_router=(base_wl == "glm_prefill"),
+                                         act_bits=act_bits)
+    if base_wl == "glm_prefill":
         npool = 2
         xs_host = np.concatenate([S.gumbel_skew_batch(sh, T, routers[0][0], routers[0][1], 0, p)[0]
                                   for p in range(npool)])
@@ -410,9 +423,10 @@ def run_workload(wl, args, dev):
         "scaling": "weak",
         "vs_baseline": None,
         # the expert FFNs' arithmetic: int4 codes times 16-bit fixed-point activations
-        # (carried as two int8 limbs) with exact int32 group sums (v_dot4 in the decode
-        # GEMV for T <= 4, int8 matrix cores for T > 4), then fp32 accumulation
-        "dtype": "i4xfx16-i32-f32acc",
+        # (carried as two int8 limbs; one int8 code with the opt-in 8-bit path) with exact
+        # int32 group sums (v_dot4 in the decode GEMV for T <= 4, int8 matrix cores for
+        # T > 4), then fp32 accumulation
+        "dtype": "i4xi8-i32-f32acc" if act_bits else "i4xfx16-i32-f32acc",
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: {WORKLOADS[wl]}",
