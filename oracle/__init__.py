@@ -41,7 +41,12 @@ class RefLayer(ctypes.Structure):
         ("sh_down_q", ctypes.c_void_p), ("sh_down_s", ctypes.c_void_p),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
         ("act_bits", ctypes.c_int32), ("act_block", ctypes.c_int32),
+        ("fmt", ctypes.c_int32),
     ]
+
+
+# expert weight formats (moe_ref.h)
+FMT_INT4, FMT_MXFP4, FMT_INT3 = 0, 1, 2
 
 
 def _load():
@@ -68,6 +73,13 @@ def _load():
         "moe_ref_rmsnorm": (ctypes.c_int, [vp, i32, i32, ctypes.c_double, vp]),
         "moe_ref_dense_mlp": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp]),
         "moe_ref_quant_act8": (None, [vp, i32, i32, vp]),
+        "moe_ref_e2m1": (ctypes.c_double, [ctypes.c_uint8]),
+        "moe_ref_ue8m0": (ctypes.c_double, [ctypes.c_uint8]),
+        "moe_ref_int3_code": (i32, [vp, i64, i64]),
+        "moe_ref_code_bytes": (i64, [i32, i64]),
+        "moe_ref_scale_bytes": (i64, [i32, i64]),
+        "moe_ref_dequantize": (ctypes.c_int, [i32, vp, vp, i64, i64, vp]),
+        "moe_ref_swiglu_fmt": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -106,12 +118,14 @@ class Layer:
         self.routed_scale = float(d["routed_scale"])
         self.n_group, self.topk_group = int(d.get("n_group", 0)), int(d.get("topk_group", 0))
         self.act_bits, self.act_block = int(d.get("act_bits", 0)), int(d.get("act_block", 0))
+        self.fmt = int(d.get("expert_fmt", FMT_INT4))
         s = RefLayer()
         s.hidden, s.n_experts, s.ffn = self.hidden, self.n_experts, self.ffn
         s.shared_ffn, s.top_k, s.top_p = self.shared_ffn, self.top_k, self.top_p
         s.norm_topk, s.routed_scale = self.norm_topk, self.routed_scale
         s.n_group, s.topk_group = self.n_group, self.topk_group
         s.act_bits, s.act_block = self.act_bits, self.act_block
+        s.fmt = self.fmt
         for k in self.FIELDS:
             setattr(s, k, _p(self.d[k]) if self.d[k] is not None and self.d[k].size else None)
         self.struct = s
@@ -146,6 +160,47 @@ def dequantize_gs64(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     w = np.empty((N, K), np.float64)
     _check(_load().moe_ref_dequantize_gs64(_p(q), _p(s), N, K, _p(w)), "dequantize")
     return w
+
+
+def e2m1(code: int) -> float:
+    return float(_load().moe_ref_e2m1(code))
+
+
+def ue8m0(e: int) -> float:
+    return float(_load().moe_ref_ue8m0(e))
+
+
+def int3_code(row_q: np.ndarray, K: int, k: int) -> int:
+    row_q = np.ascontiguousarray(row_q, dtype=np.uint8)
+    assert row_q.size == 3 * K // 8
+    return int(_load().moe_ref_int3_code(_p(row_q), K, k))
+
+
+def code_bytes(fmt: int, K: int) -> int:
+    return int(_load().moe_ref_code_bytes(fmt, K))
+
+
+def scale_bytes(fmt: int, K: int) -> int:
+    return int(_load().moe_ref_scale_bytes(fmt, K))
+
+
+def dequantize(fmt: int, q: np.ndarray, s: np.ndarray, K: int) -> np.ndarray:
+    """W[N][K] (fp64) of a matrix in any expert format (q [N][code bytes], s [N][...])."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s)
+    N = q.shape[0]
+    assert q.shape[1] == code_bytes(fmt, K) and s.nbytes == N * scale_bytes(fmt, K)
+    w = np.empty((N, K), np.float64)
+    _check(_load().moe_ref_dequantize(fmt, _p(q), _p(s), N, K, _p(w)), "dequantize")
+    return w
+
+
+def swiglu_fmt(fmt: int, gq, gs, uq, us, dq, ds, H: int, F: int, x: np.ndarray) -> np.ndarray:
+    arrs = [np.ascontiguousarray(a) for a in (gq, gs, uq, us, dq, ds)]
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty((H,), np.float64)
+    _check(_load().moe_ref_swiglu_fmt(fmt, *[_p(a) for a in arrs], H, F, _p(x), _p(y)), "swiglu_fmt")
+    return y
 
 
 def logits(L: Layer, x: np.ndarray) -> np.ndarray:

@@ -10,7 +10,8 @@
  * Citations:
  *   [R] "MoE 路由与专家流式加载" (colibri-analysis 07), §1.1-§1.4
  *   [Q] "colibrì 深度拆解：1300行纯C代码驱动7440亿参数大模型", §5.2
- *   [C] "colibri 开发演进实录：从 CHANGELOG 看多引擎 MoE 推理框架的工程迭代脉络", §2.1, §2.2
+ *   [C] "colibri 开发演进实录：从 CHANGELOG 看多引擎 MoE 推理框架的工程迭代脉络", §2.1, §2.2,
+ *       §五 and §六 (fp4 / MXFP4 experts), §8.3 (int3-g64)
  */
 #include "moe_ref.h"
 
@@ -95,6 +96,77 @@ int moe_ref_dequantize_gs64(const uint8_t *q, const float *s, int64_t N, int64_t
 }
 
 /* ------------------------------------------------------------------------- */
+/* The other expert formats (moe_ref.h)                                        */
+/* ------------------------------------------------------------------------- */
+
+/* [C] §五/§六 name fp4 experts with UE8M0 block scales and MXFP4 experts; the reading
+ * is the OCP Microscaling FP4 element: sign, a two-bit exponent with bias 1 and one
+ * mantissa bit.  Exponent 0 is subnormal: 0 or one half. */
+double moe_ref_e2m1(uint8_t code) {
+    const int sgn = (code >> 3) & 1;
+    const int ex = (code >> 1) & 3;
+    const int man = code & 1;
+    double mag;
+    if (ex == 0)
+        mag = 0.5 * man;
+    else
+        mag = ldexp(1.0 + 0.5 * man, ex - 1);
+    return sgn ? -mag : mag;
+}
+
+/* UE8M0: an unsigned biased exponent and nothing else; the all-ones byte is NaN. */
+double moe_ref_ue8m0(uint8_t e) {
+    if (e == 255) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* [C] §8.3 (fmt=5): 3-bit codes, one scale per 64.  Bit planes as moe_ref.h states. */
+int32_t moe_ref_int3_code(const uint8_t *row_q, int64_t K, int64_t k) {
+    const int64_t G = k / 64;
+    const int i = (int)(k % 64);
+    /* i = 16d + 8a + 2b + o for the low-bit plane */
+    const int d = i / 16, a = (i / 8) % 2, b = (i / 2) % 4, o = i % 2;
+    const int low = (row_q[16 * G + 4 * d + b] >> (2 * (2 * a + o))) & 3;
+    /* i = 32h + 8m + 2b + o for the sign plane */
+    const int h = i / 32, m = (i / 8) % 4;
+    const int sign = (row_q[K / 4 + 8 * G + 4 * h + b] >> (2 * m + o)) & 1;
+    return low - 4 * sign;
+}
+
+int64_t moe_ref_code_bytes(int32_t fmt, int64_t K) { return fmt == MOE_REF_FMT_INT3 ? 3 * K / 8 : K / 2; }
+
+int64_t moe_ref_scale_bytes(int32_t fmt, int64_t K) {
+    return fmt == MOE_REF_FMT_MXFP4 ? K / 32 : 4 * (K / 64);
+}
+
+/* W[n][k] of a matrix in format fmt, fp64.  Every product here is exact in fp64: a
+ * code of at most 4 bits times an fp32 scale or a power of two. */
+static double ref_weight_fmt(int32_t fmt, const uint8_t *q, const void *s, int64_t K, int64_t n,
+                             int64_t k) {
+    const uint8_t *row_q = q + n * moe_ref_code_bytes(fmt, K);
+    if (fmt == MOE_REF_FMT_MXFP4) {
+        const uint8_t *row_e = (const uint8_t *)s + n * (K / 32);
+        const uint8_t byte = row_q[k / 2];
+        const uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+        return moe_ref_e2m1(code) * moe_ref_ue8m0(row_e[k / 32]);
+    }
+    const float *row_s = (const float *)s + n * (K / 64);
+    const int32_t c = fmt == MOE_REF_FMT_INT3 ? moe_ref_int3_code(row_q, K, k) : ref_code(row_q, k);
+    return (double)c * (double)row_s[k / 64];
+}
+
+static int ref_fmt_ok(int32_t fmt) {
+    return fmt == MOE_REF_FMT_INT4 || fmt == MOE_REF_FMT_MXFP4 || fmt == MOE_REF_FMT_INT3;
+}
+
+int moe_ref_dequantize(int32_t fmt, const uint8_t *q, const void *s, int64_t N, int64_t K, double *w) {
+    if (!ref_fmt_ok(fmt) || !q || !s || !w || N < 0 || K <= 0 || K % 64 != 0) return REF_EINVAL;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) w[n * K + k] = ref_weight_fmt(fmt, q, s, K, n, k);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Steps 1-2: router logits and noaux_tc selection ([R] §1.1, §1.2)            */
 /* ------------------------------------------------------------------------- */
 
@@ -108,6 +180,7 @@ static int ref_layer_ok(const moe_ref_layer *L) {
     if (L->n_group < 0) return 0;
     if (L->act_bits != 0 && L->act_bits != 16 && L->act_bits != 8) return 0;
     if (L->act_bits == 8 && L->act_block <= 0) return 0;
+    if (!ref_fmt_ok(L->fmt)) return 0;
     if (L->n_group > 256) return 0;
     if (L->n_group > 1) { /* equal groups of at least two experts, enough experts kept */
         if (L->n_experts % L->n_group != 0 || L->n_experts / L->n_group < 2) return 0;
@@ -364,10 +437,11 @@ void moe_ref_quant_act8(const double *v, int32_t K, int32_t block, double *out) 
 
 /* act_block > 0: the opt-in 8-bit activations, x and the SwiGLU output quantised per
  * act_block values before their products. */
-static int ref_swiglu_q(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
-                        const uint8_t *dq, const float *ds, int32_t H, int32_t F,
+static int ref_swiglu_q(int32_t fmt, const uint8_t *gq, const void *gs, const uint8_t *uq,
+                        const void *us, const uint8_t *dq, const void *ds, int32_t H, int32_t F,
                         const float *x, double *y, int32_t act_block) {
     if (!gq || !gs || !uq || !us || !dq || !ds || !x || !y) return REF_EINVAL;
+    if (!ref_fmt_ok(fmt)) return REF_EINVAL;
     if (H <= 0 || F <= 0 || H % 64 != 0 || F % 64 != 0 || act_block < 0) return REF_EINVAL;
     double *hbuf = (double *)malloc(sizeof(double) * (size_t)F);
     double *xin = (double *)malloc(sizeof(double) * (size_t)H);
@@ -382,8 +456,8 @@ static int ref_swiglu_q(const uint8_t *gq, const float *gs, const uint8_t *uq, c
     for (int32_t f = 0; f < F; f++) {
         double g = 0.0, u = 0.0;
         for (int32_t h = 0; h < H; h++) {
-            g += ref_weight(gq, gs, H, f, h) * xin[h];
-            u += ref_weight(uq, us, H, f, h) * xin[h];
+            g += ref_weight_fmt(fmt, gq, gs, H, f, h) * xin[h];
+            u += ref_weight_fmt(fmt, uq, us, H, f, h) * xin[h];
         }
         double silu = g / (1.0 + exp(-g)); /* SiLU(g) = g * sigmoid(g) */
         hbuf[f] = silu * u;
@@ -392,7 +466,7 @@ static int ref_swiglu_q(const uint8_t *gq, const float *gs, const uint8_t *uq, c
 #pragma omp parallel for schedule(static)
     for (int32_t n = 0; n < H; n++) {
         double acc = 0.0;
-        for (int32_t f = 0; f < F; f++) acc += ref_weight(dq, ds, F, n, f) * hbuf[f];
+        for (int32_t f = 0; f < F; f++) acc += ref_weight_fmt(fmt, dq, ds, F, n, f) * hbuf[f];
         y[n] = acc;
     }
     free(hbuf);
@@ -403,7 +477,13 @@ static int ref_swiglu_q(const uint8_t *gq, const float *gs, const uint8_t *uq, c
 int moe_ref_swiglu(const uint8_t *gq, const float *gs, const uint8_t *uq, const float *us,
                    const uint8_t *dq, const float *ds, int32_t H, int32_t F,
                    const float *x, double *y) {
-    return ref_swiglu_q(gq, gs, uq, us, dq, ds, H, F, x, y, 0);
+    return ref_swiglu_q(MOE_REF_FMT_INT4, gq, gs, uq, us, dq, ds, H, F, x, y, 0);
+}
+
+int moe_ref_swiglu_fmt(int32_t fmt, const uint8_t *gq, const void *gs, const uint8_t *uq,
+                       const void *us, const uint8_t *dq, const void *ds, int32_t H, int32_t F,
+                       const float *x, double *y) {
+    return ref_swiglu_q(fmt, gq, gs, uq, us, dq, ds, H, F, x, y, 0);
 }
 
 /* the activation block of a layer: act_block values when the 8-bit path is on, else 0 */
@@ -411,15 +491,18 @@ static int32_t ref_act_block(const moe_ref_layer *L) { return L->act_bits == 8 ?
 
 /* Expert e's tensors inside the stacked arrays. */
 static void ref_expert_ptrs(const moe_ref_layer *L, int32_t e, const uint8_t **gq,
-                            const float **gs, const uint8_t **uq, const float **us,
-                            const uint8_t **dq, const float **ds) {
+                            const void **gs, const uint8_t **uq, const void **us,
+                            const uint8_t **dq, const void **ds) {
     const int64_t H = L->hidden, F = L->ffn;
-    *gq = L->gate_q + (int64_t)e * F * (H / 2);
-    *gs = L->gate_s + (int64_t)e * F * (H / 64);
-    *uq = L->up_q + (int64_t)e * F * (H / 2);
-    *us = L->up_s + (int64_t)e * F * (H / 64);
-    *dq = L->down_q + (int64_t)e * H * (F / 2);
-    *ds = L->down_s + (int64_t)e * H * (F / 64);
+    const int32_t fmt = L->fmt;
+    const int64_t gu_q = F * moe_ref_code_bytes(fmt, H), gu_s = F * moe_ref_scale_bytes(fmt, H);
+    const int64_t d_q = H * moe_ref_code_bytes(fmt, F), d_s = H * moe_ref_scale_bytes(fmt, F);
+    *gq = L->gate_q + (int64_t)e * gu_q;
+    *gs = (const uint8_t *)L->gate_s + (int64_t)e * gu_s;
+    *uq = L->up_q + (int64_t)e * gu_q;
+    *us = (const uint8_t *)L->up_s + (int64_t)e * gu_s;
+    *dq = L->down_q + (int64_t)e * d_q;
+    *ds = (const uint8_t *)L->down_s + (int64_t)e * d_s;
 }
 
 int moe_ref_expert_ffn(const moe_ref_layer *L, const float *x, int32_t T,
@@ -429,11 +512,11 @@ int moe_ref_expert_ffn(const moe_ref_layer *L, const float *x, int32_t T,
     for (int32_t e = 0; e < E; e++) {
         for (int32_t r = off[e]; r < off[e + 1]; r++) {
             const uint8_t *gq, *uq, *dq;
-            const float *gs, *us, *ds;
+            const void *gs, *us, *ds;
             ref_expert_ptrs(L, e, &gq, &gs, &uq, &us, &dq, &ds);
             int32_t t = row_tok[r];
             if (t < 0 || t >= T) return REF_EINVAL;
-            int rc = ref_swiglu_q(gq, gs, uq, us, dq, ds, H, L->ffn, x + (int64_t)t * H,
+            int rc = ref_swiglu_q(L->fmt, gq, gs, uq, us, dq, ds, H, L->ffn, x + (int64_t)t * H,
                                   y_rows + (int64_t)r * H, ref_act_block(L));
             if (rc) return rc;
         }
@@ -472,15 +555,15 @@ int moe_ref_layer_forward(const moe_ref_layer *L, const float *x, int32_t T,
         /* weighted sum over the kept picks, in slot order */
         for (int32_t j = 0; j < keff && rc == 0; j++) {
             const uint8_t *gq, *uq, *dq;
-            const float *gs, *us, *ds;
+            const void *gs, *us, *ds;
             ref_expert_ptrs(L, ids[j], &gq, &gs, &uq, &us, &dq, &ds);
-            rc = ref_swiglu_q(gq, gs, uq, us, dq, ds, H, L->ffn, xt, y, ref_act_block(L));
+            rc = ref_swiglu_q(L->fmt, gq, gs, uq, us, dq, ds, H, L->ffn, xt, y, ref_act_block(L));
             if (rc) break;
             for (int32_t h = 0; h < H; h++) ot[h] += (double)w[j] * y[h];
         }
         /* the shared expert: every token, weight 1, not scaled */
         if (rc == 0 && L->shared_ffn > 0) {
-            rc = ref_swiglu_q(L->sh_gate_q, L->sh_gate_s, L->sh_up_q, L->sh_up_s,
+            rc = ref_swiglu_q(L->fmt, L->sh_gate_q, L->sh_gate_s, L->sh_up_q, L->sh_up_s,
                               L->sh_down_q, L->sh_down_s, H, L->shared_ffn, xt, y, ref_act_block(L));
             if (rc) break;
             for (int32_t h = 0; h < H; h++) ot[h] += y[h];

@@ -60,8 +60,10 @@ def _load():
     lib.synth_normal_f32.argtypes = [u64, i64, d, d, vp]
     lib.synth_quantize_gs64.argtypes = [vp, i64, i64, vp, vp]
     lib.synth_q4_normal.argtypes = [u64, i64, i64, d, vp, vp]
+    lib.synth_q3_normal.argtypes = [u64, i64, i64, d, vp, vp]
+    lib.synth_f4_normal.argtypes = [u64, i64, i64, d, vp, vp]
     for f in ("synth_u64", "synth_uniform_f64", "synth_normal_f64", "synth_normal_f32",
-              "synth_quantize_gs64", "synth_q4_normal"):
+              "synth_quantize_gs64", "synth_q4_normal", "synth_q3_normal", "synth_f4_normal"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -137,6 +139,34 @@ def q4_normal(seed: int, name: str, N: int, K: int, std: float, q_out=None, s_ou
     return q, s
 
 
+# expert weight formats (the library's MOE_FMT_* values)
+FMT_INT4, FMT_MXFP4, FMT_INT3 = 0, 1, 2
+FMT_NAMES = {FMT_INT4: "int4-gs64", FMT_MXFP4: "mxfp4", FMT_INT3: "int3-g64"}
+
+
+def code_bytes(fmt: int, K: int) -> int:
+    """Bytes of one row's codes: 4 bits per element, or 3 for int3-g64."""
+    return 3 * K // 8 if fmt == FMT_INT3 else K // 2
+
+
+def scale_shape(fmt: int, K: int):
+    """(elements per row, dtype) of one row's scales."""
+    return (K // 32, np.uint8) if fmt == FMT_MXFP4 else (K // 64, np.float32)
+
+
+def q_normal(fmt: int, seed: int, name: str, N: int, K: int, std: float, q_out=None, s_out=None):
+    """W[N][K] ~ N(0, std^2) (the same fp32 draws for every format) in expert format fmt."""
+    if fmt == FMT_INT4:
+        return q4_normal(seed, name, N, K, std, q_out, s_out)
+    ns, sdt = scale_shape(fmt, K)
+    q = np.empty((N, code_bytes(fmt, K)), np.uint8) if q_out is None else q_out
+    s = np.empty((N, ns), sdt) if s_out is None else s_out
+    assert q.shape == (N, code_bytes(fmt, K)) and s.shape == (N, ns) and s.dtype == sdt
+    f = _load().synth_q3_normal if fmt == FMT_INT3 else _load().synth_f4_normal
+    f(key(seed, name), N, K, std, _ptr(q), _ptr(s))
+    return q, s
+
+
 @dataclass(frozen=True)
 class Shape:
     """Layer hyper-parameters and how its synthetic inputs are drawn."""
@@ -158,6 +188,7 @@ class Shape:
     layers: int = 1
     logits: str = "router"           # "router" | "gumbel_skew" (constructed)
     extra: dict = field(default_factory=dict)
+    expert_fmt: int = FMT_INT4       # expert weight format (FMT_*)
 
 
 SHAPES = {
@@ -186,34 +217,41 @@ def custom(name: str, **kw) -> Shape:
 
 
 def expert_bytes(sh: Shape, ffn: int | None = None) -> int:
-    """int4 codes + fp32 gs64 scales of one expert's three matrices."""
+    """Codes + scales of one expert's three matrices in the shape's expert format."""
     F = sh.ffn if ffn is None else ffn
-    w = 3 * sh.hidden * F
-    return w // 2 + (w // 64) * 4
+    fmt = sh.expert_fmt
+    total = 0
+    for N, K in ((F, sh.hidden), (F, sh.hidden), (sh.hidden, F)):
+        ns, sdt = scale_shape(fmt, K)
+        total += N * (code_bytes(fmt, K) + ns * np.dtype(sdt).itemsize)
+    return total
 
 
 class Bank:
-    """Stacked int4-gs64 expert weights plus the shared expert (host numpy)."""
+    """Stacked expert weights (the shape's expert format) plus the shared expert (host numpy)."""
 
     def __init__(self, sh: Shape, seed: int = 0):
         H, E, F, Fs = sh.hidden, sh.n_experts, sh.ffn, sh.shared_ffn
+        fmt = sh.expert_fmt
         tag = f"bank:{sh.bank or sh.name}"
-        self.gate_q = np.empty((E, F, H // 2), np.uint8)
-        self.gate_s = np.empty((E, F, H // 64), np.float32)
-        self.up_q = np.empty((E, F, H // 2), np.uint8)
-        self.up_s = np.empty((E, F, H // 64), np.float32)
-        self.down_q = np.empty((E, H, F // 2), np.uint8)
-        self.down_s = np.empty((E, H, F // 64), np.float32)
+        nsh, sdt = scale_shape(fmt, H)
+        nsf, _ = scale_shape(fmt, F)
+        self.gate_q = np.empty((E, F, code_bytes(fmt, H)), np.uint8)
+        self.gate_s = np.empty((E, F, nsh), sdt)
+        self.up_q = np.empty((E, F, code_bytes(fmt, H)), np.uint8)
+        self.up_s = np.empty((E, F, nsh), sdt)
+        self.down_q = np.empty((E, H, code_bytes(fmt, F)), np.uint8)
+        self.down_s = np.empty((E, H, nsf), sdt)
         for e in range(E):
-            q4_normal(seed, f"{tag}/gate/{e}", F, H, sh.weight_std, self.gate_q[e], self.gate_s[e])
-            q4_normal(seed, f"{tag}/up/{e}", F, H, sh.weight_std, self.up_q[e], self.up_s[e])
-            q4_normal(seed, f"{tag}/down/{e}", H, F, sh.weight_std, self.down_q[e], self.down_s[e])
+            q_normal(fmt, seed, f"{tag}/gate/{e}", F, H, sh.weight_std, self.gate_q[e], self.gate_s[e])
+            q_normal(fmt, seed, f"{tag}/up/{e}", F, H, sh.weight_std, self.up_q[e], self.up_s[e])
+            q_normal(fmt, seed, f"{tag}/down/{e}", H, F, sh.weight_std, self.down_q[e], self.down_s[e])
         if Fs > 0:
-            self.sh_gate_q, self.sh_gate_s = q4_normal(seed, f"{tag}/shared/gate", Fs, H, sh.weight_std)
-            self.sh_up_q, self.sh_up_s = q4_normal(seed, f"{tag}/shared/up", Fs, H, sh.weight_std)
-            self.sh_down_q, self.sh_down_s = q4_normal(seed, f"{tag}/shared/down", H, Fs, sh.weight_std)
+            self.sh_gate_q, self.sh_gate_s = q_normal(fmt, seed, f"{tag}/shared/gate", Fs, H, sh.weight_std)
+            self.sh_up_q, self.sh_up_s = q_normal(fmt, seed, f"{tag}/shared/up", Fs, H, sh.weight_std)
+            self.sh_down_q, self.sh_down_s = q_normal(fmt, seed, f"{tag}/shared/down", H, Fs, sh.weight_std)
         else:
-            z8, z32 = np.zeros((0,), np.uint8), np.zeros((0,), np.float32)
+            z8, z32 = np.zeros((0,), np.uint8), np.zeros((0,), sdt)
             self.sh_gate_q = self.sh_up_q = self.sh_down_q = z8
             self.sh_gate_s = self.sh_up_s = self.sh_down_s = z32
 
@@ -296,7 +334,7 @@ def gumbel_skew_batch(sh: Shape, T: int, router_w: np.ndarray, bias: np.ndarray,
 def layer_params(sh: Shape) -> dict:
     return dict(hidden=sh.hidden, n_experts=sh.n_experts, ffn=sh.ffn, shared_ffn=sh.shared_ffn,
                 top_k=sh.top_k, top_p=sh.top_p, norm_topk=sh.norm_topk,
-                routed_scale=sh.routed_scale)
+                routed_scale=sh.routed_scale, expert_fmt=sh.expert_fmt)
 
 
 def make_layer(sh: Shape, seed: int = 0, layer: int = 0, bank: Bank | None = None) -> dict:

@@ -17,7 +17,14 @@
  * symmetric absmax quantiser (one fp32 scale per 64 consecutive K, scale =
  * max|w|/7, code = clamp(rint(w/scale), -8, 7), two codes per byte with the
  * even element in the low nibble) -- the offline conversion that produces the
- * weights the layer consumes, not a step of the layer.
+ * weights the layer consumes, not a step of the layer.  The other expert formats
+ * are produced the same way from the same fp32 draws:
+ *  - int3-g64: scale = max|w|/3 per 64, code = clamp(rint(w/scale), -4, 3), the codes'
+ *    low two bits and sign bits written into the two bit planes of the library's layout;
+ *  - MXFP4 (OCP Microscaling): per 32 consecutive K the shared exponent
+ *    X = floor(log2(max|w|)) - 2 (2 = the largest E2M1 exponent), stored as X + 127,
+ *    and each element the E2M1 value nearest to w / 2^X (ties to the even mantissa),
+ *    saturated at 6.
  */
 #include <math.h>
 #include <stdint.h>
@@ -133,6 +140,97 @@ void synth_q4_normal(uint64_t key, int64_t N, int64_t K, double std, uint8_t *q,
             for (int i = 0; i < 64; i++)
                 w[i] = (float)(std * normal_at(key, (uint64_t)(n * K + g * 64 + i)));
             quant_group(w, q + n * (K / 2) + g * 32, s + n * (K / 64) + g);
+        }
+    }
+}
+
+/* ---- int3-g64 ---------------------------------------------------------------
+ * Element i = 16d + 8a + 2b + o of a 64-group: low two bits at bits 2(2a+o).. of byte
+ * 16G + 4d + b of the low plane; i = 32h + 8m + 2b + o: sign at bit 2m+o of byte
+ * 8G + 4h + b of the sign plane (which starts K/4 bytes into the row). */
+static void quant_group3(const float *w, uint8_t *lowp, uint8_t *signp, float *s) {
+    float amax = 0.0f;
+    for (int i = 0; i < 64; i++) {
+        float a = fabsf(w[i]);
+        amax = a > amax ? a : amax;
+    }
+    float sc = amax / 3.0f;
+    *s = sc;
+    memset(lowp, 0, 16);
+    memset(signp, 0, 8);
+    for (int d = 0; d < 4; d++)
+        for (int a = 0; a < 2; a++)
+            for (int b = 0; b < 4; b++)
+                for (int o = 0; o < 2; o++) {
+                    const int i = 16 * d + 8 * a + 2 * b + o;
+                    int c = 0;
+                    if (sc > 0.0f) {
+                        float r = rintf(w[i] / sc);
+                        r = r > 3.0f ? 3.0f : (r < -4.0f ? -4.0f : r);
+                        c = (int)r;
+                    }
+                    const int bits = c & 7; /* 3-bit two's complement */
+                    lowp[4 * d + b] |= (uint8_t)((bits & 3) << (2 * (2 * a + o)));
+                    const int h = i / 32, m = (i / 8) % 4;
+                    signp[4 * h + b] |= (uint8_t)(((bits >> 2) & 1) << (2 * m + o));
+                }
+}
+
+void synth_q3_normal(uint64_t key, int64_t N, int64_t K, double std, uint8_t *q, float *s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float w[64];
+        uint8_t *row = q + n * (3 * K / 8);
+        for (int64_t g = 0; g < K / 64; g++) {
+            for (int i = 0; i < 64; i++)
+                w[i] = (float)(std * normal_at(key, (uint64_t)(n * K + g * 64 + i)));
+            quant_group3(w, row + 16 * g, row + K / 4 + 8 * g, s + n * (K / 64) + g);
+        }
+    }
+}
+
+/* ---- MXFP4 ------------------------------------------------------------------ */
+static const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static void quant_block_fp4(const float *w, uint8_t *q, uint8_t *e) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        float a = fabsf(w[i]);
+        amax = a > amax ? a : amax;
+    }
+    int X = -127;
+    if (amax > 0.0f) {
+        int ex;
+        frexpf(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+        X = ex - 1 - 2;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    *e = (uint8_t)(X + 127);
+    for (int i = 0; i < 32; i += 2) {
+        int c[2];
+        for (int h = 0; h < 2; h++) {
+            const double v = ldexp((double)w[i + h], -X);
+            const double a = fabs(v);
+            int best = 0;
+            for (int m = 1; m < 8; m++) {
+                const double dm = fabs(a - kE2M1[m]), db = fabs(a - kE2M1[best]);
+                if (dm < db || (dm == db && (m & 1) == 0)) best = m;
+            }
+            c[h] = best | (v < 0.0 && best != 0 ? 8 : 0);
+        }
+        q[i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+    }
+}
+
+void synth_f4_normal(uint64_t key, int64_t N, int64_t K, double std, uint8_t *q, uint8_t *e) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float w[32];
+        for (int64_t b = 0; b < K / 32; b++) {
+            for (int i = 0; i < 32; i++)
+                w[i] = (float)(std * normal_at(key, (uint64_t)(n * K + b * 32 + i)));
+            quant_block_fp4(w, q + n * (K / 2) + b * 16, e + n * (K / 32) + b);
         }
     }
 }
