@@ -32,6 +32,27 @@
  *   W[n][k] = q(n,k) * s[n][k/64].
  * Routed expert tensors are stacked by expert id: gate/up q [E][F][H/2], s [E][F][H/64];
  * down q [E][H][F/2], s [E][H][F/64].
+ *
+ * Other expert formats (moe_layer.expert_fmt, one format for the routed and the shared
+ * experts), a matrix W[N][K] with K a multiple of 64:
+ * MOE_FMT_MXFP4 -- fp4 experts with UE8M0 block scales ([C] §五; the MXFP4 experts of
+ *   [C] §六), read as the OCP Microscaling FP4 element: E2M1 codes (bit 3 sign, bits 2-1
+ *   exponent with bias 1, bit 0 mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+ *   packed two per byte like int4 (element 2j in the low nibble of byte j),
+ *   q : uint8 [N][K/2];  s : uint8 [N][K/32], one UE8M0 exponent per 32 consecutive
+ *   elements;  W[n][k] = e2m1(q(n,k)) * 2^(s[n][k/32] - 127), an exponent byte of 255
+ *   being NaN.
+ * MOE_FMT_INT3_G64 -- int3-g64 ([C] §8.3, fmt=5: 3-bit weights, one scale per 64): codes
+ *   c in [-4, 3], W[n][k] = c * s[n][k/64], s : fp32 [N][K/64];  q : uint8 [N][3K/8], per
+ *   row two bit planes: bytes [0, K/4) hold the codes' low two bits, bytes [K/4, 3K/8)
+ *   their sign bits (c = low - 4 sign).  Element i = 16d + 8a + 2b + o (d < 4, a < 2,
+ *   b < 4, o < 2) of 64-group G has its low bits at bits 2(2a+o) and 2(2a+o)+1 of byte
+ *   16G + 4d + b; written i = 32h + 8m + 2b + o (h < 2, m < 4), its sign bit is bit
+ *   2m+o of byte K/4 + 8G + 4h + b.  (The pages fix no bit layout.  This one lets a
+ *   32-bit word of either plane give four codes of the same parity by one shift and
+ *   mask, in the element order the int4 path uses.)
+ * Stacked routed tensors hold E such matrices back to back (q: E*F or E*H rows of the
+ * format's row bytes; s likewise).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -60,9 +81,13 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };        /* output element type of moe_layer_f
 #define MOE_MAX_TOKENS 4096
 #define MOE_MAX_DIM 16384                  /* hidden, ffn, shared_ffn */
 
+enum { MOE_FMT_INT4_G64 = 0, MOE_FMT_MXFP4 = 1, MOE_FMT_INT3_G64 = 2 };  /* moe_layer.expert_fmt */
+
+/* One quantised matrix: codes and scales in the layer's expert format (int4-gs64:
+ * q [N][K/2], s fp32 [N][K/64]; the other formats as described above). */
 typedef struct {
-    const uint8_t *q; /* [N][K/2] */
-    const float *s;   /* [N][K/64] */
+    const uint8_t *q;
+    const void *s;
 } moe_q4;
 
 typedef struct {
@@ -93,8 +118,12 @@ typedef struct {
      * changes results): per block (the same blocks: 32 values for T <= 4, 256 above) the
      * codes rint(x * 2^n) in [-127, 127] with n the largest integer (at most 149) for
      * which max|x| * 2^n <= 127, for x and for the SwiGLU output; the matrix-core path
-     * then runs one int8 product per group instead of two.  Other values: MOE_EINVAL. */
+     * then runs one int8 product per group instead of two.  Other values: MOE_EINVAL.
+     * With expert_fmt MOE_FMT_MXFP4 only 0 or 16 (MOE_EUNSUPPORTED for 8). */
     int32_t act_bits;
+    /* Expert weight format, MOE_FMT_* (0: int4-gs64); other values MOE_EINVAL.  How each
+     * format enters the products is described at moe_expert_ffn. */
+    int32_t expert_fmt;
 } moe_layer;
 
 /* Optional routing outputs of moe_layer_forward.  Any member may be NULL. */
@@ -152,6 +181,11 @@ int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32
  * per block of consecutive values (32 for T <= 4, 256 for larger T): one rounding of
  * less than max|x| / 32639 per value, none for values with at most 15 significant
  * bits relative to the block's largest; the dot products are exact int32 sums.
+ * int3-g64 experts enter the same way.  MXFP4 experts: the E2M1 values times their
+ * block's power of two are exact in fp32 and bf16; for T <= 4 they multiply the fp32
+ * activations with fp32 accumulation, above that each activation is split into two
+ * bf16 terms (x = hi + lo + r with |r| <= 2^-16 |x|) for bf16 matrix-core products
+ * accumulated in fp32.
  * Inputs n_uniq/uniq/off/row_tok as produced by moe_union (device).
  * Output: y_rows [T*k][H] fp32; rows past off[E] are left untouched. */
 int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,

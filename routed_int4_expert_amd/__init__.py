@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EALIGN, MOE_EDEVICE = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
+MOE_FMT_INT4_G64, MOE_FMT_MXFP4, MOE_FMT_INT3_G64 = 0, 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_DIM = 256, 16, 4096, 16384
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_union", "moe_expert_ffn",
@@ -49,6 +50,7 @@ class LayerC(ctypes.Structure):
         ("gate", Q4), ("up", Q4), ("down", Q4),
         ("sh_gate", Q4), ("sh_up", Q4), ("sh_down", Q4),
         ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32), ("act_bits", ctypes.c_int32),
+        ("expert_fmt", ctypes.c_int32),
     ]
 
 
@@ -164,7 +166,8 @@ class Layer:
     def __init__(self, params: dict, tensors: dict):
         self.params = {k: params[k] for k in PARAMS}
         self.params.update(n_group=int(params.get("n_group", 0)), topk_group=int(params.get("topk_group", 0)),
-                           act_bits=int(params.get("act_bits", 0)))
+                           act_bits=int(params.get("act_bits", 0)),
+                           expert_fmt=int(params.get("expert_fmt", MOE_FMT_INT4_G64)))
         self.t = dict(tensors)
         c = LayerC()
         c.hidden, c.n_experts = int(params["hidden"]), int(params["n_experts"])
@@ -173,6 +176,7 @@ class Layer:
         c.routed_scale = float(params["routed_scale"])
         c.n_group, c.topk_group = self.params["n_group"], self.params["topk_group"]
         c.act_bits = self.params["act_bits"]
+        c.expert_fmt = self.params["expert_fmt"]
         g = self.t.get
         c.router_w = _ptr(g("router_w"))
         c.router_bias = _ptr(g("router_bias"))

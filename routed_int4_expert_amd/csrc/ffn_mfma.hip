@@ -23,6 +23,17 @@
 //    chunk step (over 16 for the codes' factor) scales into the fp32 running sum.
 //    The one rounding of x is x16 itself.
 //
+// int3-g64 codes (moe.h bit planes) take the same path: a lane's operand is one word of
+// the low-bit plane (16 codes in the int4 order above) and its 16 sign bits, placed
+// as 32 c in the top three bits of each byte (the chunk's sums then carry a factor
+// 32 instead of 16).
+// MXFP4 codes are turned into their exact bf16 values (E2M1 times the block's power of
+// two, by the hardware's scaled fp4 -> bf16 conversion) and multiply bf16 activations
+// on v_mfma_f32_16x16x32_bf16, one 32-element block (one scale) per product; each
+// activation enters as two bf16 terms hi = bf16(x), lo = bf16(x - hi), 256 bytes per
+// row and 64-group (hi of the group's two blocks, then lo), and the products
+// accumulate in the fp32 accumulators across the whole reduction.
+//
 // Work item = up to 16 or, for batches with many rows per expert, 32 rows of one
 // expert (one or two 16-row MFMA blocks) x a block of outputs: 4 column sets x 32
 // outputs (gate and up for the same columns) or 4 x 64 outputs (down).  Experts with more rows, and the shared expert, span several
@@ -48,11 +59,19 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 constexpr uint32_t kHighNibbles = 0xF0F0F0F0u;  // 16 q per byte
-constexpr int kGroupBytes = 128;                // one row's 64-group: 4 x 16 B hi, then 4 x 16 B lo
 constexpr int kCG = 4;                          // groups per K chunk
-constexpr int kChunkBytes = kCG * kGroupBytes;  // a row's chunk: 512 B
-constexpr int kRowPitch = kChunkBytes + 16;     // +16: rows start in distinct LDS banks
+// one row's 64-group of prepared activations: 4 x 16 B hi, then 4 x 16 B lo (int8
+// limbs), or 2 x 64 B hi, then 2 x 64 B lo (bf16 terms, MXFP4)
+template <int FMT>
+constexpr int group_bytes() { return FMT == kFmtF4 ? 256 : 128; }
+template <int FMT>
+constexpr int chunk_bytes() { return kCG * group_bytes<FMT>(); }  // a row's chunk: 512 or 1024 B
+template <int FMT>
+constexpr int row_pitch() { return chunk_bytes<FMT>() + 16; }     // +16: rows start in distinct LDS banks
 // a column set's weight codes of one chunk in LDS: 4 B blocks x 16 rows x 128 B, rows
 // 144 B apart so the 8-byte operand reads of 16 rows hit distinct banks
 constexpr int kCodePitch = 144;
@@ -71,7 +90,14 @@ struct PrepJob {
     float *step;
     int blocks;  // workgroups of 256 threads this job takes
     int act8;    // the opt-in 8-bit codes (hi bytes 0, lo bytes the code)
+    int bf16;    // the MXFP4 path's two bf16 terms per value instead (no steps)
 };
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
+    const uint32_t b = __float_as_uint(v);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);  // NaN stays NaN
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
 
 __device__ __forceinline__ uint32_t pack_bytes(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
@@ -95,6 +121,26 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
         e[0] = v0.x; e[1] = v0.y; e[2] = v0.z; e[3] = v0.w;
         e[4] = v1.x; e[5] = v1.y; e[6] = v1.z; e[7] = v1.w;
     }
+    if (j.bf16) {
+        // hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in fp32), in element order:
+        // word b of the row is block (b % 8) / 4 of group b / 8, 16 bytes at (b % 4) * 16
+        if (live) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const uint16_t h0 = bf16_bits_rne(e[2 * s]), h1 = bf16_bits_rne(e[2 * s + 1]);
+                const float r0 = e[2 * s] - __uint_as_float((uint32_t)h0 << 16);
+                const float r1 = e[2 * s + 1] - __uint_as_float((uint32_t)h1 << 16);
+                hw[s] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lw[s] = (uint32_t)bf16_bits_rne(r0) | ((uint32_t)bf16_bits_rne(r1) << 16);
+            }
+            const int G = b / 8, wg = b % 8;
+            uint8_t *grp = j.frag + ((size_t)row * NGp + G) * group_bytes<kFmtF4>() + (wg / 4) * 64 + (wg % 4) * 16;
+            *reinterpret_cast<uint4 *>(grp) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4 *>(grp + 128) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        return;
+    }
     // the chunk's largest magnitude as bits (an integer max, so NaN and Inf count)
     uint32_t mb = 0;
 #pragma unroll
@@ -115,7 +161,7 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     }
     if (live) {
         const int G = b / 8, wg = b % 8;
-        uint8_t *grp = j.frag + ((size_t)row * NGp + G) * kGroupBytes;
+        uint8_t *grp = j.frag + ((size_t)row * NGp + G) * group_bytes<kFmtI4>();
         *reinterpret_cast<uint2 *>(grp + 8 * wg) =
             make_uint2(pack_bytes(hi[0], hi[2], hi[4], hi[6]), pack_bytes(hi[1], hi[3], hi[5], hi[7]));
         *reinterpret_cast<uint2 *>(grp + 64 + 8 * wg) =
@@ -124,9 +170,11 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     if (in_rows && w == 0) j.step[(size_t)row * NC + c] = finite ? (nz ? ldexpf(1.0f, -sh) : 0.0f) : __builtin_nanf("");
 }
 
-static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step, int act8 = 0) {
+static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step, int act8 = 0,
+                        int bf16 = 0) {
     PrepJob j;
     j.act8 = act8;
+    j.bf16 = bf16;
     j.src = src;
     j.rows = rows;
     j.K = K;
@@ -286,19 +334,21 @@ constexpr int kCompWaves = kColSets * kCW;
 constexpr int kMfmaThreads = kWave * (kCompWaves + kLoadWaves);  // 768
 constexpr int kNBL = 4 / kCW;                                   // 16-column blocks per compute wave
 constexpr int kBufCodes = kColSets * 64 * kCodePitch;          // [column set][64 rows][144 B]
-constexpr int kBufScales = kColSets * 64 * 4 * 4;              // [256 columns][4 groups] fp32
 constexpr int kMaxWorkPerWg = 64;
 
-// An LDS chunk buffer for items of IRB 16-row blocks: codes, scales, the activation
-// tile [16 IRB rows][528 B] and the rows' fp32 chunk steps.
-template <int IRB>
+// An LDS chunk buffer for items of IRB 16-row blocks: codes, scales ([256 columns]
+// [4 groups] fp32, or for MXFP4 [256 columns][4 groups][2 blocks] fp32 powers of two),
+// the activation tile [16 IRB rows][528 or 1040 B] and the rows' fp32 chunk steps.
+template <int IRB, int FMT>
 struct MfmaBuf {
+    static constexpr int kScales = kColSets * 64 * 4 * 4 * (FMT == kFmtF4 ? 2 : 1);
     static constexpr int kRows = 16 * IRB;
-    static constexpr int kAct = kRows * kRowPitch;
+    static constexpr int kAct = kRows * row_pitch<FMT>();
     static constexpr int kNs = kRows * 4;
-    static constexpr int kBytes = kBufCodes + kBufScales + kAct + kNs;
-    static constexpr int kActLoads = kRows * kChunkBytes / 16 / kLoadThreads;  // 16-byte loads per thread
-    static_assert(kActLoads == 2 * IRB, "two 16-byte loads per row block and thread");
+    static constexpr int kBytes = kBufCodes + kScales + kAct + kNs;
+    static constexpr int kActPerRow = chunk_bytes<FMT>() / 16 / 16;  // 16-byte loads per row and thread
+    static constexpr int kActLoads = IRB * kActPerRow;              // per thread
+    static_assert(kRows * chunk_bytes<FMT>() / 16 / kLoadThreads == kActLoads, "activation loads");
 };
 
 template <int IR>
@@ -328,6 +378,28 @@ struct ChunkRegs {
     float n;
 };
 
+// 16 int3 codes of one output row (a low-plane word and the 16 sign bits at bits
+// 4(p % 2) .. 4(p % 2) + 3 of each byte of the sign word) -> the 16 signed bytes 32 c:
+// per bit pair s the four elements the int4 order puts in dword s.
+__device__ __forceinline__ i32x4_t code_bytes_i3(uint32_t lw, uint32_t sw) {
+    i32x4_t v;
+    v.x = (int)(((lw << 5) & 0x60606060u) | ((sw << 7) & 0x80808080u));
+    v.y = (int)(((lw << 3) & 0x60606060u) | ((sw << 6) & 0x80808080u));
+    v.z = (int)(((lw << 1) & 0x60606060u) | ((sw << 5) & 0x80808080u));
+    v.w = (int)(((lw >> 1) & 0x60606060u) | ((sw << 4) & 0x80808080u));
+    return v;
+}
+
+// 8 E2M1 codes (one word, elements 2j in the low nibble of byte j) times the block's
+// power of two -> the 8 exact bf16 values of a B operand, in element order.
+__device__ __forceinline__ bf16x8_t code_bf16_f4(uint32_t w, float scale) {
+    const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
 // IRB: 16-row blocks per work item (items hold at most 16 IRB rows; with IRB = 2 an
 // item of at most 16 rows computes one block).  Twelve waves: two compute waves per
 // column set, each taking two of the set's four 16-column blocks (gate/up: a gate block
@@ -339,12 +411,16 @@ struct ChunkRegs {
 // bytes) and no shift-add.  TAB: routed experts read through the residency tier's
 // pointer table (a separate instantiation: the table lookups would otherwise add
 // register pressure to the default kernel).
-template <bool GU, int IRB, bool A8, bool TAB>
+template <bool GU, int IRB, bool A8, bool TAB, int FMT>
 __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
     constexpr int kThreads = kMfmaThreads, NBL = kNBL;
-    using Buf = MfmaBuf<IRB>;
+    using Buf = MfmaBuf<IRB, FMT>;
     constexpr int IR = Buf::kRows, kBufBytes = Buf::kBytes, kBufAct = Buf::kAct;
-    constexpr int kActLoads = Buf::kActLoads, kRowBlocks = IRB;
+    constexpr int kActLoads = Buf::kActLoads, kRowBlocks = IRB, kActPerRow = Buf::kActPerRow;
+    constexpr int kBufScales = Buf::kScales;
+    constexpr int kGroupBytes = group_bytes<FMT>(), kChunkBytes = chunk_bytes<FMT>();
+    constexpr int kRowPitch = row_pitch<FMT>();
+    static_assert(!(A8 && FMT == kFmtF4), "the MXFP4 path has no 8-bit activations");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     WorkDesc<IR> *work = reinterpret_cast<WorkDesc<IR> *>(lds + 2 * kBufBytes);
     const int tid = threadIdx.x;
@@ -400,7 +476,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         // an up row for odd i (gate/up), whatever the lane; so is scale column sc_col(i).
         int pk = -1;
         const uint8_t *qb0 = nullptr, *qb1 = nullptr, *abase = nullptr;
-        const float *sb0 = nullptr, *sb1 = nullptr, *nbase = nullptr;  // nbase: chunk steps
+        const uint8_t *sb0 = nullptr, *sb1 = nullptr;  // scales, as bytes
+        const float *nbase = nullptr;                  // chunk steps
         uint32_t qo[8], so[4], no = 0;
         const uint8_t *arow[kRowBlocks] = {};  // 64-bit: union rows x fragment bytes can pass 2^32
         bool two = false;                       // the item has a second row block
@@ -415,19 +492,19 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const int e = __builtin_amdgcn_readfirstlane(d.e);
             const int nb0 = __builtin_amdgcn_readfirstlane(d.nb0);
             int K, N;
+            moe_q4 m0, m1;
             if (GU) {
                 K = a.H;
                 N = e >= 0 ? a.F : a.Fs;
                 if (TAB && e >= 0) {  // the residency tier's slots
-                    qb0 = a.tab[3 * e].q;     sb0 = a.tab[3 * e].s;
-                    qb1 = a.tab[3 * e + 1].q; sb1 = a.tab[3 * e + 1].s;
+                    m0 = a.tab[3 * e];
+                    m1 = a.tab[3 * e + 1];
                 } else if (e >= 0) {
-                    const size_t gq = (size_t)e * a.F * (a.H / 2), gs = (size_t)e * a.F * (a.H / 64);
-                    qb0 = a.gate.q + gq; sb0 = a.gate.s + gs;
-                    qb1 = a.up.q + gq;   sb1 = a.up.s + gs;
+                    m0 = fmt_stack_at(a.gate, FMT, e, a.F, a.H);
+                    m1 = fmt_stack_at(a.up, FMT, e, a.F, a.H);
                 } else {
-                    qb0 = a.sh_gate.q; sb0 = a.sh_gate.s;
-                    qb1 = a.sh_up.q;   sb1 = a.sh_up.s;
+                    m0 = a.sh_gate;
+                    m1 = a.sh_up;
                 }
                 abase = a.x_frag;
                 nbase = a.x_step;
@@ -435,36 +512,41 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
                 if (e >= 0) {
-                    if constexpr (TAB) {
-                        qb0 = a.tab[3 * e + 2].q; sb0 = a.tab[3 * e + 2].s;
-                    } else {
-                        const size_t dq = (size_t)e * a.H * (a.F / 2), ds = (size_t)e * a.H * (a.F / 64);
-                        qb0 = a.down.q + dq; sb0 = a.down.s + ds;
-                    }
+                    if constexpr (TAB) m0 = a.tab[3 * e + 2];
+                    else m0 = fmt_stack_at(a.down, FMT, e, a.H, a.F);
                     abase = a.hr_frag;
                     nbase = a.hr_step;
                 } else {
-                    qb0 = a.sh_down.q; sb0 = a.sh_down.s;
+                    m0 = a.sh_down;
                     abase = a.hs_frag;
                     nbase = a.hs_step;
                 }
-                qb1 = qb0;
-                sb1 = sb0;
+                m1 = m0;
             }
+            qb0 = m0.q;
+            qb1 = m1.q;
+            sb0 = static_cast<const uint8_t *>(m0.s);
+            sb1 = static_cast<const uint8_t *>(m1.s);
             NG = K / 64;
             const int NGp = mfma_groups_padded(K);
             qlast = (uint32_t)(K / 2 - 16);
+            const uint32_t rowq = (uint32_t)fmt_code_bytes(FMT, K), rows_ = (uint32_t)fmt_scale_bytes(FMT, K);
+            if constexpr (FMT == kFmtI3) {
+                // code lane t % 8: the low plane of group 4c + t % 8 (16 B, lanes 0-3) or the
+                // sign plane of group 4c + t % 8 - 4 (8 B, lanes 4-7); qlast: plane start
+                qlast = (t % 8) < 4 ? 0u : (uint32_t)(K / 4);
+            }
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 bool second;
                 const int n = min(load_row_output<GU>(t / 8 + 32 * i, nb0, second), N - 1);
-                qo[i] = (uint32_t)n * (uint32_t)(K / 2);
+                qo[i] = (uint32_t)n * rowq;
             }
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 bool second;
                 const int n = min(load_row_output<GU>(sc_col(i), nb0, second), N - 1);
-                so[i] = (uint32_t)n * (uint32_t)NG;
+                so[i] = (uint32_t)n * rows_;
             }
 #pragma unroll
             for (int rb = 0; rb < kRowBlocks; rb++)
@@ -476,19 +558,47 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
         auto load = [&](ChunkRegs<kActLoads> &v) __attribute__((always_inline)) {
             const int k = lk, c = lc;  // always a chunk that exists
             if (k != pk) rows_of(k);
-            const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
+            if constexpr (FMT == kFmtI3) {
+                const int t8 = t % 8;
+                const uint32_t g = (uint32_t)min(kCG * c + (t8 & 3), NG - 1);  // always a group of the row
+                if (t8 < 4) {
+                    // (two 8-byte loads: int3 rows are 3K/8 bytes long, so only 8-byte aligned)
 #pragma unroll
-            for (int i = 0; i < 8; i++) v.q[i] = *reinterpret_cast<const u32x4_t *>(((i & 1) ? qb1 : qb0) + (qo[i] + off));
+                    for (int i = 0; i < 8; i++) {
+                        const uint2 *src = reinterpret_cast<const uint2 *>(((i & 1) ? qb1 : qb0) + (qo[i] + 16 * g));
+                        const uint2 w0 = src[0], w1 = src[1];
+                        v.q[i] = u32x4_t{w0.x, w0.y, w1.x, w1.y};
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const uint2 w = *reinterpret_cast<const uint2 *>(((i & 1) ? qb1 : qb0) + (qo[i] + qlast + 8 * g));
+                        v.q[i] = u32x4_t{w.x, w.y, 0u, 0u};
+                    }
+                }
+            } else {
+                const uint32_t off = min((uint32_t)(128 * c + 16 * (t % 8)), qlast);
+#pragma unroll
+                for (int i = 0; i < 8; i++) v.q[i] = *reinterpret_cast<const u32x4_t *>(((i & 1) ? qb1 : qb0) + (qo[i] + off));
+            }
             const uint32_t sg = (uint32_t)min(kCG * c + t % 4, NG - 1);
+            if constexpr (FMT == kFmtF4) {  // the group's two exponent bytes, as raw bits
 #pragma unroll
-            for (int i = 0; i < 4; i++) v.s[i] = ((i & 1) ? sb1 : sb0)[so[i] + sg];
+                for (int i = 0; i < 4; i++)
+                    v.s[i] = __uint_as_float((uint32_t) * reinterpret_cast<const uint16_t *>(((i & 1) ? sb1 : sb0) + so[i] + 2 * sg));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    v.s[i] = reinterpret_cast<const float *>(((i & 1) ? sb1 : sb0) + so[i])[sg];
+            }
             // the second row block's rows only if the item has them (else the registers
             // keep older values, which no compute wave reads)
 #pragma unroll
             for (int i = 0; i < kActLoads; i++)
-                if (i < 2 || two)
-                    v.a[i] = *reinterpret_cast<const uint4 *>(arow[i / 2] + (uint32_t)(c * kChunkBytes + 256 * (i % 2)));
-            v.n = nbase[no + c];
+                if (i < kActPerRow || two)
+                    v.a[i] = *reinterpret_cast<const uint4 *>(arow[i / kActPerRow] +
+                                                              (uint32_t)(c * kChunkBytes + 256 * (i % kActPerRow)));
+            if constexpr (FMT != kFmtF4) v.n = nbase[no + c];
             // advance; past the last chunk the head stays there (that chunk is loaded again)
             int nk = lk, nc = lc + 1;
             if (nc >= work[nk].nch) {
@@ -506,17 +616,35 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int r = t / 8 + 32 * i;
-                *reinterpret_cast<u32x4_t *>(B + (r / 64) * 64 * kCodePitch + (r % 64) * kCodePitch + 16 * (t % 8)) = v.q[i];
+                uint8_t *row = B + (r / 64) * 64 * kCodePitch + (r % 64) * kCodePitch;
+                if constexpr (FMT == kFmtI3) {
+                    // a row's chunk: low planes of its 4 groups (64 B), then their sign planes (32 B)
+                    const int t8 = t % 8;
+                    if (t8 < 4) *reinterpret_cast<u32x4_t *>(row + 16 * t8) = v.q[i];
+                    else *reinterpret_cast<uint2 *>(row + 64 + 8 * (t8 - 4)) = make_uint2(v.q[i].x, v.q[i].y);
+                } else {
+                    *reinterpret_cast<u32x4_t *>(row + 16 * (t % 8)) = v.q[i];
+                }
             }
+            if constexpr (FMT == kFmtF4) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * sc_col(i) + t % 4] = v.s[i];
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t eb = __float_as_uint(v.s[i]);
+                    *reinterpret_cast<float2 *>(reinterpret_cast<float *>(B + kBufCodes) + 8 * sc_col(i) + 2 * (t % 4)) =
+                        make_float2(ue8m0_f32(eb & 0xFFu), ue8m0_f32(eb >> 8));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) reinterpret_cast<float *>(B + kBufCodes)[4 * sc_col(i) + t % 4] = v.s[i];
+            }
 #pragma unroll
             for (int i = 0; i < kActLoads; i++) {
-                const int ar = 16 * (i / 2) + t / 16;
-                *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * (i % 2))) = v.a[i];
+                const int ar = 16 * (i / kActPerRow) + t / 16;
+                *reinterpret_cast<uint4 *>(B + kBufCodes + kBufScales + ar * kRowPitch + 16 * (t % 16 + 16 * (i % kActPerRow))) = v.a[i];
             }
-            if (t < IR)  // a lane's four rows' steps are one read
-                reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct)[t] = v.n;
+            if constexpr (FMT != kFmtF4)
+                if (t < IR)  // a lane's four rows' steps are one read
+                    reinterpret_cast<float *>(B + kBufCodes + kBufScales + kBufAct)[t] = v.n;
         };
         ChunkRegs<kActLoads> r0, r1;
 #pragma unroll
@@ -605,8 +733,14 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 Opnd o;
                 uint2 w[NBL];
 #pragma unroll
-                for (int b = 0; b < NBL; b++)
-                    w[b] = *reinterpret_cast<const uint2 *>(cw + (16 * gblk(b) + j) * kCodePitch + 32 * gi + 8 * p);
+                for (int b = 0; b < NBL; b++) {
+                    const uint8_t *cr = cw + (16 * gblk(b) + j) * kCodePitch;
+                    if constexpr (FMT == kFmtI3)  // low-plane word p, the sign word of p / 2
+                        w[b] = make_uint2(*reinterpret_cast<const uint32_t *>(cr + 16 * gi + 4 * p),
+                                          *reinterpret_cast<const uint32_t *>(cr + 64 + 8 * gi + 4 * (p / 2)) >> (4 * (p % 2)));
+                    else
+                        w[b] = *reinterpret_cast<const uint2 *>(cr + 32 * gi + 8 * p);
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; rb++) {
                     const uint8_t *ar = tile + (16 * rb + j) * kRowPitch + gi * kGroupBytes + 16 * p;
@@ -614,7 +748,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                     o.a[rb][1] = *reinterpret_cast<const i32x4_t *>(ar + 64);
                 }
 #pragma unroll
-                for (int b = 0; b < NBL; b++) o.bo[b] = code_bytes(w[b]);
+                for (int b = 0; b < NBL; b++) {
+                    if constexpr (FMT == kFmtI3) o.bo[b] = code_bytes_i3(w[b].x, w[b].y);
+                    else o.bo[b] = code_bytes(w[b]);
+                }
                 return o;
             };
             const i32x4_t zero = {0, 0, 0, 0};
@@ -651,14 +788,52 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                         }
                 if (gi + 1 < kCG) cur = nxt;
             }
-            // the chunk's sums times the row steps (over 16: the codes entered as 16 q)
+            // the chunk's sums times the row steps (over 16: the codes entered as 16 q; int3:
+            // over 32)
+            constexpr float kUnit = FMT == kFmtI3 ? 0.03125f : 0.0625f;
 #pragma unroll
             for (int rb = 0; rb < RB; rb++)
 #pragma unroll
                 for (int b = 0; b < NBL; b++)
 #pragma unroll
                     for (int v = 0; v < 4; v++)
-                        acc[rb][b][v] = fmaf(csum[rb][b][v], st4[rb][v] * 0.0625f, acc[rb][b][v]);
+                        acc[rb][b][v] = fmaf(csum[rb][b][v], st4[rb][v] * kUnit, acc[rb][b][v]);
+        };
+        // MXFP4: per group and 32-element block, the B operands of this lane's columns (8
+        // E2M1 codes times the block's power of two, as bf16) and the rows' hi and lo
+        // bf16 terms; two bf16 products per block accumulate straight into acc.
+        auto run_chunk_f4 = [&](const uint8_t *B, int ng, auto rbc) __attribute__((always_inline)) {
+            constexpr int RB = decltype(rbc)::value;
+            const uint8_t *cw = B + cs * 64 * kCodePitch;
+            const float *scl = reinterpret_cast<const float *>(B + kBufCodes);
+            const uint8_t *tile = B + kBufCodes + kBufScales;
+#pragma unroll
+            for (int gi = 0; gi < kCG; gi++) {
+                if (gi >= ng) break;
+#pragma unroll
+                for (int blk = 0; blk < 2; blk++) {
+                    bf16x8_t bo[NBL], ah[RB], al[RB];
+#pragma unroll
+                    for (int b = 0; b < NBL; b++) {
+                        const int col = 16 * gblk(b) + j;
+                        const uint32_t w = *reinterpret_cast<const uint32_t *>(cw + col * kCodePitch + 32 * gi + 16 * blk + 4 * p);
+                        bo[b] = code_bf16_f4(w, scl[8 * (cs * 64 + col) + 2 * gi + blk]);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; rb++) {
+                        const uint8_t *ar = tile + (16 * rb + j) * kRowPitch + gi * kGroupBytes + 64 * blk + 16 * p;
+                        ah[rb] = *reinterpret_cast<const bf16x8_t *>(ar);
+                        al[rb] = *reinterpret_cast<const bf16x8_t *>(ar + 128);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+                        for (int b = 0; b < NBL; b++) {
+                            acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[rb], bo[b], acc[rb][b], 0, 0, 0);
+                            acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[rb], bo[b], acc[rb][b], 0, 0, 0);
+                        }
+                }
+            }
         };
         lds_barrier();
         for (int s = 0; s < S; s++) {
@@ -673,7 +848,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
 #pragma unroll
                     for (int b = 0; b < NBL; b++) acc[rb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-            if constexpr (IRB == 2) {
+            if constexpr (FMT == kFmtF4) {
+                static_assert(IRB == 1, "MXFP4 items hold at most 16 rows");
+                run_chunk_f4(B, ng, std::integral_constant<int, 1>());
+            } else if constexpr (IRB == 2) {
                 if (d.R > 16) run_chunk(B, ng, std::integral_constant<int, 2>());
                 else run_chunk(B, ng, std::integral_constant<int, 1>());
             } else {
@@ -704,7 +882,7 @@ static int mfma_cus() {
     return cus;
 }
 
-template <bool GU, int IRB, bool A8, bool TAB>
+template <bool GU, int IRB, bool A8, bool TAB, int FMT>
 static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
     const int nmax = GU ? (a.with_shared ? (a.with_routed ? max(a.F, a.Fs) : a.Fs) : a.F) : a.H;
     const int nb = (nmax + (GU ? 127 : 255)) / (GU ? 128 : 256);
@@ -713,27 +891,36 @@ static hipError_t launch_gemm_rb(const MfmaArgs &a, int shared_items, const char
     // one workgroup per CU, more if a workgroup's table would overflow
     long G = mfma_cus();
     if ((total_max + G - 1) / G > kMaxWorkPerWg) G = (total_max + kMaxWorkPerWg - 1) / kMaxWorkPerWg;
-    const size_t lds = 2 * (size_t)MfmaBuf<IRB>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB, A8, TAB>),
+    const size_t lds = 2 * (size_t)MfmaBuf<IRB, FMT>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>);
+    static_assert(2 * (size_t)MfmaBuf<IRB, FMT>::kBytes + kMaxWorkPerWg * sizeof(WorkDesc<16 * IRB>) <= 160 * 1024,
+                  "the chunk buffers fit the CU's LDS");
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&q4_mfma_kernel<GU, IRB, A8, TAB, FMT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipGetLastError();
     ProfScope prof(name, st);
-    q4_mfma_kernel<GU, IRB, A8, TAB><<<(int)G, kMfmaThreads, lds, st>>>(a);
+    q4_mfma_kernel<GU, IRB, A8, TAB, FMT><<<(int)G, kMfmaThreads, lds, st>>>(a);
     return hipGetLastError();
 }
 
-// the work items' row count (16 or 32) selects the kernel
+// the work items' row count (16 or 32) selects the kernel; MXFP4 items have at most 16
 template <bool GU>
 static hipError_t launch_gemm(const MfmaArgs &a, int shared_items, const char *name, hipStream_t st) {
-#define MOE_GEMM_CASE(A8, TAB)                                                                  \
-    if (!!a.act8 == A8 && (a.tab != nullptr) == TAB)                                            \
-        return a.item_rows > 16 ? launch_gemm_rb<GU, 2, A8, TAB>(a, shared_items, name, st)     \
-                                : launch_gemm_rb<GU, 1, A8, TAB>(a, shared_items, name, st);
-    MOE_GEMM_CASE(false, false)
-    MOE_GEMM_CASE(true, false)
-    MOE_GEMM_CASE(false, true)
-    MOE_GEMM_CASE(true, true)
+#define MOE_GEMM_CASE(A8, TAB, FMT)                                                                       \
+    if (!!a.act8 == A8 && (a.tab != nullptr) == TAB && a.fmt == FMT)                                      \
+        return a.item_rows > 16 ? launch_gemm_rb<GU, 2, A8, TAB, FMT>(a, shared_items, name, st)          \
+                                : launch_gemm_rb<GU, 1, A8, TAB, FMT>(a, shared_items, name, st);
+    MOE_GEMM_CASE(false, false, kFmtI4)
+    MOE_GEMM_CASE(true, false, kFmtI4)
+    MOE_GEMM_CASE(false, true, kFmtI4)
+    MOE_GEMM_CASE(true, true, kFmtI4)
+    MOE_GEMM_CASE(false, false, kFmtI3)
+    MOE_GEMM_CASE(true, false, kFmtI3)
+    MOE_GEMM_CASE(false, true, kFmtI3)
+    MOE_GEMM_CASE(true, true, kFmtI3)
 #undef MOE_GEMM_CASE
+    if (a.fmt == kFmtF4 && !a.act8 && a.item_rows <= 16)
+        return a.tab ? launch_gemm_rb<GU, 1, false, true, kFmtF4>(a, shared_items, name, st)
+                     : launch_gemm_rb<GU, 1, false, false, kFmtF4>(a, shared_items, name, st);
     return hipErrorInvalidValue;
 }
 
@@ -752,7 +939,8 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     it.n_items = a.n_items;
     it.with_union = a.union_in_prep;
     it.uni = a.uni;
-    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step, a.act8), none, it, "prep_x+items", st);
+    const int bf = a.fmt == kFmtF4;
+    e = launch_prep(prep_job(a.x, a.T, a.H, a.x_frag, a.x_step, a.act8, bf), none, it, "prep_x+items", st);
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + a.item_rows - 1) / a.item_rows : 0;
     if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
@@ -761,8 +949,8 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     ItemsJob no_items = it;
     no_items.items = nullptr;
     no_items.with_union = 0;
-    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step, a.act8) : none,
-                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step, a.act8) : none,
+    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step, a.act8, bf) : none,
+                    a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step, a.act8, bf) : none,
                     no_items, "prep_h", st);
     if (e != hipSuccess) return e;
     return launch_gemm<false>(a, shared_items, "ffn_down_mfma", st);

@@ -34,6 +34,9 @@ static int check_dims(const moe_layer *L) {
     if (!isfinite(L->routed_scale)) return MOE_EINVAL;
     if (L->n_experts > MOE_MAX_EXPERTS || L->top_k > MOE_MAX_TOPK) return MOE_EUNSUPPORTED;
     if (L->act_bits != 0 && L->act_bits != 16 && L->act_bits != 8) return MOE_EINVAL;
+    if (L->expert_fmt != MOE_FMT_INT4_G64 && L->expert_fmt != MOE_FMT_MXFP4 && L->expert_fmt != MOE_FMT_INT3_G64)
+        return MOE_EINVAL;
+    if (L->expert_fmt == MOE_FMT_MXFP4 && L->act_bits == 8) return MOE_EUNSUPPORTED;
     if (L->n_group < 0) return MOE_EINVAL;
     if (L->n_group > 1) {
         if (L->n_group > 64 || L->n_experts % L->n_group || L->n_experts / L->n_group < 2) return MOE_EINVAL;
@@ -155,12 +158,14 @@ Plan make_plan(const moe_layer &L, int T) {
         // fragment rows padded to whole 4-group chunks
         const size_t gh = mfma_groups_padded((int)H), gf = mfma_groups_padded((int)F),
                      gs = Fs ? mfma_groups_padded((int)Fs) : 0;
-        // (128 bytes per row and group; one fp32 step per row and 4-group chunk)
-        p.x_frag = take(Tz * gh * 128);
+        // (128 bytes per row and group, 256 for the MXFP4 path's bf16 terms; one fp32
+        // step per row and 4-group chunk)
+        const size_t gb = L.expert_fmt == MOE_FMT_MXFP4 ? 256 : 128;
+        p.x_frag = take(Tz * gh * gb);
         p.x_step = take(Tz * gh);
-        p.hr_frag = take(Tz * k * gf * 128);
+        p.hr_frag = take(Tz * k * gf * gb);
         p.hr_step = take(Tz * k * gf);
-        p.hs_frag = take(Tz * gs * 128);
+        p.hs_frag = take(Tz * gs * gb);
         p.hs_step = take(Tz * gs);
         p.max_items = mfma_max_items(p.max_units, (int)(Tz * k));
         p.items = take((size_t)p.max_items * 16);
@@ -249,6 +254,7 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     m.gu_out = f.gu_out;
     m.tab = f.tab;
     m.act8 = f.act8;
+    m.fmt = f.fmt;
     m.x = f.x;
     m.x_frag = at<uint8_t>(ws, p.x_frag);
     m.x_step = at<float>(ws, p.x_step);
@@ -279,7 +285,8 @@ static MfmaArgs mfma_args(const FfnArgs &f, const Plan &p, int E, int k, void *w
     m.E = E;
     m.max_units = f.max_units;
     m.max_rows = f.T * k;
-    m.item_rows = mfma_item_rows(m.max_rows, E);
+    // (MXFP4 items hold at most 16 rows: the bf16 activation tile of 32 would not fit the LDS)
+    m.item_rows = f.fmt == kFmtF4 ? 16 : mfma_item_rows(m.max_rows, E);
     m.max_items = p.max_items;
     m.with_routed = f.with_routed;
     m.with_shared = f.with_shared;
@@ -303,6 +310,7 @@ static FfnArgs ffn_args(const moe_layer &L, const Plan &p, const float *x, int T
     a.gu_out = gu_out;
     a.tab = nullptr;
     a.act8 = L.act_bits == 8 ? 1 : 0;
+    a.fmt = L.expert_fmt;
     a.xq = p.xq ? at<float>(ws, p.xq) : nullptr;
     a.rows_max = T * L.top_k;
     a.x = x;
@@ -347,7 +355,8 @@ static int check_tier(const moe_tier *t) {
 
 static TierArgs tier_args(const moe_layer &L, const moe_tier &t) {
     TierArgs a;
-    a.lay = tier_layout(L.hidden, L.ffn, L.n_experts, t.n_slots);
+    a.lay = tier_layout(L.hidden, L.ffn, L.n_experts, t.n_slots, L.expert_fmt);
+    a.fmt = L.expert_fmt;
     a.slots = static_cast<uint8_t *>(t.slots);
     a.state = static_cast<uint8_t *>(t.state);
     a.gate = L.gate;
@@ -601,12 +610,12 @@ int moe_layer_forward(const moe_layer *L, const float *x, int32_t T, void *out, 
 
 size_t moe_tier_slot_bytes(const moe_layer *L) {
     if (check_dims(L) != MOE_OK) return 0;
-    return tier_layout(L->hidden, L->ffn, L->n_experts, 1).slot;
+    return tier_layout(L->hidden, L->ffn, L->n_experts, 1, L->expert_fmt).slot;
 }
 
 size_t moe_tier_state_bytes(const moe_layer *L, int32_t n_slots) {
     if (check_dims(L) != MOE_OK || n_slots < 1 || n_slots > kTierMaxSlots) return 0;
-    return tier_layout(L->hidden, L->ffn, L->n_experts, n_slots).total;
+    return tier_layout(L->hidden, L->ffn, L->n_experts, n_slots, L->expert_fmt).total;
 }
 
 int moe_tier_init(const moe_layer *L, const moe_tier *tier, const int32_t *pins, int32_t n_pin,

@@ -22,6 +22,28 @@ __device__ __forceinline__ float gate_up_out(int mode, float g, float u) {
     return mode == kGuSwiglu ? g / (1.0f + expf(-g)) * u : (mode == kGuGate ? g : u);
 }
 
+// ---------------------------------------------------------------- expert formats
+// The stored layout of one N x K matrix (moe.h): code bytes and scale bytes per row.
+constexpr int kFmtI4 = MOE_FMT_INT4_G64, kFmtF4 = MOE_FMT_MXFP4, kFmtI3 = MOE_FMT_INT3_G64;
+__host__ __device__ constexpr size_t fmt_code_bytes(int fmt, size_t K) {
+    return fmt == kFmtI3 ? 3 * K / 8 : K / 2;
+}
+__host__ __device__ constexpr size_t fmt_scale_bytes(int fmt, size_t K) {
+    return fmt == kFmtF4 ? K / 32 : 4 * (K / 64);
+}
+// matrix e of a stack of N x K matrices
+__host__ __device__ inline moe_q4 fmt_stack_at(const moe_q4 &m, int fmt, int e, size_t N, size_t K) {
+    moe_q4 r;
+    r.q = m.q + (size_t)e * N * fmt_code_bytes(fmt, K);
+    r.s = static_cast<const uint8_t *>(m.s) + (size_t)e * N * fmt_scale_bytes(fmt, K);
+    return r;
+}
+// A UE8M0 exponent byte as the fp32 value 2^(e - 127) (2^-127 is subnormal; 255 is NaN).
+__device__ __forceinline__ float ue8m0_f32(uint32_t e) {
+    return e == 255u ? __uint_as_float(0x7FC00000u) : (e == 0u ? __uint_as_float(0x00400000u)
+                                                                : __uint_as_float(e << 23));
+}
+
 // ---------------------------------------------------------------- activation blocks
 // Both expert-FFN paths take activations as fixed point per block: x16 = rint(x * 2^n)
 // with n the largest integer for which max|x| * 2^n <= 32639 = 127 * 256 + 127 (so
@@ -149,6 +171,7 @@ struct FfnArgs {
     // residency tier's slots), or, when null, the stacked gate/up/down above
     const moe_q4 *tab;
     int act8;  // opt-in 8-bit activation blocks (moe_layer::act_bits == 8)
+    int fmt;   // expert weight format (kFmt*)
     float *xq;     // T <= kGemvMaxTokens with act8: x in 8-bit blocks (workspace [T][H])
     int rows_max;  // routed rows the batch can have (T * k)
     // Selection and union inside the gate/up launch (one token): every routed
@@ -193,6 +216,7 @@ struct MfmaArgs {
     int gu_out;     // as FfnArgs::gu_out
     const moe_q4 *tab;  // as FfnArgs::tab
     int act8;           // as FfnArgs::act8
+    int fmt;            // as FfnArgs::fmt
     int with_routed, with_shared;
     int union_in_prep;  // build the union (uni) before the work list, in the same workgroup
     UnionArgs uni;
@@ -239,10 +263,11 @@ struct TierLayout {
 
 __host__ __device__ inline size_t tier_align(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-__host__ __device__ inline TierLayout tier_layout(int H, int F, int E, int S) {
+__host__ __device__ inline TierLayout tier_layout(int H, int F, int E, int S, int fmt) {
     TierLayout t;
     size_t o = 0;
-    const size_t wq = (size_t)F * H / 2, ws = (size_t)F * (H / 64) * 4;  // one matrix's codes, scales
+    // one matrix's codes and scales (gate/up [F][H] and down [H][F] take the same bytes)
+    const size_t wq = (size_t)F * fmt_code_bytes(fmt, H), ws = (size_t)F * fmt_scale_bytes(fmt, H);
     t.gq = o; o = tier_align(o + wq, 256);
     t.gs = o; o = tier_align(o + ws, 256);
     t.uq = o; o = tier_align(o + wq, 256);
@@ -275,6 +300,7 @@ struct TierArgs {
     uint8_t *state;
     moe_q4 gate, up, down;  // the host backing store, stacked by expert id
     int H, F, n_pinned;
+    int fmt;                // expert weight format
 };
 
 struct TierPins {

@@ -49,23 +49,19 @@ __device__ __forceinline__ TierView tier_view(const TierArgs &a) {
 __device__ __forceinline__ void tier_point(const TierArgs &a, const TierView &v, int e, int s) {
     uint8_t *sl = a.slots + (size_t)s * a.lay.slot;
     v.tab[3 * e + 0].q = sl + a.lay.gq;
-    v.tab[3 * e + 0].s = reinterpret_cast<const float *>(sl + a.lay.gs);
+    v.tab[3 * e + 0].s = sl + a.lay.gs;
     v.tab[3 * e + 1].q = sl + a.lay.uq;
-    v.tab[3 * e + 1].s = reinterpret_cast<const float *>(sl + a.lay.us);
+    v.tab[3 * e + 1].s = sl + a.lay.us;
     v.tab[3 * e + 2].q = sl + a.lay.dq;
-    v.tab[3 * e + 2].s = reinterpret_cast<const float *>(sl + a.lay.ds);
+    v.tab[3 * e + 2].s = sl + a.lay.ds;
 }
 
 // expert e's matrices in the backing store (read over the host link; used only when no
 // slot is free, which the host-side checks rule out)
 __device__ __forceinline__ void tier_point_backing(const TierArgs &a, const TierView &v, int e) {
-    const size_t cq = (size_t)e * a.F * (a.H / 2), cs = (size_t)e * a.F * (a.H / 64);
-    v.tab[3 * e + 0].q = a.gate.q + cq;
-    v.tab[3 * e + 0].s = a.gate.s + cs;
-    v.tab[3 * e + 1].q = a.up.q + cq;
-    v.tab[3 * e + 1].s = a.up.s + cs;
-    v.tab[3 * e + 2].q = a.down.q + cq;
-    v.tab[3 * e + 2].s = a.down.s + cs;
+    v.tab[3 * e + 0] = fmt_stack_at(a.gate, a.fmt, e, a.F, a.H);
+    v.tab[3 * e + 1] = fmt_stack_at(a.up, a.fmt, e, a.F, a.H);
+    v.tab[3 * e + 2] = fmt_stack_at(a.down, a.fmt, e, a.H, a.F);
 }
 
 // ------------------------------------------------------------------ init
@@ -366,12 +362,14 @@ __global__ __launch_bounds__(256) void tier_copy_kernel(TierArgs a) {
     if (job >= v.hdr[1]) return;
     const int e = v.copies[2 * job], s = v.copies[2 * job + 1];
     uint8_t *sl = a.slots + (size_t)s * a.lay.slot;
-    const size_t cq = (size_t)e * a.F * (a.H / 2), cs = (size_t)e * a.F * (a.H / 64);
-    const size_t nq = (size_t)a.F * a.H / 2 / 16, ns = (size_t)a.F * (a.H / 64) * 4 / 16;
+    // every matrix of the three takes F * code bytes(H) and F * scale bytes(H), multiples of 16
+    const size_t nq = (size_t)a.F * fmt_code_bytes(a.fmt, a.H) / 16, ns = (size_t)a.F * fmt_scale_bytes(a.fmt, a.H) / 16;
+    const moe_q4 g = fmt_stack_at(a.gate, a.fmt, e, a.F, a.H), u = fmt_stack_at(a.up, a.fmt, e, a.F, a.H),
+                 d = fmt_stack_at(a.down, a.fmt, e, a.H, a.F);
     const uint4 *src[6] = {
-        reinterpret_cast<const uint4 *>(a.gate.q + cq), reinterpret_cast<const uint4 *>(a.gate.s + cs),
-        reinterpret_cast<const uint4 *>(a.up.q + cq), reinterpret_cast<const uint4 *>(a.up.s + cs),
-        reinterpret_cast<const uint4 *>(a.down.q + cq), reinterpret_cast<const uint4 *>(a.down.s + cs)};
+        reinterpret_cast<const uint4 *>(g.q), static_cast<const uint4 *>(g.s),
+        reinterpret_cast<const uint4 *>(u.q), static_cast<const uint4 *>(u.s),
+        reinterpret_cast<const uint4 *>(d.q), static_cast<const uint4 *>(d.s)};
     const size_t dst_off[6] = {a.lay.gq, a.lay.gs, a.lay.uq, a.lay.us, a.lay.dq, a.lay.ds};
     const size_t n16[6] = {nq, ns, nq, ns, nq, ns};
     const size_t stride = (size_t)gridDim.x * blockDim.x;

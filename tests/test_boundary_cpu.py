@@ -88,6 +88,9 @@ def call_forward(c, T=4, x=0x20000, out=0x30000, dtype=0, ws=0x40000, wsb=None):
     (dict(n_group=-1), M.MOE_EINVAL),
     (dict(act_bits=4), M.MOE_EINVAL),
     (dict(act_bits=-8), M.MOE_EINVAL),
+    (dict(expert_fmt=3), M.MOE_EINVAL),
+    (dict(expert_fmt=-1), M.MOE_EINVAL),
+    (dict(expert_fmt=M.MOE_FMT_MXFP4, act_bits=8), M.MOE_EUNSUPPORTED),
 ])
 def test_forward_validation_codes(kw, code):
     assert call_forward(_layer(**kw)) == code
@@ -237,3 +240,23 @@ def test_dense_validation_codes():
     assert fwd(ok, wsb=16) == M.MOE_EWORKSPACE
     assert fwd(ok, T=0) == M.MOE_OK
     assert lib.moe_dense_forward(None, 0x20000, 4, 0x30000, 0, 0x40000, 1 << 30, None) == M.MOE_EINVAL
+
+
+def test_format_workspace_and_tier_sizes():
+    """Per-format byte counts the host computes: the MXFP4 matrix-core path needs larger
+    activation fragments; a tier slot holds one expert in the layer's format."""
+    base = _layer(hidden=2048, ffn=512, shared_ffn=512, n_experts=64, top_k=8)
+    sizes = {}
+    for fmt in (M.MOE_FMT_INT4_G64, M.MOE_FMT_MXFP4, M.MOE_FMT_INT3_G64):
+        c = _layer(hidden=2048, ffn=512, shared_ffn=512, n_experts=64, top_k=8, expert_fmt=fmt)
+        sizes[fmt] = (ws_bytes(c, 64), ws_bytes(c, 4), M.lib().moe_tier_slot_bytes(ctypes.byref(c)))
+    assert sizes[M.MOE_FMT_INT4_G64][1] == sizes[M.MOE_FMT_MXFP4][1] == sizes[M.MOE_FMT_INT3_G64][1]
+    assert sizes[M.MOE_FMT_MXFP4][0] > sizes[M.MOE_FMT_INT4_G64][0] == sizes[M.MOE_FMT_INT3_G64][0]
+    H, F = 2048, 512
+    def slot(code, scale):  # six tensors, each rounded up to 256 bytes
+        r = lambda b: (b + 255) // 256 * 256
+        return 3 * (r(code) + r(scale))
+    assert sizes[M.MOE_FMT_INT4_G64][2] == slot(F * H // 2, F * H // 64 * 4)
+    assert sizes[M.MOE_FMT_MXFP4][2] == slot(F * H // 2, F * H // 32)
+    assert sizes[M.MOE_FMT_INT3_G64][2] == slot(F * 3 * H // 8, F * H // 64 * 4)
+    assert ws_bytes(base, 64) == sizes[M.MOE_FMT_INT4_G64][0]

@@ -141,6 +141,17 @@ def test_tier_glm_decode():
                  dtype=M.MOE_BF16)
 
 
+@pytest.mark.parametrize("fmt", [S.FMT_MXFP4, S.FMT_INT3], ids=["mxfp4", "int3"])
+def test_tier_other_formats(fmt):
+    """The tier over MXFP4 and int3-g64 experts: slots sized for the format, copies of
+    the format's bytes; GEMV (1-4 tokens) and matrix-core (9-40 tokens) batches."""
+    sh = S.custom(f"tier_{S.FMT_NAMES[fmt]}", hidden=320, n_experts=32, ffn=192, shared_ffn=64,
+                  top_k=4, tokens=40, bias_amp=0.05, router_std=1 / 16.0, expert_fmt=fmt)
+    d = S.make_layer(sh, seed=0)
+    st = run_sequence(sh, d, 40, [0, 9, 20, 31], [1, 3, 9, 40, 2, 16, 4, 24, 1])
+    assert st["misses"] > 0
+
+
 def test_tier_rejects_a_too_small_cache():
     sh = S.custom("tier_small", hidden=256, n_experts=64, ffn=128, shared_ffn=64, top_k=4, tokens=8)
     d = S.make_layer(sh, seed=0)

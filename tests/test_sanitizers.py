@@ -41,7 +41,7 @@ def test_abi_host_side_under_asan_ubsan(tmp_path):
     lib = str(tmp_path / "libmoe_san.so")
     san = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
-    _run([B.HIPCC] + B.FLAGS + san + [os.path.join(B.CSRC, s) for s in B.SOURCES] + ["-o", lib])
+    B.build(extra=san, out=lib)
     exe = str(tmp_path / "san_abi")
     _run([clang, "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
           os.path.join(HERE, "sanitize_abi_main.c"), lib, "-Wl,-rpath," + str(tmp_path), "-o", exe])
