@@ -54,20 +54,34 @@ WORKLOADS = {
                         "block, one int8 product per group)",
     "glm_verify16": "the GLM-shaped decode layer on 16 tokens per step (a multi-token verification "
                     "or small prefill chunk: 1-2 rows per union expert), fp32 out",
+    "glm_decode_int3": "glm_decode with int3-g64 experts (3-bit codes in two bit planes, fp32 scale "
+                       "per 64)",
+    "glm_decode_mxfp4": "glm_decode with MXFP4 experts (E2M1 codes, UE8M0 exponent per 32)",
+    "glm_prefill_int3": "glm_prefill with int3-g64 experts",
+    "glm_prefill_mxfp4": "glm_prefill with MXFP4 experts (bf16 matrix cores, two-term activations)",
 }
 DEFAULT_ORDER = ("glm_decode", "small_decode", "glm_verify16", "glm_prefill", "glm_prefill_act8",
-                 "glm_stack16", "glm_rows256")
+                 "glm_stack16", "glm_rows256", "glm_decode_int3", "glm_decode_mxfp4",
+                 "glm_prefill_int3", "glm_prefill_mxfp4")
 # resident layer copies cycled per step (enough distinct HBM to defeat the last-level cache)
 COPIES = {"glm_decode": 8, "small_decode": 8, "glm_prefill": 2, "glm_stack16": 16, "glm_rows256": 2,
-          "glm_prefill_act8": 2, "glm_verify16": 8}
+          "glm_prefill_act8": 2, "glm_verify16": 8, "glm_decode_int3": 8, "glm_decode_mxfp4": 8,
+          "glm_prefill_int3": 2, "glm_prefill_mxfp4": 2}
+# workload-name suffixes: the opt-in 8-bit activations, or another expert format
+SUFFIX_FMT = {"_int3": 2, "_mxfp4": 1}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def q4_bytes(n, k):
-    """int4 codes + fp32 gs64 scales of an [n][k] matrix."""
+def mat_bytes(fmt, n, k):
+    """Codes + scales of an [n][k] matrix: int4-gs64 (4 bits + fp32 per 64), MXFP4 (4 bits +
+    one byte per 32), int3-g64 (3 bits + fp32 per 64)."""
+    if fmt == 1:
+        return n * k // 2 + n * (k // 32)
+    if fmt == 2:
+        return n * 3 * k // 8 + n * (k // 64) * 4
     return n * k // 2 + n * (k // 64) * 4
 
 
@@ -90,7 +104,7 @@ _BANKS = {}
 def bank_for(sh):
     """The host expert bank of a shape (cached: the GLM-shaped workloads share one)."""
     from routed_int4_expert_amd import synth as S
-    key = (sh.bank or sh.name, sh.n_experts, sh.hidden, sh.ffn, sh.shared_ffn)
+    key = (sh.bank or sh.name, sh.n_experts, sh.hidden, sh.ffn, sh.shared_ffn, sh.expert_fmt)
     if key not in _BANKS:
         t0 = time.time()
         _BANKS[key] = S.Bank(sh, seed=0)
@@ -231,11 +245,16 @@ def run_workload(wl, args, dev):
 
     import dataclasses
     act_bits = 8 if wl.endswith("_act8") else 0
-    base_wl = wl[:-len("_act8")] if act_bits else wl
+    fmt = next((f for suf, f in SUFFIX_FMT.items() if wl.endswith(suf)), 0)
+    base_wl = wl
+    for suf in ("_act8",) + tuple(SUFFIX_FMT):
+        if base_wl.endswith(suf):
+            base_wl = base_wl[:-len(suf)]
     if base_wl == "glm_verify16":
         sh = dataclasses.replace(S.SHAPES["glm_decode"], tokens=16)
     else:
         sh = S.SHAPES[base_wl]
+    sh = dataclasses.replace(sh, expert_fmt=fmt)
     T, H, F, Fs, E = sh.tokens, sh.hidden, sh.ffn, sh.shared_ffn, sh.n_experts
     stack = wl == "glm_stack16"
     nlay = COPIES[wl] if args.layers is None else (sh.layers if stack else args.layers)
@@ -249,7 +268,7 @@ def run_workload(wl, args, dev):
         npool = max(1, 64 // T)
         xs_host = S.tokens(sh, npool * T, seed=0, pool=0)
     xpool = torch.from_numpy(xs_host).to(dev)
-    out_bf16 = wl == "glm_decode"
+    out_bf16 = base_wl == "glm_decode"
     out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
     ws = layers[0].workspace(T, dev)
     per_step = nlay if stack else 1
@@ -389,11 +408,11 @@ def run_workload(wl, args, dev):
     # gate/up: every unit's codes + scales, x read, h written; down: codes + scales, h read, y written
     units = {
         "gateup": dict(name="ffn_gateup" if gemv else "ffn_gateup_mfma",
-                       bytes=(n_uniq.mean() * 2 * q4_bytes(F, H) + 2 * q4_bytes(Fs, H) + T * H * 4
+                       bytes=(n_uniq.mean() * 2 * mat_bytes(fmt, F, H) + 2 * mat_bytes(fmt, Fs, H) + T * H * 4
                               + (rows.mean() * F + T * Fs) * 4),
                        flops=2.0 * 2 * H * (F * rows.mean() + Fs * T)),
         "down": dict(name="ffn_down" if gemv else "ffn_down_mfma",
-                     bytes=(n_uniq.mean() * q4_bytes(H, F) + q4_bytes(H, Fs)
+                     bytes=(n_uniq.mean() * mat_bytes(fmt, H, F) + mat_bytes(fmt, H, Fs)
                             + (rows.mean() * F + T * Fs) * 4 + (rows.mean() + T) * H * 4),
                      flops=2.0 * H * (F * rows.mean() + Fs * T)),
     }
@@ -426,7 +445,12 @@ def run_workload(wl, args, dev):
         # (carried as two int8 limbs; one int8 code with the opt-in 8-bit path) with exact
         # int32 group sums (v_dot4 in the decode GEMV for T <= 4, int8 matrix cores for
         # T > 4), then fp32 accumulation
-        "dtype": "i4xi8-i32-f32acc" if act_bits else "i4xfx16-i32-f32acc",
+        # (int3 codes likewise, and doubled E2M1 values on the GEMV; MXFP4 above 4 tokens:
+        # exact bf16 weights times two bf16 terms per activation on the bf16 matrix cores,
+        # fp32 accumulation)
+        "dtype": ("i4xi8-i32-f32acc" if act_bits else
+                  {0: "i4xfx16-i32-f32acc", 2: "i3xfx16-i32-f32acc"}.get(fmt) or
+                  ("e2m1xfx16-i32-f32acc" if T <= 4 else "e2m1xbf16x2-f32acc")),
         "data": "synthetic",
         "config": {
             "workload": f"{wl}: {WORKLOADS[wl]}",

@@ -181,11 +181,12 @@ int moe_union(const moe_layer *L, const int32_t *ids, const int32_t *keff, int32
  * per block of consecutive values (32 for T <= 4, 256 for larger T): one rounding of
  * less than max|x| / 32639 per value, none for values with at most 15 significant
  * bits relative to the block's largest; the dot products are exact int32 sums.
- * int3-g64 experts enter the same way.  MXFP4 experts: the E2M1 values times their
- * block's power of two are exact in fp32 and bf16; for T <= 4 they multiply the fp32
- * activations with fp32 accumulation, above that each activation is split into two
- * bf16 terms (x = hi + lo + r with |r| <= 2^-16 |x|) for bf16 matrix-core products
- * accumulated in fp32.
+ * int3-g64 experts enter the same way, and so do MXFP4 experts for T <= 4 (their doubled
+ * E2M1 values are integers in [-12, 12]; the 32-element activation blocks match the
+ * exponent blocks).  Above T = 4 MXFP4 experts enter as their exact bf16 values (E2M1
+ * times the block's power of two) and each activation as two bf16 terms
+ * (x = hi + lo + r with |r| <= 2^-16 |x|), for bf16 matrix-core products accumulated
+ * in fp32.
  * Inputs n_uniq/uniq/off/row_tok as produced by moe_union (device).
  * Output: y_rows [T*k][H] fp32; rows past off[E] are left untouched. */
 int moe_expert_ffn(const moe_layer *L, const float *x, int32_t T, const int32_t *n_uniq,

@@ -28,10 +28,12 @@
 // low-bit plane and one word of the sign plane; shift and mask give the unsigned
 // u = c + 4 in [0, 7] of four elements of one parity per step, in the element order
 // above, and sum(c x16) = 256 sum(u hi) + sum(u lo) - 4 sum(x16).
-// MXFP4 codes: a lane's 16-byte load is one 32-element block with one UE8M0 exponent.
-// The activations are staged as plain fp32 (36 floats per 32-element chunk); the E2M1
-// values come out of the hardware's fp4 -> fp32 conversion (exact), multiply x in
-// fp32, and the block's dot product is scaled by 2^(e - 127).
+// MXFP4 codes: a lane's 16-byte load is one 32-element block with one UE8M0 exponent,
+// matching the 32-element activation chunk.  Every E2M1 value doubled is an integer
+// 2v in [-12, 12]: two byte permutes (a table of the magnitudes, one of their
+// negatives) indexed by the code's low three bits, and a select on its sign bit, give
+// 2v as four signed bytes of one parity per word; sum(2v x16) is an exact int32 sum,
+// times the chunk's step, the block's 2^(e - 127) and 1/2.
 //
 // The gate/up kernel finishes with the fused SiLU(g) * u epilogue and writes
 // h [rows][F]; the down kernel writes the unweighted y [rows][H].  Each output
@@ -51,12 +53,7 @@ namespace moe {
 // and 8 sum(x16) (int32) at dword 17, then padding: the 16-byte reads of 8
 // consecutive lanes (80 bytes apart) hit distinct banks.
 constexpr int kChunkPitch = 20;
-constexpr int kChunkPitchF = 36;     // fp32 staging (MXFP4): 32 values and padding
 constexpr float kX16Max = 32639.0f;  // 127 * 256 + 127: both bytes of x16 stay in [-128, 127]
-
-// dwords of LDS per 32-element chunk of a staged row
-template <int FMT>
-constexpr int chunk_pitch() { return FMT == kFmtF4 ? kChunkPitchF : kChunkPitch; }
 
 // the value of each lane's DPP source lane (CTRL: a quad_perm or row_ror control, for
 // which every source lane is in the same row)
@@ -103,30 +100,31 @@ __device__ __forceinline__ int dot32_i3(const uint4 q, const uint4 *xv) {
     return (ah << 8) + al;  // |.| < 2^23: 32 products of at most 7 * 32639
 }
 
-// sum over the 32 E2M1 values of one block times the fp32 chunk px (32 floats), in
-// fp32: the conversion is exact (a value of at most 2 significant bits, scale 1)
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot32_f4(const uint4 q, const float *px) {
+// sum over the 32 E2M1 codes of one block of 2v_i * x16_i (2v the doubled value, an
+// integer in [-12, 12]), the chunk staged as 4 uint4 of byte limbs.  Per word: the low
+// three bits of each code select its doubled magnitude from {0, 1, 2, 3, 4, 6, 8, 12}
+// (one byte permute) and its negative (another); the sign bit, spread to a byte mask by a
+// shift and a multiply by 255, picks one of the two (bit select).
+__device__ __forceinline__ int dot32_f4(const uint4 q, const uint4 *xv) {
+    constexpr uint32_t kPosLo = 0x03020100u, kPosHi = 0x0C080604u;  // 0, 1, 2, 3 | 4, 6, 8, 12
+    constexpr uint32_t kNegLo = 0xFDFEFF00u, kNegHi = 0xF4F8FAFCu;  // their negatives
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-    const float4 *x4 = reinterpret_cast<const float4 *>(px);
-    float s0 = 0.f, s1 = 0.f;
+    int ah = 0, al = 0;
 #pragma unroll
     for (int d = 0; d < 4; d++) {
-        const float4 xa = x4[2 * d], xb = x4[2 * d + 1];
-        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 0);  // elements 8d, 8d+1
-        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
-        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
-        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
-        s0 = fmaf(v0.x, xa.x, s0);
-        s1 = fmaf(v0.y, xa.y, s1);
-        s0 = fmaf(v1.x, xa.z, s0);
-        s1 = fmaf(v1.y, xa.w, s1);
-        s0 = fmaf(v2.x, xb.x, s0);
-        s1 = fmaf(v2.y, xb.y, s1);
-        s0 = fmaf(v3.x, xb.z, s0);
-        s1 = fmaf(v3.y, xb.w, s1);
+        const uint32_t se = wd[d] & 0x07070707u, so = (wd[d] >> 4) & 0x07070707u;
+        const uint32_t me = ((wd[d] >> 3) & 0x01010101u) * 0xFFu, mo = ((wd[d] >> 7) & 0x01010101u) * 0xFFu;
+        const uint32_t pe = __builtin_amdgcn_perm(kPosHi, kPosLo, se), ne = __builtin_amdgcn_perm(kNegHi, kNegLo, se);
+        const uint32_t po = __builtin_amdgcn_perm(kPosHi, kPosLo, so), no = __builtin_amdgcn_perm(kNegHi, kNegLo, so);
+        const uint32_t ve = (ne & me) | (pe & ~me);  // elements 8d, 8d+2, 8d+4, 8d+6
+        const uint32_t vo = (no & mo) | (po & ~mo);  // elements 8d+1, 8d+3, 8d+5, 8d+7
+        const uint4 x = xv[d];
+        ah = __builtin_amdgcn_sdot4((int)ve, (int)x.x, ah, false);
+        ah = __builtin_amdgcn_sdot4((int)vo, (int)x.y, ah, false);
+        al = __builtin_amdgcn_sdot4((int)ve, (int)x.z, al, false);
+        al = __builtin_amdgcn_sdot4((int)vo, (int)x.w, al, false);
     }
-    return s0 + s1;
+    return (ah << 8) + al;  // |.| < 2^24: 32 products of at most 12 * 32639
 }
 
 // Sum over each group of LPR lanes, in a fixed order (deterministic); the group's
@@ -321,40 +319,15 @@ __device__ __forceinline__ void stage_commit(const StageBatch &sb, float *xs, in
     }
 }
 
-// The fp32 staging of the MXFP4 path: each 8-element item copied to its place in the
-// row's chunks (36 floats per chunk, items at 0, 8, 16, 24).
-__device__ __forceinline__ void stage_commit_f32(const StageBatch &sb, float *xs, int rowpitch, int K,
-                                                 int n8, int i0, int nt) {
-#pragma unroll
-    for (int b = 0; b < kStageBatch; b++) {
-        const int i = i0 + b * nt;
-        if (i >= n8) continue;
-        const int r = i / (K / 8), g = i % (K / 8);
-        float4 *dst = reinterpret_cast<float4 *>(xs + (size_t)r * rowpitch + (g / 4) * kChunkPitchF + (g % 4) * 8);
-        dst[0] = sb.v[b][0];
-        dst[1] = sb.v[b][1];
-    }
-}
-
-template <int FMT>
-__device__ __forceinline__ void stage_commit_fmt(const StageBatch &sb, float *xs, int rowpitch, int K,
-                                                 int n8, int i0, int nt) {
-    if constexpr (FMT == kFmtF4)
-        stage_commit_f32(sb, xs, rowpitch, K, n8, i0, nt);
-    else
-        stage_commit(sb, xs, rowpitch, K, n8, i0, nt);
-}
-
 // The thread's batches from item `first` on (its number among the nt threads, for a
 // whole staging).
-template <int FMT>
 __device__ __forceinline__ void stage_rows(float *xs, int rowpitch, const float *xin,
                                            const int32_t *rt, int rc, int R, int K, int first, int nt) {
     const int n8 = R * (K / 8);
     for (int i0 = first; i0 < n8; i0 += kStageBatch * nt) {
         StageBatch sb;
         stage_issue(sb, xin, rt, rc, K, n8, i0, nt);
-        stage_commit_fmt<FMT>(sb, xs, rowpitch, K, n8, i0, nt);
+        stage_commit(sb, xs, rowpitch, K, n8, i0, nt);
     }
 }
 
@@ -375,7 +348,7 @@ struct GemvShape {
 template <int LPR, int RM, bool GU, int FMT>
 __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit, int bx) {
     using S = GemvShape<LPR, RM, GU>;
-    constexpr int kPitch = chunk_pitch<FMT>();
+    constexpr int kPitch = kChunkPitch;
     extern __shared__ float xs[];  // [RM][C * kPitch] (+ selection and union, when fused)
     const int H = a.H;
 
@@ -388,7 +361,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         if (threadIdx.x < kWave)
             select_union_one(a, lds, bx == 0 && unit == 0);
         else
-            stage_rows<FMT>(xs, (H / 32) * kPitch, a.x, nullptr, 0, 1, H, (int)threadIdx.x - kWave,
+            stage_rows(xs, (H / 32) * kPitch, a.x, nullptr, 0, 1, H, (int)threadIdx.x - kWave,
                             blockDim.x - kWave);
         __syncthreads();
         const int k = a.sel.k, E = a.sel.E;
@@ -513,8 +486,8 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         StageBatch sb0;
         stage_issue(sb0, xin, rt, 0, K, n80, tid, blockDim.x);
         load_step(0, q, sc);
-        stage_commit_fmt<FMT>(sb0, xs, rowpitch, K, n80, tid, blockDim.x);
-        stage_rows<FMT>(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x);
+        stage_commit(sb0, xs, rowpitch, K, n80, tid, blockDim.x);
+        stage_rows(xs, rowpitch, xin, rt, 0, min(RM, nrows), K, tid + kStageBatch * blockDim.x, blockDim.x);
         __syncthreads();
     }
 
@@ -522,7 +495,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
         const int R = min(RM, nrows - rc);
         if (rc > 0) {
             __syncthreads();  // previous rows fully consumed
-            stage_rows<FMT>(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x);
+            stage_rows(xs, rowpitch, xin, rt, rc, R, K, tid, blockDim.x);
             __syncthreads();
         }
 
@@ -549,16 +522,7 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
                 for (int r = 0; r < RM; r++) {
                     if (r < R) {
                         const float *px = xs + r * rowpitch + c * kPitch;
-                        if constexpr (FMT == kFmtF4) {
-#pragma unroll
-                            for (int f = 0; f < S::NF; f++)
-#pragma unroll
-                                for (int m = 0; m < S::NM; m++) {
-                                    const float blk = ue8m0_f32(__float_as_uint(scc[f][m]));
-                                    acc[f][m][r] = fmaf(blk, dot32_f4(qc[f][m], px), acc[f][m][r]);
-                                    __builtin_amdgcn_sched_barrier(0);
-                                }
-                        } else {
+                        {
                             uint4 xv[4];
 #pragma unroll
                             for (int v = 0; v < 4; v++) xv[v] = *reinterpret_cast<const uint4 *>(px + 4 * v);
@@ -569,10 +533,16 @@ __device__ __forceinline__ void gemv_body(const FfnArgs &a, int passes, int unit
                             for (int f = 0; f < S::NF; f++)
 #pragma unroll
                                 for (int m = 0; m < S::NM; m++) {
-                                    // sum(q x16), exact (int3: sum((c + 4) x16) - 4 sum(x16))
-                                    const int iv = FMT == kFmtI3 ? dot32_i3(qc[f][m], xv) - (c8 >> 1)
-                                                                 : dot32_i8(qc[f][m], xv) - c8;
-                                    acc[f][m][r] = fmaf(scc[f][m] * sx, (float)iv, acc[f][m][r]);
+                                    // sum(q x16), exact (int3: sum((c + 4) x16) - 4 sum(x16); MXFP4:
+                                    // sum(2v x16), the block scale halved)
+                                    if constexpr (FMT == kFmtF4) {
+                                        const float blk = ue8m0_f32(__float_as_uint(scc[f][m])) * 0.5f;
+                                        acc[f][m][r] = fmaf(blk * sx, (float)dot32_f4(qc[f][m], xv), acc[f][m][r]);
+                                    } else {
+                                        const int iv = FMT == kFmtI3 ? dot32_i3(qc[f][m], xv) - (c8 >> 1)
+                                                                     : dot32_i8(qc[f][m], xv) - c8;
+                                        acc[f][m][r] = fmaf(scc[f][m] * sx, (float)iv, acc[f][m][r]);
+                                    }
                                     // one row at a time: keeps the unpacked codes of a single row live
                                     __builtin_amdgcn_sched_barrier(0);
                                 }
@@ -671,7 +641,7 @@ static int device_cus() {
 template <int LPR, int RM, bool GU, int FMT>
 static hipError_t launch_one(const FfnArgs &a, int N, int K, hipStream_t st) {
     using S = GemvShape<LPR, RM, GU>;
-    size_t lds = (size_t)RM * (K / 32) * chunk_pitch<FMT>() * sizeof(float);
+    size_t lds = (size_t)RM * (K / 32) * kChunkPitch * sizeof(float);
     if (GU && RM == 1 && a.fuse_select) lds += select_lds_words(a.sel.E, a.sel.T, a.sel.k) * sizeof(uint32_t);
     if (lds > 64 * 1024) {
         // raise the dynamic-LDS cap for this kernel; the launch itself reports a real failure

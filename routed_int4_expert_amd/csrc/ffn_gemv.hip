@@ -8,7 +8,8 @@ namespace moe {
 template hipError_t gemv_dispatch<kFmtI4>(bool, const FfnArgs &, int, int, int, hipStream_t);
 
 int rows_per_pass(int T, int K, int fmt) {
-    const size_t row_bytes = (size_t)(K / 32) * (fmt == kFmtF4 ? kChunkPitchF : kChunkPitch) * sizeof(float);
+    (void)fmt;  // every format stages the same 16-bit chunks
+    const size_t row_bytes = (size_t)(K / 32) * kChunkPitch * sizeof(float);
     int rm = T >= 3 ? 4 : (T == 2 ? 2 : 1);
     while (rm > 1 && (size_t)rm * row_bytes > 160 * 1024) rm >>= 1;
     return rm;

@@ -492,19 +492,19 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             const int e = __builtin_amdgcn_readfirstlane(d.e);
             const int nb0 = __builtin_amdgcn_readfirstlane(d.nb0);
             int K, N;
-            moe_q4 m0, m1;
             if (GU) {
                 K = a.H;
                 N = e >= 0 ? a.F : a.Fs;
                 if (TAB && e >= 0) {  // the residency tier's slots
-                    m0 = a.tab[3 * e];
-                    m1 = a.tab[3 * e + 1];
+                    qb0 = a.tab[3 * e].q;     sb0 = static_cast<const uint8_t *>(a.tab[3 * e].s);
+                    qb1 = a.tab[3 * e + 1].q; sb1 = static_cast<const uint8_t *>(a.tab[3 * e + 1].s);
                 } else if (e >= 0) {
-                    m0 = fmt_stack_at(a.gate, FMT, e, a.F, a.H);
-                    m1 = fmt_stack_at(a.up, FMT, e, a.F, a.H);
+                    const size_t gq = (size_t)e * a.F * fmt_code_bytes(FMT, a.H), gs = (size_t)e * a.F * fmt_scale_bytes(FMT, a.H);
+                    qb0 = a.gate.q + gq; sb0 = static_cast<const uint8_t *>(a.gate.s) + gs;
+                    qb1 = a.up.q + gq;   sb1 = static_cast<const uint8_t *>(a.up.s) + gs;
                 } else {
-                    m0 = a.sh_gate;
-                    m1 = a.sh_up;
+                    qb0 = a.sh_gate.q; sb0 = static_cast<const uint8_t *>(a.sh_gate.s);
+                    qb1 = a.sh_up.q;   sb1 = static_cast<const uint8_t *>(a.sh_up.s);
                 }
                 abase = a.x_frag;
                 nbase = a.x_step;
@@ -512,25 +512,26 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
                 K = e >= 0 ? a.F : a.Fs;
                 N = a.H;
                 if (e >= 0) {
-                    if constexpr (TAB) m0 = a.tab[3 * e + 2];
-                    else m0 = fmt_stack_at(a.down, FMT, e, a.H, a.F);
+                    if constexpr (TAB) {
+                        qb0 = a.tab[3 * e + 2].q; sb0 = static_cast<const uint8_t *>(a.tab[3 * e + 2].s);
+                    } else {
+                        const size_t dq = (size_t)e * a.H * fmt_code_bytes(FMT, a.F), ds = (size_t)e * a.H * fmt_scale_bytes(FMT, a.F);
+                        qb0 = a.down.q + dq; sb0 = static_cast<const uint8_t *>(a.down.s) + ds;
+                    }
                     abase = a.hr_frag;
                     nbase = a.hr_step;
                 } else {
-                    m0 = a.sh_down;
+                    qb0 = a.sh_down.q; sb0 = static_cast<const uint8_t *>(a.sh_down.s);
                     abase = a.hs_frag;
                     nbase = a.hs_step;
                 }
-                m1 = m0;
+                qb1 = qb0;
+                sb1 = sb0;
             }
-            qb0 = m0.q;
-            qb1 = m1.q;
-            sb0 = static_cast<const uint8_t *>(m0.s);
-            sb1 = static_cast<const uint8_t *>(m1.s);
             NG = K / 64;
             const int NGp = mfma_groups_padded(K);
             qlast = (uint32_t)(K / 2 - 16);
-            const uint32_t rowq = (uint32_t)fmt_code_bytes(FMT, K), rows_ = (uint32_t)fmt_scale_bytes(FMT, K);
+            const uint32_t rowq = (uint32_t)fmt_code_bytes(FMT, K), rows_ = FMT == kFmtF4 ? (uint32_t)(K / 32) : (uint32_t)NG;
             if constexpr (FMT == kFmtI3) {
                 // code lane t % 8: the low plane of group 4c + t % 8 (16 B, lanes 0-3) or the
                 // sign plane of group 4c + t % 8 - 4 (8 B, lanes 4-7); qlast: plane start
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void q4_mfma_kernel(MfmaArgs a) {
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    v.s[i] = reinterpret_cast<const float *>(((i & 1) ? sb1 : sb0) + so[i])[sg];
+                    v.s[i] = reinterpret_cast<const float *>((i & 1) ? sb1 : sb0)[so[i] + sg];
             }
             // the second row block's rows only if the item has them (else the registers
             // keep older values, which no compute wave reads)

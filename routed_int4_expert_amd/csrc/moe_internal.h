@@ -38,10 +38,12 @@ __host__ __device__ inline moe_q4 fmt_stack_at(const moe_q4 &m, int fmt, int e, 
     r.s = static_cast<const uint8_t *>(m.s) + (size_t)e * N * fmt_scale_bytes(fmt, K);
     return r;
 }
-// A UE8M0 exponent byte as the fp32 value 2^(e - 127) (2^-127 is subnormal; 255 is NaN).
+// A UE8M0 exponent byte as the fp32 value 2^(e - 127): the bits e << 23, plus bit 22 for
+// e = 0 (2^-127 is the subnormal 0x00400000) and for e = 255 (NaN 0x7FC00000 instead of
+// infinity).  Integer operations only, no branch.
 __device__ __forceinline__ float ue8m0_f32(uint32_t e) {
-    return e == 255u ? __uint_as_float(0x7FC00000u) : (e == 0u ? __uint_as_float(0x00400000u)
-                                                                : __uint_as_float(e << 23));
+    const uint32_t edge = ((e + 1u) & 0xFFu) <= 1u ? 1u : 0u;  // e is 0 or 255
+    return __uint_as_float((e << 23) | (edge << 22));
 }
 
 // ---------------------------------------------------------------- activation blocks
