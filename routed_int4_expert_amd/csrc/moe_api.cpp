@@ -420,8 +420,10 @@ int layer_forward_run(const moe_layer *L, const float *x, int32_t T, void *out, 
     FfnArgs a = ffn_args(*L, p, x, T, n_uniq, uniq, off, row_tok, y_routed, ws);
     if (sel_in_ffn) {
         e = run_logits(*L, p, x, T, ws, st);
-    } else if (T <= kSelectUnionTokens) {
-        // small batch: selection and union in one workgroup
+    } else if (T <= kSelectUnionTokens && T <= kRouterGemvTokens) {
+        // small batch: selection and union in one workgroup, from the gates and keys the
+        // one-slice router wrote (with a sliced router, one workgroup summing every
+        // token's partial logits would take longer than per-token selection workgroups)
         e = run_logits(*L, p, x, T, ws, st);
         if (e == hipSuccess)
             e = launch_select_union(select_args(*L, p, T, ids, w, keff, ws),

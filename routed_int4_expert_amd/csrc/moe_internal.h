@@ -83,7 +83,7 @@ __device__ __forceinline__ int act_shift(uint32_t mb, const ActRule &r) {
 // experts per workgroup with a split over H so small batches still cover the chip.
 constexpr int kRouterTile = 64;
 constexpr int kRouterKC = 64;  // H elements staged per LDS step
-constexpr int kRouterGemvTokens = 8;  // at most this many tokens: one wave per expert instead
+constexpr int kRouterGemvTokens = 8;  // at most this many tokens: one workgroup per expert instead
 
 struct RouterSplit {
     int S;       // number of H slices
