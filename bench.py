@@ -506,12 +506,14 @@ def _device_address(t):
     return p.value
 
 
-def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
+def run_tier(args, dev, n_layers=4, n_slots=200, n_pin=64):
     """Decode through n_layers GLM-shaped layers whose routed experts (5.4 GB each) live in
     pinned host memory, each layer with a residency tier of n_slots HBM slots (n_pin pinned,
-    chosen from a usage warm-up).  One token per step, Zipf-skewed routing with top-p 0.7.
-    Timed without and with router-lookahead prefetch (layer l+1's router on layer l's
-    input, on a copy stream), and with every expert resident in HBM for comparison."""
+    chosen from a usage warm-up).  200 of 256 slots per layer is the share of a 370 GB
+    expert bank that 288 GB of HBM holds.  One token per step, Zipf-skewed routing with
+    top-p 0.7.  Timed without and with router-lookahead prefetch (layer l+1's router on
+    layer l's input, on a copy stream that runs beside layer l's forward), and with every
+    expert resident in HBM for comparison."""
     import dataclasses
     import torch
     import routed_int4_expert_amd as M
@@ -538,7 +540,9 @@ def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
         res_layers.append(M.Layer(S.layer_params(sh), rts))
     log(f"glm_tier: {n_layers} layers in pinned host memory ({n_layers * 5.46:.1f} GB) and resident "
         f"copies ready in {time.time() - t0:.1f} s")
-    npool = 64
+    # a fresh token every step (no token repeats within a timed run): the experts a step
+    # needs are not the ones a recent step already brought in
+    npool = 1024
     xs = torch.from_numpy(S.tokens(sh, npool, seed=0)).to(dev)
     hbuf = torch.empty((T, H), dtype=torch.float32, device=dev)
     xbuf = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(n_layers)]
@@ -554,9 +558,12 @@ def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
     def step(i, fwd_of, prefetch=False):
         x = xs[i % npool:i % npool + 1]
         M.moe_residual_rmsnorm(x, None, h_out=hbuf, x_out=xbuf[0])
+        done = None  # the copy stream's event after layer l's own prefetch
         for l in range(n_layers):
             if l > 0:
                 M.moe_residual_rmsnorm(hbuf, out, h_out=hbuf, x_out=xbuf[l])
+            if prefetch and done is not None:
+                comp.wait_event(done)  # layer l's prefetch, not the one enqueued below
             if prefetch and l + 1 < n_layers:
                 ev = torch.cuda.Event()
                 ev.record(comp)
@@ -564,9 +571,11 @@ def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
                 with torch.cuda.stream(copy):
                     M.moe_route(layers[l + 1], xbuf[l], pid, pw, pk, ws=ws2, stream=copy)
                     tiers[l + 1].prefetch(pid, pk, stream=copy)
-            if prefetch and l > 0:
-                comp.wait_stream(copy)
+                done = torch.cuda.Event()
+                done.record(copy)
             fwd_of(l, xbuf[l])
+        if prefetch:
+            comp.wait_stream(copy)
 
     def tier_fwd(l, x):
         tiers[l].forward(x, out=out, ws=ws)
@@ -593,14 +602,15 @@ def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
         for l in range(n_layers):
             tiers[l].init(pins[l])
         torch.cuda.synchronize()
-        for i in range(args.warmup):
-            step(1000 + i, tier_fwd, prefetch=(mode == "prefetch"))
+        # untimed steps that fill the cache past the pinned store (steady state)
+        for i in range(max(args.warmup, 96)):
+            step(200 + i, tier_fwd, prefetch=(mode == "prefetch"))
         torch.cuda.synchronize()
         st0 = [t.read_state() for t in tiers]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(K):
-            step(2000 + i, tier_fwd, prefetch=(mode == "prefetch"))
+            step(400 + i, tier_fwd, prefetch=(mode == "prefetch"))
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / K
@@ -618,7 +628,7 @@ def run_tier(args, dev, n_layers=4, n_slots=64, n_pin=16):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(K):
-        step(2000 + i, res_fwd)
+        step(400 + i, res_fwd)
     e1.record()
     torch.cuda.synchronize()
     ms_res = e0.elapsed_time(e1) / K

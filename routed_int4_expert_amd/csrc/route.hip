@@ -1,9 +1,10 @@
 // route.hip -- steps 1 and 2 of the MoE layer on gfx950: router logits and
 // noaux_tc sigmoid selection ("MoE 路由与专家流式加载" §1.1, §1.2).
 //
-// Logits, few tokens (T <= 8): one wave per expert streams the expert's router
-// row once (lanes across H) and applies it to every token, accumulating in fp64
-// (fp32 x fp32 products are exact in fp64).
+// Logits, few tokens (T <= 8): one workgroup per expert streams the expert's router
+// row once (four waves across H) and applies it to every token, accumulating in fp64
+// (fp32 x fp32 products are exact in fp64); the logits are complete, so it also
+// writes each one's sigmoid gate and choice key for the selection.
 // Logits, more tokens: each workgroup owns a 64-token x 64-expert tile and one
 // slice of H; fp32 tiles of x and Wr are staged through LDS and the fp64 matrix
 // cores accumulate their exact products.  The per-slice partial sums go to the
