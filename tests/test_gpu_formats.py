@@ -130,3 +130,79 @@ def test_mxfp4_block_exponents_and_nan(T):
     ref = R.layer_forward(R.Layer(bad), x)
     assert np.isnan(ref).all()
     assert np.isnan(out.cpu().numpy()).all()
+
+
+# ------------------------------------------------------------------ GLM-sized layers
+@pytest.fixture(scope="module", params=FMTS, ids=FMT_IDS)
+def glm_fmt_bank(request):
+    fmt = request.param
+    sh = S.custom("glm_fmt", **{k: getattr(S.SHAPES["glm_decode"], k) for k in (
+        "hidden", "n_experts", "ffn", "shared_ffn", "top_k", "top_p", "norm_topk", "routed_scale",
+        "router_std", "bias_amp")}, bank="glm", expert_fmt=fmt)
+    say(f"generating the GLM-shaped {S.FMT_NAMES[fmt]} expert bank (257 experts)")
+    return fmt, S.Bank(sh, seed=0)
+
+
+def _glm_fmt_layer(base, fmt, bank):
+    import dataclasses
+    sh = dataclasses.replace(S.SHAPES[base], expert_fmt=fmt)
+    return sh, S.make_layer(sh, seed=0, bank=bank)
+
+
+@pytest.mark.timeout(600)
+def test_glm_decode_and_verify_formats(glm_fmt_bank):
+    """The GLM-shaped layer (H 6144, 256 experts of F 2048, top-8) in each format, as the
+    bench runs it: one-token decode on three token pools (the GEMV with the fused
+    selection) and a 16-token batch (matrix cores), every output against the oracle."""
+    fmt, bank = glm_fmt_bank
+    sh, d = _glm_fmt_layer("glm_decode", fmt, bank)
+    layer = M.Layer.from_host(d, DEV)
+    Lr = R.Layer(d)
+    for pool in range(3):
+        x = S.make_batch(sh, d, seed=0, pool=pool)
+        xd = torch.from_numpy(x).to(DEV)
+        check_routing(d, layer, x, xd, sh)
+        out = M.moe_layer_forward(layer, xd)
+        torch.cuda.synchronize()
+        rel, mx = assert_close(out.cpu().numpy(), R.layer_forward(Lr, x), f"glm {S.FMT_NAMES[fmt]} decode")
+        say(f"GLM {S.FMT_NAMES[fmt]} decode pool {pool}: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+    x = S.tokens(sh, 16, seed=0, pool=7)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    out = M.moe_layer_forward(layer, xd)
+    torch.cuda.synchronize()
+    rel, mx = assert_close(out.cpu().numpy(), R.layer_forward(Lr, x), f"glm {S.FMT_NAMES[fmt]} 16 tokens")
+    say(f"GLM {S.FMT_NAMES[fmt]} 16 tokens: rel-L2 {rel:.2e} max-abs {mx:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_glm_prefill_formats(glm_fmt_bank):
+    """The 512-token GLM prefill batch in each format: routing and union exact for every
+    token; the rows of the expert with the most rows (moe_expert_ffn) and the layer output
+    of 48 tokens spread over the batch within the bar."""
+    fmt, bank = glm_fmt_bank
+    sh, d = _glm_fmt_layer("glm_prefill", fmt, bank)
+    x = S.make_batch(sh, d, seed=0)
+    layer = M.Layer.from_host(d, DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    ids, w, keff, rids, rw, rkeff = check_routing(d, layer, x, xd, sh)
+    un, ru = check_union(layer, ids, keff, rids, rkeff, sh.n_experts, sh.top_k)
+    counts = np.diff(ru["off"])
+    Lr = R.Layer(d)
+    y = M.moe_expert_ffn(layer, xd, un)
+    out = M.moe_layer_forward(layer, xd)
+    torch.cuda.synchronize()
+    hot = int(np.argmax(counts))
+    r0, r1 = int(ru["off"][hot]), int(ru["off"][hot + 1])
+    off_e = np.clip(ru["off"], r0, r1).astype(np.int32)
+    ref_rows = R.expert_ffn(Lr, x, off_e, ru["row_tok"])[r0:r1]
+    rel, mx = assert_close(y.cpu().numpy()[r0:r1], ref_rows, f"glm {S.FMT_NAMES[fmt]} prefill expert {hot}")
+    say(f"GLM {S.FMT_NAMES[fmt]} prefill expert {hot} ({r1 - r0} rows): rel-L2 {rel:.2e}")
+    toks = np.linspace(0, sh.tokens - 1, 48).astype(np.int32)
+    ref = R.layer_forward(Lr, x, toks=toks)
+    got = out.cpu().numpy()[toks]
+    rel, mx = assert_close(got, ref, f"glm {S.FMT_NAMES[fmt]} prefill sampled tokens")
+    for i in range(len(toks)):
+        assert_close(got[i], ref[i], f"glm {S.FMT_NAMES[fmt]} prefill token {toks[i]}")
+    say(f"GLM {S.FMT_NAMES[fmt]} prefill, 48 tokens: rel-L2 {rel:.2e} max-abs {mx:.2e}")
