@@ -488,11 +488,107 @@ def run_workload(wl, args, dev):
         "kernel_rooflines": kernels,
         "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
     }
+    if wl == "glm_prefill":
+        rec_out["compute_bound_subsets"] = compute_subsets(layers[0], xpool[:T], args.steps)
     extra = dict(bank=bank, routers=routers, xs_host=xs_host, sh=sh)
     del layers, ws, xpool, out, hbuf, xbuf, nu, offb
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec_out, extra
+
+
+def compute_subsets(layer, x, reps, min_rows=88):
+    """Matrix-core utilisation where the prefill's expert FFNs are compute-bound.
+
+    With about 16 rows per union expert most of the prefill layer streams weights, so
+    its FFN time is bound by HBM.  Three subsets have enough rows per weight byte to be
+    bound by the matrix cores instead, and each is timed alone with per-kernel HIP events:
+    the routed experts that the batch gives at least ``min_rows`` rows (their rows only,
+    through moe_expert_ffn), the shared expert on all of the batch's tokens
+    (moe_dense_forward with the shared weights), and a grouped GEMM of the batch's eight
+    most-used experts with every token routed to each of them (R_e = T rows each).
+    Useful flops are 2*H*F per row for each of gate, up and down; the int8 matrix cores
+    run two limb products per useful product, so their issue rate is twice the useful one."""
+    import torch
+    import routed_int4_expert_amd as M
+
+    T, H, E, k = x.shape[0], layer.hidden, layer.n_experts, layer.top_k
+    F = layer.c.ffn
+    dev = x.device
+    ws = layer.workspace(T, dev)
+    ids, _w, keff = M.moe_route(layer, x, ws=ws)
+    un = M.moe_union(layer, ids, keff, ws=ws)
+    torch.cuda.synchronize()
+    off = un["off"].cpu().numpy().astype(np.int64)
+    row_tok = un["row_tok"].cpu().numpy()
+    cnt = np.diff(off)
+
+    def union_of(experts, rows_of):
+        experts = sorted(experts)
+        c = np.zeros(E, dtype=np.int64)
+        rt = []
+        for e in experts:
+            r = rows_of(e)
+            c[e] = len(r)
+            rt.append(r)
+        o = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+        rt = np.concatenate(rt).astype(np.int32) if rt else np.zeros(0, np.int32)
+        u = np.full(E, -1, np.int32)
+        u[:len(experts)] = experts
+        nrows = int(o[-1])
+        rtp = np.full(max(T * k, nrows, 1), -1, np.int32)
+        rtp[:nrows] = rt
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return dict(n_uniq=t(np.array([len(experts)], np.int32)), uniq=t(u), off=t(o), row_tok=t(rtp)), nrows
+
+    def timed(fn, rows, ffn):
+        fn()
+        torch.cuda.synchronize()
+        M.moe_prof_begin()
+        for _ in range(reps):
+            fn()
+        kern = M.moe_prof_end()
+        torch.cuda.synchronize()
+        res = {"rows": int(rows)}
+        tot_flops, tot_ms = 0.0, 0.0
+        for role, name in (("gateup", "ffn_gateup_mfma"), ("down", "ffn_down_mfma")):
+            launches, ms = kern.get(name, (0, float("nan")))
+            us = ms * 1e3 / max(launches, 1)
+            flops = 2.0 * H * ffn * rows * (2 if role == "gateup" else 1)
+            tot_flops += flops
+            tot_ms += ms / max(launches, 1)
+            res[role] = {"kernel": name, "avg_launch_us": float(us),
+                         "useful_tflops": float(flops / (us * 1e-6) / 1e12),
+                         "util_vs_bf16_dense": float(flops / (us * 1e-6) / BF16_PEAK_FLOPS),
+                         "i8_issue_util": float(2 * flops / (us * 1e-6) / I8_PEAK_OPS)}
+        res["ffn_useful_tflops"] = float(tot_flops / (tot_ms * 1e-3) / 1e12)
+        res["ffn_util_vs_bf16_dense"] = float(tot_flops / (tot_ms * 1e-3) / BF16_PEAK_FLOPS)
+        return res
+
+    out = {"min_rows": min_rows}
+    hot = [int(e) for e in np.nonzero(cnt >= min_rows)[0]]
+    if hot:
+        sub, nrows = union_of(hot, lambda e: row_tok[off[e]:off[e + 1]])
+        y = torch.zeros((max(T * k, nrows), H), dtype=torch.float32, device=dev)
+        r = timed(lambda: M.moe_expert_ffn(layer, x, sub, y_rows=y, ws=ws), nrows, F)
+        r["experts"] = len(hot)
+        r["rows_per_expert"] = [int(cnt[e]) for e in hot]
+        out["experts_ge_min_rows"] = r
+    top8 = [int(e) for e in np.argsort(-cnt, kind="stable")[:8]]
+    sub, nrows = union_of(top8, lambda e: np.arange(T))
+    y = torch.zeros((nrows, H), dtype=torch.float32, device=dev)
+    r = timed(lambda: M.moe_expert_ffn(layer, x, sub, y_rows=y, ws=ws), nrows, F)
+    r["experts"] = len(top8)
+    r["rows_per_expert"] = T
+    out["grouped_gemm_all_tokens"] = r
+    dense = M.Dense({kk: layer.t["sh_" + kk] for kk in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")})
+    dws = dense.workspace(T, dev)
+    yd = torch.empty((T, H), dtype=torch.float32, device=dev)
+    r = timed(lambda: M.moe_dense_forward(dense, x, out=yd, ws=dws), T, dense.ffn)
+    r["shared_ffn"] = dense.ffn
+    out["shared_expert"] = r
+    del ws, dws, y, yd
+    return out
 
 
 def _device_address(t):
