@@ -488,8 +488,21 @@ def run_workload(wl, args, dev):
         "kernel_rooflines": kernels,
         "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
     }
+    # the bars the layer is held to: a step at 0.70 of the HBM peak on its algorithmic bytes;
+    # where rows per expert make the FFN compute-bound, half the dense bf16 peak in useful flops
+    frac_step = rec_out["step_roofline"]["frac_of_hbm_peak"]
+    rec_out["target"] = {"hbm_frac_of_step_needed": 0.70, "hbm_frac_of_step": frac_step,
+                         "ms_per_step_at_target": float(step_bytes / (0.70 * HBM_PEAK_GBPS * 1e9) * 1e3),
+                         "met": bool(frac_step >= 0.70)}
+    if wl == "glm_rows256":
+        util = kernels["gateup"]["mfma_util_vs_bf16_dense"]
+        rec_out["target"].update(bf16_util_needed=0.5, gateup_bf16_util=util, met=bool(util >= 0.5))
     if wl == "glm_prefill":
-        rec_out["compute_bound_subsets"] = compute_subsets(layers[0], xpool[:T], args.steps)
+        sub = compute_subsets(layers[0], xpool[:T], args.steps)
+        rec_out["compute_bound_subsets"] = sub
+        best = max(v["ffn_util_vs_bf16_dense"] for v in sub.values() if isinstance(v, dict))
+        rec_out["target"].update(bf16_util_needed_on_compute_bound_subsets=0.5,
+                                 best_subset_bf16_util=best)
     extra = dict(bank=bank, routers=routers, xs_host=xs_host, sh=sh)
     del layers, ws, xpool, out, hbuf, xbuf, nu, offb
     torch.cuda.synchronize()
@@ -809,7 +822,8 @@ def main():
         else:
             subs[wl] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "dtype", "config", "timing",
                                             "step_roofline", "roofline", "kernel_rooflines",
-                                            "kernels_us_per_step")}
+                                            "kernels_us_per_step", "target", "compute_bound_subsets")
+                        if k in rec}
             log(f"{wl}: {rec['value']:.0f} tokens/s, {rec['ms_per_step'] * 1e3:.1f} us/step, "
                 f"gate/up {rec['roofline']['frac']:.2f} of HBM peak")
     tiers = list(TIER_WORKLOADS) if args.workload == "all" else [w for w in TIER_WORKLOADS if w == args.workload]

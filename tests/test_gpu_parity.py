@@ -114,6 +114,13 @@ SMALL = [
     # every expert has about 256 rows (eight 32-row items) and the shared expert 512
     S.custom("rows256", hidden=512, n_experts=16, ffn=256, shared_ffn=256, top_k=8, tokens=512,
              bias_amp=0.05),
+    # few (item, output block) pairs on the matrix cores, K = 1344 (21 groups: the last of
+    # six chunks holds one group) and F = 320 (a partial output block); then 32-row items
+    # (T*k >= 8E) of a small layer at T = 64
+    S.custom("split_gu", hidden=1344, n_experts=8, ffn=320, shared_ffn=192, top_k=2, tokens=16,
+             top_p=0.9, routed_scale=2.5),
+    S.custom("split_gu32", hidden=1024, n_experts=4, ffn=256, shared_ffn=128, top_k=4, tokens=64,
+             bias_amp=0.1),
 ]
 
 
@@ -294,19 +301,21 @@ def test_item_row_boundaries():
     full_parity(sh, d, x)
 
 
-@pytest.mark.parametrize("T", [3, 24, 40], ids=["gemv", "mfma16", "mfma32"])
+@pytest.mark.parametrize("T,H", [(3, 256), (24, 256), (40, 256), (24, 1024)],
+                         ids=["gemv", "mfma16", "mfma32", "mfma16_k1024"])
 @pytest.mark.parametrize("mode", ["gate", "up"])
-def test_exact_expert_products(T, mode):
+def test_exact_expert_products(T, H, mode):
     """Exactness special case: activations in {-1, 0, 1} and every gs64 scale 2^-6.
 
-    Each pre-activation is 2^-6 times an integer of at most 12 bits, so the 16-bit
-    activation blocks represent x and the pre-activations exactly and every product
-    and partial sum is exact in int32 and fp32.  With the gate/up step writing the
-    gate (or up) pre-activation P instead of SiLU(g) * u, the expert rows
+    Each pre-activation is 2^-6 times an integer of at most 14 bits (H <= 1024), so the
+    16-bit activation blocks represent x and the pre-activations exactly and every
+    product and partial sum is exact in int32 and fp32.  With the gate/up step writing
+    the gate (or up) pre-activation P instead of SiLU(g) * u, the expert rows
     y = Wd P must equal the exact value bit for bit: T = 3 runs the GEMV kernels,
-    T = 24 the matrix-core kernels with 16-row items, T = 40 with 32-row items.
+    T = 24 the matrix-core kernels with 16-row items, T = 40 with 32-row items, and
+    T = 24 at H = 1024 the matrix-core kernels over four K chunks per row.
     """
-    sh = S.custom(f"exact{T}", hidden=256, n_experts=8, ffn=128, shared_ffn=64, top_k=2,
+    sh = S.custom(f"exact{T}_{H}", hidden=H, n_experts=8, ffn=128, shared_ffn=64, top_k=2,
                   tokens=T)
     d = S.make_layer(sh, seed=0)
     for key in ("gate_s", "up_s", "down_s", "sh_gate_s", "sh_up_s", "sh_down_s"):
