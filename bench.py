@@ -188,11 +188,15 @@ def counted_traffic(workload, kernel):
     for e in data.get("entries", []):
         if e.get("workload") != workload or e.get("kernel") != kernel:
             continue
-        try:
-            with open(os.path.join(ROOT, e["source"]), "rb") as f:
-                if hashlib.sha256(f.read()).hexdigest() != e["source_sha256"]:
-                    return None
-        except OSError:
+        # every source file of the kernel and its launch unchanged since the counters
+        for src, sha in zip(e.get("sources", []), e.get("sources_sha256", [])):
+            try:
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    if hashlib.sha256(f.read()).hexdigest() != sha:
+                        return None
+            except OSError:
+                return None
+        if not e.get("sources"):
             return None
         return float(e["hbm_bytes_per_launch"])
     return None

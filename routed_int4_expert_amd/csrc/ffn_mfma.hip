@@ -91,6 +91,9 @@ struct PrepJob {
     int blocks;  // workgroups of 256 threads this job takes
     int act8;    // the opt-in 8-bit codes (hi bytes 0, lo bytes the code)
     int bf16;    // the MXFP4 path's two bf16 terms per value instead (no steps)
+    // the rows in use, or nullptr for all: the routed h rows stop at the union's row count
+    // off[E] (top-p may keep fewer than T*k picks); no work item reads a row past it
+    const int32_t *live_rows;
 };
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
@@ -109,9 +112,10 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
     const int NGp = mfma_groups_padded(K), NC = NGp / kCG;
     const long i = (long)blk * blockDim.x + threadIdx.x;  // (row, chunk, word of the chunk)
     const long n = (long)rows * NC * 32;
-    const bool in_rows = i < n;
-    const long ii = in_rows ? i : n - 1;
+    const long ii = i < n ? i : n - 1;
     const int row = (int)(ii / (NC * 32)), c = (int)(ii / 32 % NC), w = (int)(ii % 32);
+    // (uniform over a chunk's 32 lanes, which all hold the same row)
+    const bool in_rows = i < n && (!j.live_rows || row < j.live_rows[0]);
     const int b = 32 * c + w;  // word of the row
     const bool live = in_rows && b < K / 8;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -171,10 +175,11 @@ __device__ __forceinline__ void prep_frag_body(const PrepJob &j, int blk) {
 }
 
 static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float *step, int act8 = 0,
-                        int bf16 = 0) {
+                        int bf16 = 0, const int32_t *live_rows = nullptr) {
     PrepJob j;
     j.act8 = act8;
     j.bf16 = bf16;
+    j.live_rows = live_rows;
     j.src = src;
     j.rows = rows;
     j.K = K;
@@ -945,12 +950,14 @@ hipError_t launch_ffn_mfma(const MfmaArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int shared_items = a.with_shared ? (a.T + a.item_rows - 1) / a.item_rows : 0;
     if ((e = launch_gemm<true>(a, shared_items, "ffn_gateup_mfma", st)) != hipSuccess) return e;
-    // h rows in fragment order: the routed rows (as many as the largest union can
-    // have) and the shared rows
+    // h rows in fragment order: the routed rows (the grid covers the largest union, the
+    // workgroups past the union's row count off[E] do nothing) and the shared rows
     ItemsJob no_items = it;
     no_items.items = nullptr;
     no_items.with_union = 0;
-    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step, a.act8, bf) : none,
+    e = launch_prep(a.with_routed ? prep_job(a.h_routed, a.max_rows, a.F, a.hr_frag, a.hr_step, a.act8, bf,
+                                             a.off + a.E)
+                                  : none,
                     a.with_shared ? prep_job(a.h_shared, a.T, a.Fs, a.hs_frag, a.hs_step, a.act8, bf) : none,
                     no_items, "prep_h", st);
     if (e != hipSuccess) return e;
