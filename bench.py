@@ -501,7 +501,7 @@ def run_workload(wl, args, dev):
     if wl == "glm_rows256":
         util = kernels["gateup"]["mfma_util_vs_bf16_dense"]
         rec_out["target"].update(bf16_util_needed=0.5, gateup_bf16_util=util, met=bool(util >= 0.5))
-    if wl == "glm_prefill":
+    if wl == "glm_prefill" and not args.no_subsets:
         sub = compute_subsets(layers[0], xpool[:T], args.steps)
         rec_out["compute_bound_subsets"] = sub
         best = max(v["ffn_util_vs_bf16_dense"] for v in sub.values() if isinstance(v, dict))
@@ -785,6 +785,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--no-tier", action="store_true", help="skip the residency-tier workload")
+    ap.add_argument("--no-subsets", action="store_true",
+                    help="skip the prefill's compute-bound subsets (their launches would enter a profile of "
+                         "the prefill's own kernels)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-long device buffer 13 times (calibrates the HBM "
                          "byte counters against a transfer of known size) and exit")
