@@ -191,9 +191,11 @@ static PrepJob prep_job(const float *src, int rows, int K, uint8_t *frag, float 
 }
 
 // ------------------------------------------------------------------ work list
-// Work items: expert e with c rows gets ceil(c / IR) items of consecutive rows.  Items
-// of more than 16 rows (two MFMA row blocks, about 1.5 times the work of one) come
-// first, then those of at most 16; each class in union order.  The kernel deals its
+// Work items: expert e with c rows gets ceil(c / IR) items of consecutive rows.  The
+// items of experts with more than 16 rows (items of two MFMA row blocks, about 1.5 times
+// the work of one, or several items) come first, then the single items of the others;
+// each class in union order, and an expert's items stay together, so that the pairs
+// that read its weights run side by side and share them in L2.  The kernel deals its
 // (item, output block) pairs to the workgroups in turn, so the longer pairs go out
 // first and the shorter ones even out the end.  One workgroup of 256 threads, one
 // thread per union slot (E <= 256); exclusive scans of the two item counts place each
@@ -219,7 +221,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *total) {
 __device__ __forceinline__ void place_items(int e, int c, int row_base, int IR, int32_t *items,
                                             int32_t *n_items) {
     const int ni = (c + IR - 1) / IR;
-    const int nbig = ni == 0 ? 0 : (ni - 1) + (c - IR * (ni - 1) > 16 ? 1 : 0);
+    const int nbig = c > 16 ? ni : 0;
     int big_total, small_total;
     const int big_base = block_exclusive_scan(nbig, &big_total);
     const int small_base = block_exclusive_scan(ni - nbig, &small_total);
