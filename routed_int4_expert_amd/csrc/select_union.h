@@ -253,13 +253,13 @@ __device__ __forceinline__ void select_token_impl(const SelectArgs &a, int t, in
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const unsigned long long sm = __ballot(sel[i]);
-        if (sel[i] && base + __popcll(sm & below) < a.k) {
-            const int pos = base + __popcll(sm & below);
+        const int pos = base + (int)__popcll(sm & below);
+        if (sel[i] && pos < a.k) {
             ps->key[pos] = key[i];
             ps->sig[pos] = sig[i];
             ps->id[pos] = lane + kWave * i;
         }
-        base += __popcll(sm);
+        base += (int)__popcll(sm);
     }
     wave_lds_sync();
     // rank of pick j (choice descending, equal choices by lower id): the k <= 16 picks
