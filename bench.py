@@ -38,6 +38,7 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill),
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_FLOPS = 2.5e15   # dense bf16 MFMA (the peak the utilisation target names)
 I8_PEAK_OPS = 5.0e15       # dense int8 MFMA (the arithmetic the matrix-core path runs)
+F64_PEAK_FLOPS = 78.6e12   # dense fp64 MFMA (the router's matrix-core path for T > 8)
 
 WORKLOADS = {
     "glm_decode": "MoE layer H=6144, 256 routed experts F=2048 + 1 shared Fs=2048, int4-gs64, "
@@ -491,6 +492,7 @@ def run_workload(wl, args, dev):
         },
         "kernel_rooflines": kernels,
         "kernels_us_per_step": {kname: v[1] * 1e3 / args.steps for kname, v in kern.items()},
+        "other_kernels": other_kernels(kern, T, H, E, sh.top_k, rows.mean(), out_bf16),
     }
     # the bars the layer is held to: a step at 0.70 of the HBM peak on its algorithmic bytes;
     # where rows per expert make the FFN compute-bound, half the dense bf16 peak in useful flops
@@ -512,6 +514,29 @@ def run_workload(wl, args, dev):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec_out, extra
+
+
+def other_kernels(kern, T, H, E, k, rows, out_bf16):
+    """The router and the combine against their own bounds: the router's fp32 weight rows
+    and tokens (HBM; for more than 8 tokens also the fp64 matrix cores, T*E*H products),
+    the combine's routed rows, shared rows and output (HBM)."""
+    res = {}
+    launches, ms = kern.get("router_logits", (0, float("nan")))
+    if launches:
+        us = ms * 1e3 / launches
+        b = E * H * 4 + T * H * 4
+        r = {"avg_launch_us": us, "bytes_per_launch": float(b),
+             "hbm_frac": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        if T > 8:
+            r["fp64_util"] = 2.0 * T * E * H / (us * 1e-6) / F64_PEAK_FLOPS
+        res["router_logits"] = r
+    launches, ms = kern.get("combine", (0, float("nan")))
+    if launches:
+        us = ms * 1e3 / launches
+        b = rows * H * 4 + T * H * 4 + T * H * (2 if out_bf16 else 4) + T * k * 8
+        res["combine"] = {"avg_launch_us": us, "bytes_per_launch": float(b),
+                          "hbm_frac": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    return res
 
 
 def compute_subsets(layer, x, reps, min_rows=88):
@@ -829,7 +854,8 @@ def main():
         else:
             subs[wl] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "dtype", "config", "timing",
                                             "step_roofline", "roofline", "kernel_rooflines",
-                                            "kernels_us_per_step", "target", "compute_bound_subsets")
+                                            "kernels_us_per_step", "other_kernels", "target",
+                                            "compute_bound_subsets")
                         if k in rec}
             log(f"{wl}: {rec['value']:.0f} tokens/s, {rec['ms_per_step'] * 1e3:.1f} us/step, "
                 f"gate/up {rec['roofline']['frac']:.2f} of HBM peak")
